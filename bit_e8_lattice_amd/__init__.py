@@ -1,0 +1,186 @@
+"""bit_e8_lattice_amd -- MI355X (gfx950) E8 lattice projection for E8-QAT.
+
+A thin ctypes binding over ``libe8q.so`` (C ABI in ``include/e8q.h``).  The
+Python functions carry the same names as the C entry points and only marshal
+arguments: torch tensors supply device memory and the current HIP stream; every
+step of the computation runs in the library's HIP kernels.  Nothing here falls
+back to the CPU: if the library is missing, calls raise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "E8QError", "lib", "library_path",
+    "e8q_project", "e8q_project_hadamard", "e8q_encode_core_escape",
+    "e8q_encode_workspace_size", "e8q_ste_backward", "e8q_core_size",
+    "e8q_status_string", "e8q_version",
+    "ESCAPE_RECORD_BYTES", "STATUS_BITS", "F32", "BF16",
+]
+
+F32, BF16 = 0, 1
+ESCAPE_RECORD_BYTES = 20
+STATUS_BITS = {
+    "NONFINITE": 1, "BAD_SCALE": 2, "INT8_RANGE": 4, "ESC_OVERFLOW": 8,
+    "X_RANGE": 16, "LOOKBACK_TIMEOUT": 32,
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libe8q.so")
+_lib = None
+
+
+class E8QError(RuntimeError):
+    def __init__(self, fn, code):
+        msg = lib().e8q_status_string(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{fn} failed: {msg} (code {code})")
+        self.code = code
+
+
+def lib():
+    """Load ``libe8q.so`` (built in-tree by ``bit_e8_lattice_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is missing: run `python -m bit_e8_lattice_amd.build`")
+    L = ctypes.CDLL(library_path)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    e = ctypes.c_int
+    L.e8q_project.argtypes = [vp, e, i64, i64, i64, vp, vp, e, vp, i32, vp, vp, vp]
+    L.e8q_project.restype = e
+    L.e8q_project_hadamard.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, vp, e, vp, vp, i32, vp, vp, vp]
+    L.e8q_project_hadamard.restype = e
+    L.e8q_encode_core_escape.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
+                                         vp, sz, vp, vp]
+    L.e8q_encode_core_escape.restype = e
+    L.e8q_encode_workspace_size.argtypes = [i64, i64, i64]
+    L.e8q_encode_workspace_size.restype = sz
+    L.e8q_ste_backward.argtypes = [vp, vp, vp, f32, e, i64, vp]
+    L.e8q_ste_backward.restype = e
+    L.e8q_core_size.argtypes = [i32]
+    L.e8q_core_size.restype = i64
+    L.e8q_status_string.argtypes = [e]
+    L.e8q_status_string.restype = ctypes.c_char_p
+    L.e8q_version.argtypes = []
+    L.e8q_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} dtype {t.dtype} not in {dtypes}")
+
+
+def _dtype_code(t):
+    return BF16 if t.dtype == torch.bfloat16 else F32
+
+
+def _shape3(w):
+    if w.dim() == 2:
+        return 1, w.shape[0], w.shape[1]
+    if w.dim() == 3:
+        return tuple(w.shape)
+    raise ValueError("weights must be [rows, cols] or [batch, rows, cols]")
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, code):
+    if code != 0:
+        raise E8QError(fn, code)
+
+
+_WDT = (torch.float32, torch.bfloat16)
+
+
+def e8q_project(w, row_scale, status, q_out=None, two_z_out=None, core_bound=-1,
+                esc_count_out=None, stream=None):
+    """``e8q_project``: q = s * nearest_E8(w / s) per 8-column group (no rotation)."""
+    _dev(w, "w", _WDT); _dev(row_scale, "row_scale", (torch.float32,))
+    _dev(q_out, "q_out", _WDT); _dev(two_z_out, "two_z_out", (torch.int8,))
+    _dev(esc_count_out, "esc_count_out", (torch.int64,)); _dev(status, "status", (torch.int32,))
+    b, r, c = _shape3(w)
+    code = lib().e8q_project(_ptr(w), _dtype_code(w), b, r, c, _ptr(row_scale), _ptr(q_out),
+                             _dtype_code(q_out) if q_out is not None else F32, _ptr(two_z_out),
+                             int(core_bound), _ptr(esc_count_out), _ptr(status), _stream(w, stream))
+    _check("e8q_project", code)
+
+
+def e8q_project_hadamard(w, row_scale, signs, had_block, status, q_out=None, two_z_out=None,
+                         rotated_out=None, core_bound=-1, esc_count_out=None, stream=None):
+    """``e8q_project_hadamard``: sign flip + blockwise Walsh-Hadamard, then project."""
+    _dev(w, "w", _WDT); _dev(row_scale, "row_scale", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,)); _dev(q_out, "q_out", _WDT)
+    _dev(two_z_out, "two_z_out", (torch.int8,)); _dev(rotated_out, "rotated_out", (torch.float32,))
+    _dev(esc_count_out, "esc_count_out", (torch.int64,)); _dev(status, "status", (torch.int32,))
+    b, r, c = _shape3(w)
+    code = lib().e8q_project_hadamard(_ptr(w), _dtype_code(w), b, r, c, _ptr(row_scale), _ptr(signs),
+                                      int(had_block), _ptr(q_out),
+                                      _dtype_code(q_out) if q_out is not None else F32,
+                                      _ptr(two_z_out), _ptr(rotated_out), int(core_bound),
+                                      _ptr(esc_count_out), _ptr(status), _stream(w, stream))
+    _check("e8q_project_hadamard", code)
+
+
+def e8q_encode_workspace_size(batch, rows, cols):
+    return int(lib().e8q_encode_workspace_size(batch, rows, cols))
+
+
+def e8q_encode_core_escape(w, row_scale, core_bound, core_idx_out, esc_out, esc_count_out,
+                           workspace, status, signs=None, had_block=0, two_z_out=None, stream=None):
+    """``e8q_encode_core_escape``: core indices (uint16 stored in an int16 tensor)
+    plus escape records (``esc_out``: uint8 tensor of 20-byte records)."""
+    _dev(w, "w", _WDT); _dev(row_scale, "row_scale", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,)); _dev(core_idx_out, "core_idx_out", (torch.int16,))
+    _dev(esc_out, "esc_out", (torch.uint8,)); _dev(esc_count_out, "esc_count_out", (torch.int64,))
+    _dev(workspace, "workspace", (torch.uint8,)); _dev(two_z_out, "two_z_out", (torch.int8,))
+    _dev(status, "status", (torch.int32,))
+    b, r, c = _shape3(w)
+    cap = 0 if esc_out is None else esc_out.numel() // ESCAPE_RECORD_BYTES
+    code = lib().e8q_encode_core_escape(_ptr(w), _dtype_code(w), b, r, c, _ptr(row_scale), _ptr(signs),
+                                        int(had_block), int(core_bound), _ptr(core_idx_out),
+                                        _ptr(esc_out), cap, _ptr(esc_count_out), _ptr(two_z_out),
+                                        _ptr(workspace), workspace.numel(), _ptr(status),
+                                        _stream(w, stream))
+    _check("e8q_encode_core_escape", code)
+
+
+def e8q_ste_backward(grad_q, grad_w=None, w_latent=None, lr=1.0, stream=None):
+    """``e8q_ste_backward``: identity STE copy and/or fused SGD on the latents."""
+    _dev(grad_q, "grad_q", _WDT); _dev(grad_w, "grad_w", (grad_q.dtype,))
+    _dev(w_latent, "w_latent", (grad_q.dtype,))
+    code = lib().e8q_ste_backward(_ptr(grad_q), _ptr(grad_w), _ptr(w_latent), float(lr),
+                                  _dtype_code(grad_q), grad_q.numel(), _stream(grad_q, stream))
+    _check("e8q_ste_backward", code)
+
+
+def e8q_core_size(core_bound):
+    return int(lib().e8q_core_size(int(core_bound)))
+
+
+def e8q_status_string(code):
+    return lib().e8q_status_string(int(code)).decode()
+
+
+def e8q_version():
+    return lib().e8q_version().decode()

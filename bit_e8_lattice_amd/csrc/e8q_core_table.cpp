@@ -1,0 +1,129 @@
+// Host construction of the core rank tables (see e8q_core_table.hpp).
+#include "e8q_core_table.hpp"
+
+#include <array>
+#include <mutex>
+
+namespace e8q {
+
+namespace {
+
+using Pt = std::array<int, 8>;
+
+// All points of C(B) in lexicographic order: coordinates are generated in
+// increasing order, depth first, with the norm budget and the single-parity
+// rule pruned early; the E8 sum rule (sum = 0 mod 4) is tested at the leaf.
+void enumerate(int bound, int tmax, std::vector<Pt>& out) {
+    Pt cur{};
+    struct Rec {
+        int bound, tmax;
+        std::vector<Pt>* out;
+        Pt* cur;
+        void go(int i, int norm, int sum, int par) {
+            if (i == 8) {
+                if (((sum % 4) + 4) % 4 == 0) out->push_back(*cur);
+                return;
+            }
+            for (int v = -tmax; v <= tmax; ++v) {
+                if (i > 0 && ((v & 1) != par)) continue;
+                const int nn = norm + v * v;
+                if (nn > bound) continue;
+                (*cur)[i] = v;
+                go(i + 1, nn, sum + v, i == 0 ? (v & 1) : par);
+            }
+        }
+    } r{bound, tmax, &out, &cur};
+    r.go(0, 0, 0, 0);
+}
+
+uint32_t half_index(const int* t, int tm) {
+    const uint32_t base = uint32_t(tm + 1);
+    uint32_t h = 0;
+    for (int i = 0; i < 4; ++i) h = h * base + uint32_t((t[i] + tm) >> 1);
+    return h;
+}
+
+}  // namespace
+
+bool build_core_table(int32_t bound, CoreTable& out) {
+    if (bound < 0 || bound > 40) return false;
+    out = CoreTable{};
+    out.bound = bound;
+    RankParams& p = out.p;
+    // even class: |t| <= largest even e with e^2 <= B; odd class: the other
+    // seven coordinates are at least 1 in magnitude, so t^2 <= B - 7.
+    int te = 0;
+    while ((te + 2) * (te + 2) <= bound) te += 2;
+    int to = -1;
+    for (int o = 1; o * o + 7 <= bound; o += 2) to = o;
+    p.tm[0] = te;
+    p.tm[1] = to;
+    const int nr = bound / 4 + 1;
+    uint32_t off = 0;
+    for (int c = 0; c < 2; ++c) {
+        const uint32_t base = p.tm[c] >= 0 ? uint32_t(p.tm[c] + 1) : 0u;
+        p.nh[c] = base * base * base * base;
+        p.off_f[c] = off;
+        off += p.nh[c];
+    }
+    for (int c = 0; c < 2; ++c) {
+        p.off_g[c] = off;
+        off += uint32_t(nr) * 2u * p.nh[c];
+    }
+    p.entries = off;
+    out.data.assign(off, uint16_t(0xFFFF));
+
+    std::vector<Pt> pts;
+    enumerate(bound, te > to ? te : to, pts);
+    out.size = int64_t(pts.size());
+    if (pts.size() > 0xFFFF) return false;
+
+    // F: index of the first core point with each first half.
+    for (size_t i = 0; i < pts.size(); ++i) {
+        const Pt& t = pts[i];
+        const int c = t[0] & 1;
+        uint16_t& f = out.data[p.off_f[c] + half_index(t.data(), p.tm[c])];
+        if (f == 0xFFFF) f = uint16_t(i);
+    }
+    // G: running count of admissible second halves per (class, norm used, sum residue).
+    for (int c = 0; c < 2; ++c) {
+        const int tm = p.tm[c];
+        if (tm < 0) continue;
+        const int base = tm + 1;
+        for (int ridx = 0; ridx < nr; ++ridx) {
+            for (int s = 0; s < 2; ++s) {
+                const int budget = bound - 4 * ridx;
+                uint32_t count = 0;
+                const uint32_t row = p.off_g[c] + uint32_t(ridx * 2 + s) * p.nh[c];
+                int d[4];
+                for (uint32_t h = 0; h < p.nh[c]; ++h) {
+                    uint32_t hh = h;
+                    for (int i = 3; i >= 0; --i) { d[i] = int(hh % uint32_t(base)); hh /= uint32_t(base); }
+                    int norm = 0, sum = 0;
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 2 * d[i] - tm;
+                        norm += t * t;
+                        sum += t;
+                    }
+                    if (norm > budget || (((sum - 2 * s) % 4) + 4) % 4 != 0) continue;
+                    out.data[row + h] = uint16_t(count);
+                    ++count;
+                }
+            }
+        }
+    }
+    // Self-check: the two-read formula reproduces every rank.
+    for (size_t i = 0; i < pts.size(); ++i) {
+        const Pt& t = pts[i];
+        const int c = t[0] & 1;
+        int na = 0, sa = 0;
+        for (int k = 0; k < 4; ++k) { na += t[k] * t[k]; sa += t[k]; }
+        const uint32_t f = out.data[p.off_f[c] + half_index(t.data(), p.tm[c])];
+        const uint32_t g = out.data[p.off_g[c] + uint32_t((na >> 2) * 2 + ((sa >> 1) & 1)) * p.nh[c] +
+                                    half_index(t.data() + 4, p.tm[c])];
+        if (f + g != uint32_t(i)) return false;
+    }
+    return true;
+}
+
+}  // namespace e8q

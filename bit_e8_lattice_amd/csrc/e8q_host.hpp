@@ -1,0 +1,56 @@
+// Host-side helpers shared by the entry points: argument checks, device
+// properties, launch sizing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "e8q.h"
+
+namespace e8q {
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Blocks for a grid-stride launch of `items` work items with `per_block`
+// items per block: enough to fill every CU `waves_per_cu`-deep, never more
+// than there is work.
+inline unsigned grid_for(uint64_t items, unsigned per_block, unsigned blocks_per_cu) {
+    uint64_t need = (items + per_block - 1) / per_block;
+    uint64_t cap = uint64_t(device_cu_count()) * blocks_per_cu;
+    if (need < 1) need = 1;
+    return unsigned(need < cap ? need : cap);
+}
+
+inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Shape checks common to the projection and encode calls.  Returns E8Q_OK or
+// E8Q_ERR_INVALID / E8Q_ERR_UNSUPPORTED.
+inline e8q_status_t check_shape(const void* w, e8q_dtype_t w_dtype, int64_t batch, int64_t rows,
+                                int64_t cols, const float* row_scale, uint32_t* status_dev) {
+    if (!w || !row_scale || !status_dev) return E8Q_ERR_INVALID;
+    if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 8) return E8Q_ERR_INVALID;
+    if (w_dtype != E8Q_F32 && w_dtype != E8Q_BF16) return E8Q_ERR_INVALID;
+    // groups of the whole call must fit 32 bits (indices are 32-bit on the device)
+    const double groups = double(batch) * double(rows) * double(cols / 8);
+    if (groups >= 4294967295.0) return E8Q_ERR_UNSUPPORTED;
+    return E8Q_OK;
+}
+
+inline e8q_status_t check_block(const int8_t* signs, int32_t had_block, int64_t cols) {
+    if (!signs) return E8Q_ERR_INVALID;
+    if (!is_pow2(had_block) || had_block < 8 || had_block > 4096 || cols % had_block)
+        return E8Q_ERR_INVALID;
+    return E8Q_OK;
+}
+
+inline float kappa_for(int32_t had_block) {
+    // fl32(1/sqrt(b)) from float64 (exact 2^-k for b = 4^k)
+    return had_block > 0 ? float(1.0 / __builtin_sqrt(double(had_block))) : 1.0f;
+}
+
+inline e8q_status_t launch_status() {
+    return hipGetLastError() == hipSuccess ? E8Q_OK : E8Q_ERR_LAUNCH;
+}
+
+}  // namespace e8q

@@ -1,0 +1,205 @@
+/*
+ * e8q.h -- C ABI of the MI355X (gfx950) E8 lattice projection library.
+ *
+ * What it computes.  E8-QAT ("E8-QAT: Efficient 2-Bit Quantization-Aware
+ * Training with Implicit Lattice Codebooks") quantizes LLM weights in groups
+ * of eight: each group of normalized coordinates is sent by arithmetic alone
+ * to its nearest point of the E8 lattice (no stored codebook is searched), an
+ * identity straight-through estimator carries gradients back to the latent
+ * weights, and for export every point is stored as a 16-bit index into a
+ * finite core or, outside the core, as an exact sparse escape record
+ * (abstract; captions of Figures 1(c), 2(a)-(c) and 6(c); Tables 3, 9, 10).
+ * The pages leave the Hadamard transform and the scales out of their figure
+ * (Figure 2 caption); the readings used here are stated with each call.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers to memory the caller owns (for
+ *     example torch tensors).  Work is enqueued on `stream` (a hipStream_t
+ *     passed as void*; NULL = the legacy default stream) and runs
+ *     asynchronously; nothing is synchronized before return.
+ *   - The return value reports only host-side checks and the launch:
+ *       E8Q_OK, E8Q_ERR_INVALID (a bad argument: null required pointer,
+ *       non-positive size, cols not a multiple of 8, bad block size or core
+ *       bound, too small workspace), E8Q_ERR_UNSUPPORTED (a dtype or size
+ *       combination this build does not implement), E8Q_ERR_LAUNCH (the HIP
+ *       launch failed), E8Q_ERR_DEVICE (a device query or the one-time rank
+ *       table upload failed).  Nothing is launched when a check fails.
+ *   - Conditions that depend on the data are reported by OR-ing E8Q_STATUS_*
+ *     bits into `*status_dev` (a device uint32 the caller zeroes beforehand).
+ *   - Weights are [batch, rows, cols] row-major; a group is 8 consecutive
+ *     columns of one row; cols % 8 == 0; batch*rows*cols < 2^40 and
+ *     rows*cols/8 < 2^32.
+ *   - Lattice points are reported as 2z (integers): z is in E8 = D8 u (D8+1/2)
+ *     iff all 2z_i are even or all odd and sum(2z) = 0 mod 4.
+ *   - Calls on different streams may run concurrently; the library keeps no
+ *     mutable device state between calls except the read-only rank tables.
+ *
+ * Numerics (bit-exact contract; the CPU oracle computes the same):
+ *   v = w (float32, bf16 widened exactly)
+ *   rotation (optional): v_j <- sign_j * v_j, then for each block of `b`
+ *     columns the un-normalized Sylvester Walsh-Hadamard transform in float32,
+ *     butterfly stages of stride 1, 2, 4, ..., b/2 in that order, each mapping
+ *     (p, q) -> (p + q, p - q); rotated value u = fl32(v * kappa_b),
+ *     kappa_b = fl32(1/sqrt(b)) (kappa = 1 without rotation)
+ *   c_r = fl32(kappa_b * fl32(1 / s_r)), x = fl32(v * c_r)
+ *   nearest E8 point of each group: n = rint(x) (ties to even), a = |x - n|,
+ *     sgn_i = +1 if x_i >= n_i else -1; D8 point: n, and if sum(n) is odd
+ *     coordinate k (largest a, lowest index) moved by sgn_k; D8+1/2 point:
+ *     n + sgn/2, and if sum(2y) != 0 mod 4 coordinate m (smallest a, lowest
+ *     index) moved by -sgn_m; the D8 point is taken iff
+ *     sum(a) - 2 + [D8 fixed](1 - 2a_k) - [D8+1/2 fixed] 2a_m <= 0, evaluated
+ *     exactly as that float64 expression with sum(a) added pairwise
+ *     ((a0+a1)+(a2+a3))+((a4+a5)+(a6+a7))
+ *   q = fl32(s_r * z); bf16 outputs round to nearest even
+ *   invalid data: row with !(s_r > 0), s_r = inf or c_r = inf -> every group
+ *     z = 0, E8Q_STATUS_BAD_SCALE; group with a non-finite x -> z = 0,
+ *     E8Q_STATUS_NONFINITE; group with some |x_i| >= 8192 -> z = 0,
+ *     E8Q_STATUS_X_RANGE.  q of a bad row is +0.
+ */
+#ifndef E8Q_H
+#define E8Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    E8Q_OK = 0,
+    E8Q_ERR_INVALID = 1,
+    E8Q_ERR_UNSUPPORTED = 2,
+    E8Q_ERR_LAUNCH = 3,
+    E8Q_ERR_DEVICE = 4
+} e8q_status_t;
+
+/* Bits OR-ed into *status_dev by the kernels. */
+enum {
+    E8Q_STATUS_NONFINITE = 1u,       /* a group had a NaN/Inf normalized coordinate      */
+    E8Q_STATUS_BAD_SCALE = 2u,       /* a row scale was not a positive finite number     */
+    E8Q_STATUS_INT8_RANGE = 4u,      /* a 2z value was saturated in an int8 output       */
+    E8Q_STATUS_ESC_OVERFLOW = 8u,    /* more escapes than esc_capacity; records cut      */
+    E8Q_STATUS_X_RANGE = 16u,        /* a group had |x_i| >= 8192                        */
+    E8Q_STATUS_LOOKBACK_TIMEOUT = 32u /* escape offsets not resolved in time (outputs invalid) */
+};
+
+typedef enum { E8Q_F32 = 0, E8Q_BF16 = 1 } e8q_dtype_t;
+
+/* One escape record, 20 bytes.  E8-QAT stores groups outside the core exactly
+ * as 20-byte coordinate records (Table 10; Figure 6(c): payload 2 + 20 rho
+ * bits per weight).  Field layout (a reading; the pages give only the size):
+ * the group index within its matrix (row * cols/8 + col/8), then 2z as int16. */
+typedef struct {
+    uint32_t group;
+    int16_t two_z[8];
+} e8q_escape_t;
+
+/* ---------------------------------------------------------------------------
+ * e8q_project -- forward projection without rotation: q = s * nearest_E8(w/s).
+ * E8-QAT abstract and Figure 1(c)/2(b) captions: every forward pass maps each
+ * group of eight normalized weights to its nearest E8 point by arithmetic.
+ *
+ *   w            [batch, rows, cols] weights, dtype w_dtype (F32 or BF16)
+ *   row_scale    [batch*rows] float32 reconstruction scale s_r
+ *   q_out        [batch, rows, cols] dequantized s*z in q_dtype, or NULL
+ *   two_z_out    [batch, rows, cols] int8 2z (saturated, E8Q_STATUS_INT8_RANGE), or NULL
+ *   core_bound   with esc_count_out: a group counts as escaped if ||2z||^2 > core_bound (>= 0)
+ *   esc_count_out [batch] int64, overwritten with the per-batch-item escape count, or NULL
+ *   status_dev   device uint32, bits OR-ed in (required)
+ * At least one of q_out, two_z_out, esc_count_out must be non-NULL.
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_project(const void* w, e8q_dtype_t w_dtype,
+                         int64_t batch, int64_t rows, int64_t cols,
+                         const float* row_scale,
+                         void* q_out, e8q_dtype_t q_dtype,
+                         int8_t* two_z_out,
+                         int32_t core_bound, int64_t* esc_count_out,
+                         uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * e8q_project_hadamard -- e8q_project after a randomized Walsh-Hadamard
+ * rotation (E8-QAT Figure 2 caption: Hadamard transforms precede the
+ * projection but are not drawn).  Arguments as e8q_project, plus:
+ *   signs        [cols] int8, each +1 or -1 (another value is undefined behaviour)
+ *   had_block    b: a power of two in [8, 4096] dividing cols
+ *   rotated_out  [batch, rows, cols] float32 u = fl32(v * kappa_b), or NULL
+ * q = s * z is in the rotated basis.
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_project_hadamard(const void* w, e8q_dtype_t w_dtype,
+                                  int64_t batch, int64_t rows, int64_t cols,
+                                  const float* row_scale,
+                                  const int8_t* signs, int32_t had_block,
+                                  void* q_out, e8q_dtype_t q_dtype,
+                                  int8_t* two_z_out, float* rotated_out,
+                                  int32_t core_bound, int64_t* esc_count_out,
+                                  uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * e8q_encode_core_escape -- export encoding (E8-QAT Figure 2(c): core indices
+ * plus sparse escape records keep the final lattice points exactly).
+ *
+ * Core C(B) = { z in E8 : ||2z||^2 <= B } (a reading of the pages' finite
+ * core; B = core_bound in [0, 40], |C(40)| = 56,881).  The core index of z is
+ * its rank among C(B) sorted lexicographically by 2z (signed, coordinate 0
+ * most significant); escaped groups get 0xFFFF.
+ *
+ *   w, w_dtype, batch, rows, cols, row_scale   as e8q_project
+ *   signs        [cols] int8 +-1, or NULL for no rotation (had_block ignored)
+ *   had_block    as e8q_project_hadamard when signs != NULL
+ *   core_idx_out [batch*rows*cols/8] uint16 (required)
+ *   esc_out      [esc_capacity] records, ascending (batch, group); the records
+ *                of batch item i start at sum(esc_count_out[0..i-1]).  Records
+ *                past esc_capacity are dropped and E8Q_STATUS_ESC_OVERFLOW is
+ *                set; esc_out may be NULL only when esc_capacity == 0.
+ *   esc_count_out [batch] int64, exact per-batch escape counts (required)
+ *   two_z_out    [batch, rows, cols] int8 2z (saturated), or NULL
+ *   workspace    device scratch of at least e8q_encode_workspace_size() bytes,
+ *                256-byte aligned; contents need no initialization and are
+ *                clobbered.  One workspace must not be shared by calls that
+ *                may run at the same time.
+ * Escape order is deterministic (it does not depend on scheduling).
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtype,
+                                    int64_t batch, int64_t rows, int64_t cols,
+                                    const float* row_scale,
+                                    const int8_t* signs, int32_t had_block,
+                                    int32_t core_bound,
+                                    uint16_t* core_idx_out,
+                                    e8q_escape_t* esc_out, int64_t esc_capacity,
+                                    int64_t* esc_count_out,
+                                    int8_t* two_z_out,
+                                    void* workspace, size_t workspace_bytes,
+                                    uint32_t* status_dev, void* stream);
+
+/* Workspace bytes e8q_encode_core_escape needs for this shape (0 on bad sizes). */
+size_t e8q_encode_workspace_size(int64_t batch, int64_t rows, int64_t cols);
+
+/* ---------------------------------------------------------------------------
+ * e8q_ste_backward -- identity straight-through estimator (E8-QAT Figure 2(b)
+ * caption), optionally fused with a plain SGD step on the latent weights
+ * (Table 4: latents are BF16).
+ *   grad_q    [n] gradient with respect to q, dtype `dtype` (required)
+ *   grad_w    [n] receives grad_q bit for bit, or NULL
+ *   w_latent  [n] updated in place: w <- fl32(w - fl32(lr * g)), rounded to
+ *             nearest even for BF16 (NaN -> 0x7FC0), or NULL
+ * At least one of grad_w, w_latent must be non-NULL; grad_w may alias neither.
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_ste_backward(const void* grad_q, void* grad_w, void* w_latent,
+                              float lr, e8q_dtype_t dtype, int64_t n, void* stream);
+
+/* |C(core_bound)|, the number of core points; -1 if core_bound is outside [0, 40].
+ * Host-only. */
+int64_t e8q_core_size(int32_t core_bound);
+
+/* Short text for a return code.  Host-only. */
+const char* e8q_status_string(e8q_status_t s);
+
+/* Library version string.  Host-only. */
+const char* e8q_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E8Q_H */

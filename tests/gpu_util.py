@@ -1,0 +1,96 @@
+"""Helpers for the GPU parity tests: run the HIP library through its Python
+binding and bring results back as numpy arrays in the oracle's formats."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_e8_lattice_amd as e8q
+import oracle
+
+
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test needs a ROCm device")
+    e8q.lib()                     # raises if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def wbits(w):
+    """Weights as the oracle takes them: bf16 bits (uint16) or float32."""
+    if w.dtype == torch.bfloat16:
+        return u16(w)
+    return w.cpu().numpy()
+
+
+def run_project(w, s, signs=None, hb=0, q_dtype=torch.bfloat16, two_z=True, rotated=False,
+                core_bound=-1):
+    d = w.device
+    st = torch.zeros(1, dtype=torch.int32, device=d)
+    q = torch.empty(w.shape, dtype=q_dtype, device=d) if q_dtype is not None else None
+    tz = torch.empty(w.shape, dtype=torch.int8, device=d) if two_z else None
+    u = torch.empty(w.shape, dtype=torch.float32, device=d) if rotated else None
+    batch = 1 if w.dim() == 2 else w.shape[0]
+    esc = torch.empty(batch, dtype=torch.int64, device=d) if core_bound >= 0 else None
+    if signs is None:
+        e8q.e8q_project(w, s, st, q_out=q, two_z_out=tz, core_bound=core_bound, esc_count_out=esc)
+    else:
+        e8q.e8q_project_hadamard(w, s, signs, hb, st, q_out=q, two_z_out=tz, rotated_out=u,
+                                 core_bound=core_bound, esc_count_out=esc)
+    torch.cuda.synchronize()
+    out = {"status": int(st.item()) & 0xFFFFFFFF}
+    if q is not None:
+        out["q"] = u16(q) if q_dtype == torch.bfloat16 else q.cpu().numpy()
+    if tz is not None:
+        out["two_z_i8"] = tz.cpu().numpy()
+    if u is not None:
+        out["u"] = u.cpu().numpy()
+    if esc is not None:
+        out["esc_count"] = esc.cpu().numpy()
+    return out
+
+
+def run_encode(w, s, core_bound, signs=None, hb=0, cap=None, two_z=False, keep_device=False):
+    d = w.device
+    batch, rows, cols = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    groups = batch * rows * cols // 8
+    if cap is None:
+        cap = groups
+    st = torch.zeros(1, dtype=torch.int32, device=d)
+    core = torch.empty(groups, dtype=torch.int16, device=d)
+    esc = torch.empty(max(cap, 1) * e8q.ESCAPE_RECORD_BYTES, dtype=torch.uint8, device=d)
+    if cap == 0:
+        esc = None
+    cnt = torch.empty(batch, dtype=torch.int64, device=d)
+    ws = torch.empty(e8q.e8q_encode_workspace_size(batch, rows, cols), dtype=torch.uint8, device=d)
+    tz = torch.empty(w.shape, dtype=torch.int8, device=d) if two_z else None
+    e8q.e8q_encode_core_escape(w, s, core_bound, core, esc, cnt, ws, st, signs=signs, had_block=hb,
+                               two_z_out=tz)
+    torch.cuda.synchronize()
+    counts = cnt.cpu().numpy()
+    n = int(min(counts.sum(), cap))
+    rec = (esc[: n * 20].cpu().numpy().view(oracle.ESCAPE_RECORD_DTYPE) if n
+           else np.zeros(0, oracle.ESCAPE_RECORD_DTYPE))
+    out = {"status": int(st.item()) & 0xFFFFFFFF, "core_idx": u16(core), "counts": counts,
+           "records": rec}
+    if tz is not None:
+        out["two_z_i8"] = tz.cpu().numpy()
+    if keep_device:
+        out["dev"] = (core, esc, cnt)
+    return out
+
+
+def first_mismatch(a, b):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if a.shape != b.shape:
+        return f"shape {a.shape} vs {b.shape}"
+    bad = np.nonzero((a != b).reshape(-1))[0]
+    if len(bad) == 0:
+        return None
+    i = bad[0]
+    return f"{len(bad)} mismatches, first at flat {i}: {a.reshape(-1)[i]} vs {b.reshape(-1)[i]}"

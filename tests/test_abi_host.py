@@ -1,0 +1,110 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, host-only helpers agree with the oracle, and argument validation
+rejects bad calls before anything is launched (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import bit_e8_lattice_amd as e8q
+    if not os.path.exists(e8q.library_path):
+        from bit_e8_lattice_amd.build import build
+        build()
+    return e8q.lib()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "e8q.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(e8q_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"e8q_project", "e8q_project_hadamard", "e8q_encode_core_escape", "e8q_ste_backward"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_core_size_matches_oracle(L):
+    for b in range(0, 41):
+        assert L.e8q_core_size(b) == oracle.core_size(b)
+    assert L.e8q_core_size(-1) == -1 and L.e8q_core_size(41) == -1
+
+
+def test_strings(L):
+    assert L.e8q_status_string(0) == b"ok"
+    assert b"invalid" in L.e8q_status_string(1)
+    assert b"gfx950" in L.e8q_version()
+
+
+def test_workspace_size(L):
+    assert L.e8q_encode_workspace_size(1, 1, 12) == 0
+    assert L.e8q_encode_workspace_size(0, 4, 8) == 0
+    groups = 128 * 4096 * 4096 // 8
+    tiles = (groups + 2047) // 2048
+    assert L.e8q_encode_workspace_size(128, 4096, 4096) == 256 + 8 * tiles
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args", [
+    # (w, dtype, batch, rows, cols, scale, q, qdt, two_z, bound, esc, status)
+    (None, 1, 1, 4, 16, FAKE, FAKE, 1, None, -1, None, FAKE),
+    (FAKE, 1, 1, 4, 12, FAKE, FAKE, 1, None, -1, None, FAKE),       # cols % 8
+    (FAKE, 1, 0, 4, 16, FAKE, FAKE, 1, None, -1, None, FAKE),       # batch
+    (FAKE, 7, 1, 4, 16, FAKE, FAKE, 1, None, -1, None, FAKE),       # dtype
+    (FAKE, 1, 1, 4, 16, None, FAKE, 1, None, -1, None, FAKE),       # scale
+    (FAKE, 1, 1, 4, 16, FAKE, FAKE, 1, None, -1, None, None),       # status
+    (FAKE, 1, 1, 4, 16, FAKE, None, 1, None, -1, None, FAKE),       # no output
+    (FAKE, 1, 1, 4, 16, FAKE, None, 1, None, -1, FAKE, FAKE),       # esc without bound
+])
+def test_project_rejects(L, args):
+    assert L.e8q_project(*args, None) == 1
+
+
+@pytest.mark.parametrize("signs,block,cols", [(None, 128, 256), (FAKE, 96, 384), (FAKE, 4, 16),
+                                              (FAKE, 8192, 8192), (FAKE, 256, 384)])
+def test_project_hadamard_rejects_blocks(L, signs, block, cols):
+    assert L.e8q_project_hadamard(FAKE, 1, 1, 4, cols, FAKE, signs, block, FAKE, 1, None, None,
+                                  -1, None, FAKE, None) == 1
+
+
+def test_project_rejects_huge(L):
+    # 2^32 groups or more is unsupported (32-bit group indices on the device)
+    assert L.e8q_project(FAKE, 1, 1 << 16, 1 << 16, 8, FAKE, FAKE, 1, None, -1, None, FAKE, None) == 2
+
+
+def test_encode_rejects(L):
+    ws = L.e8q_encode_workspace_size(1, 4, 16)
+    base = [FAKE, 1, 1, 4, 16, FAKE, None, 0, 16, FAKE, FAKE, 10, FAKE, None, FAKE, ws, FAKE, None]
+    bad = []
+    b = list(base); b[8] = 41; bad.append(b)                      # core bound
+    b = list(base); b[8] = -1; bad.append(b)
+    b = list(base); b[9] = None; bad.append(b)                    # core index output
+    b = list(base); b[12] = None; bad.append(b)                   # counts
+    b = list(base); b[14] = None; bad.append(b)                   # workspace
+    b = list(base); b[15] = ws - 1; bad.append(b)                 # too small
+    b = list(base); b[14] = ctypes.c_void_p(0x10010); bad.append(b)   # misaligned
+    b = list(base); b[10] = None; bad.append(b)                   # capacity without records
+    b = list(base); b[6] = FAKE; b[7] = 24; bad.append(b)         # bad block
+    for args in bad:
+        assert L.e8q_encode_core_escape(*args) == 1, args
+
+
+def test_ste_rejects(L):
+    assert L.e8q_ste_backward(None, FAKE, None, 1.0, 1, 10, None) == 1
+    assert L.e8q_ste_backward(FAKE, None, None, 1.0, 1, 10, None) == 1
+    assert L.e8q_ste_backward(FAKE, FAKE, None, 1.0, 1, 0, None) == 1
+    assert L.e8q_ste_backward(FAKE, FAKE, None, 1.0, 5, 10, None) == 1
+    assert L.e8q_ste_backward(FAKE, FAKE, None, 1.0, 1, 10, None) == 1     # grad_w aliases grad_q
