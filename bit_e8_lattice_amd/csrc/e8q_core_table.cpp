@@ -2,7 +2,6 @@
 #include "e8q_core_table.hpp"
 
 #include <array>
-#include <mutex>
 
 namespace e8q {
 
@@ -36,10 +35,9 @@ void enumerate(int bound, int tmax, std::vector<Pt>& out) {
     r.go(0, 0, 0, 0);
 }
 
-uint32_t half_index(const int* t, int tm) {
-    const uint32_t base = uint32_t(tm + 1);
+uint32_t half_index(const int* t, int tm, uint32_t ub) {
     uint32_t h = 0;
-    for (int i = 0; i < 4; ++i) h = h * base + uint32_t((t[i] + tm) >> 1);
+    for (int i = 0; i < 4; ++i) h = h * ub + uint32_t((t[i] + tm) >> 1);
     return h;
 }
 
@@ -58,20 +56,11 @@ bool build_core_table(int32_t bound, CoreTable& out) {
     for (int o = 1; o * o + 7 <= bound; o += 2) to = o;
     p.tm[0] = te;
     p.tm[1] = to;
-    const int nr = bound / 4 + 1;
-    uint32_t off = 0;
-    for (int c = 0; c < 2; ++c) {
-        const uint32_t base = p.tm[c] >= 0 ? uint32_t(p.tm[c] + 1) : 0u;
-        p.nh[c] = base * base * base * base;
-        p.off_f[c] = off;
-        off += p.nh[c];
-    }
-    for (int c = 0; c < 2; ++c) {
-        p.off_g[c] = off;
-        off += uint32_t(nr) * 2u * p.nh[c];
-    }
-    p.entries = off;
-    out.data.assign(off, uint16_t(0xFFFF));
+    p.ub = uint32_t((te > to ? te : to) + 1);
+    p.nh = p.ub * p.ub * p.ub * p.ub;
+    p.nstate = 2u * uint32_t(bound / 4 + 1);
+    p.entries = 2u * p.nh + 2u * p.nstate * p.nh;
+    out.data.assign(p.entries, uint16_t(0xFFFF));
 
     std::vector<Pt> pts;
     enumerate(bound, te > to ? te : to, pts);
@@ -82,33 +71,34 @@ bool build_core_table(int32_t bound, CoreTable& out) {
     for (size_t i = 0; i < pts.size(); ++i) {
         const Pt& t = pts[i];
         const int c = t[0] & 1;
-        uint16_t& f = out.data[p.off_f[c] + half_index(t.data(), p.tm[c])];
+        uint16_t& f = out.data[uint32_t(c) * p.nh + half_index(t.data(), p.tm[c], p.ub)];
         if (f == 0xFFFF) f = uint16_t(i);
     }
-    // G: running count of admissible second halves per (class, norm used, sum residue).
+    // G: running count of admissible second halves per (class, state).
     for (int c = 0; c < 2; ++c) {
         const int tm = p.tm[c];
         if (tm < 0) continue;
-        const int base = tm + 1;
-        for (int ridx = 0; ridx < nr; ++ridx) {
-            for (int s = 0; s < 2; ++s) {
-                const int budget = bound - 4 * ridx;
-                uint32_t count = 0;
-                const uint32_t row = p.off_g[c] + uint32_t(ridx * 2 + s) * p.nh[c];
-                int d[4];
-                for (uint32_t h = 0; h < p.nh[c]; ++h) {
-                    uint32_t hh = h;
-                    for (int i = 3; i >= 0; --i) { d[i] = int(hh % uint32_t(base)); hh /= uint32_t(base); }
-                    int norm = 0, sum = 0;
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 2 * d[i] - tm;
-                        norm += t * t;
-                        sum += t;
-                    }
-                    if (norm > budget || (((sum - 2 * s) % 4) + 4) % 4 != 0) continue;
-                    out.data[row + h] = uint16_t(count);
-                    ++count;
+        for (uint32_t state = 0; state < p.nstate; ++state) {
+            const int budget = bound - 2 * int(state >> 1) * 2;   // B - ||tA||^2, ||tA||^2 = 4 * (state/2)
+            const int s = int(state & 1u);                         // sum tA = 2s (mod 4)
+            uint32_t count = 0;
+            const uint32_t row = 2u * p.nh + (uint32_t(c) * p.nstate + state) * p.nh;
+            int d[4];
+            for (uint32_t h = 0; h < p.nh; ++h) {
+                uint32_t hh = h;
+                for (int i = 3; i >= 0; --i) { d[i] = int(hh % p.ub); hh /= p.ub; }
+                int norm = 0, sum = 0;
+                bool ok = true;
+                for (int i = 0; i < 4; ++i) {
+                    if (d[i] > tm) ok = false;
+                    const int t = 2 * d[i] - tm;
+                    norm += t * t;
+                    sum += t;
                 }
+                // tB must fit the remaining budget and make the total sum 0 mod 4
+                if (!ok || norm > budget || (((sum + 2 * s) % 4) + 4) % 4 != 0) continue;
+                out.data[row + h] = uint16_t(count);
+                ++count;
             }
         }
     }
@@ -118,9 +108,10 @@ bool build_core_table(int32_t bound, CoreTable& out) {
         const int c = t[0] & 1;
         int na = 0, sa = 0;
         for (int k = 0; k < 4; ++k) { na += t[k] * t[k]; sa += t[k]; }
-        const uint32_t f = out.data[p.off_f[c] + half_index(t.data(), p.tm[c])];
-        const uint32_t g = out.data[p.off_g[c] + uint32_t((na >> 2) * 2 + ((sa >> 1) & 1)) * p.nh[c] +
-                                    half_index(t.data() + 4, p.tm[c])];
+        const uint32_t state = uint32_t(na >> 1) + uint32_t((sa >> 1) & 1);
+        const uint32_t f = out.data[uint32_t(c) * p.nh + half_index(t.data(), p.tm[c], p.ub)];
+        const uint32_t g = out.data[2u * p.nh + (uint32_t(c) * p.nstate + state) * p.nh +
+                                    half_index(t.data() + 4, p.tm[c], p.ub)];
         if (f + g != uint32_t(i)) return false;
     }
     return true;

@@ -2,17 +2,22 @@
 //
 // E8-QAT stores each in-core group as a 16-bit index (abstract; Figure 2(c)
 // caption; Table 3 checks that all core codewords decode consistently).  The
-// index used here is the rank of 2z among C(B) in lexicographic order.  The
-// device computes it with two table reads by splitting 2z = (tA, tB) into
+// index used here is the rank of t = 2z among C(B) in lexicographic order.
+// The device computes it with two table reads by splitting t = (tA, tB) into
 // halves of four coordinates:
 //
-//   rank(t) = F[c][h(tA)] + G[c][ ||tA||^2 / 4 ][ (sum tA / 2) mod 2 ][ h(tB) ]
+//   rank(t) = F[c][h(tA)] + G[c][state(tA)][h(tB)]
 //
-// c = parity class of t (all even / all odd), h() the mixed-radix index of a
-// half with digits (t_i + tmax_c) / 2.  F counts core points whose first half
-// is lexicographically smaller than tA; G counts admissible second halves
-// smaller than tB for the state left by tA (remaining norm budget, required
-// sum residue mod 4).  Both are built on the host by plain enumeration.
+// c = parity class of t (0: all even, 1: all odd).  Digits d_i = (t_i +
+// tm_c) / 2 lie in [0, tm_c], where tm_c is the largest |t_i| a core point of
+// class c can have; both classes use one radix ub = max(tm_0, tm_1) + 1, so
+// h(.) = sum d_i ub^(3-i) < ub^4 = nh.  F counts core points whose first
+// half is lexicographically smaller than tA.  state = ||tA||^2 / 2 +
+// ((sum tA / 2) mod 2) encodes what tA leaves for tB (norm budget, required
+// sum residue mod 4); G counts admissible second halves smaller than tB.
+//
+// Layout (uint16 entries): F[c] at c*nh, G[c][state] at 2*nh + (c*nstate +
+// state)*nh, nstate = 2*(B/4 + 1).
 #pragma once
 
 #include <stdint.h>
@@ -22,25 +27,22 @@
 namespace e8q {
 
 struct RankParams {
-    int32_t tm[2];       // largest |2z_i| per class (even, odd); -1 if the class is empty
-    uint32_t nh[2];      // (tm+1)^4: half indices per class
-    uint32_t off_f[2];   // F table offsets (entries)
-    uint32_t off_g[2];   // G table offsets (entries)
-    uint32_t entries;    // total uint16 entries
+    int32_t tm[2];       // largest |t_i| per class (even, odd); -1 if the class is empty
+    uint32_t ub;         // digit radix shared by both classes
+    uint32_t nh;         // ub^4
+    uint32_t nstate;     // 2 * (bound/4 + 1)
+    uint32_t entries;    // 2*nh + 2*nstate*nh
 };
 
 struct CoreTable {
     int32_t bound = -1;
     int64_t size = 0;            // |C(B)|
     RankParams p{};
-    std::vector<uint16_t> data;  // F and G tables, laid out by RankParams
+    std::vector<uint16_t> data;
 };
 
 // Build (and self-check) the table for 0 <= bound <= 40.  Returns false if the
 // self-check fails.
 bool build_core_table(int32_t bound, CoreTable& out);
-
-// Largest core bound whose table is small enough for LDS (<= 32 KB).
-constexpr int32_t kLdsTableMaxBound = 31;
 
 }  // namespace e8q

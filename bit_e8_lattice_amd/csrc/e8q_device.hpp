@@ -82,12 +82,28 @@ __device__ __forceinline__ void apply_signs(const int8_t* signs, uint32_t col0, 
 
 // ------------------------------------------------------------------ Hadamard
 // Un-normalized Sylvester WHT over blocks of HB columns held by HB/8 lanes.
-// Stage order: stride 1, 2, 4 in-lane, then 8, 16, ... across lanes.  The
-// lane holding the lower index of a pair keeps p + q, the other q_low - own,
-// i.e. (p, q) -> (p + q, p - q) exactly as the contract states.
+// Stage order: stride 1, 2, 4 inside a lane, then strides 8, 16, 32, 64
+// across lanes; each butterfly maps (p, q) to (p + q, p - q) exactly as the
+// contract states.
+//
+// Cross-lane stages use one v_fmac_f32 with a DPP-permuted operand per
+// element: new = own + eps * partner.  gfx9 DPP has no xor-4 lane pattern, so
+// logical lane L of a 16-lane row sits on physical lane
+// P = L0*1 ^ L1*2 ^ L2*7 ^ L3*8: logical partners L^1, L^2, L^4, L^8 are then
+// the physical patterns quad_perm[1,0,3,2], quad_perm[2,3,0,1],
+// row_half_mirror (xor 7) and row_ror:8 (xor 8).  With eps = +1 on the lane
+// holding the lower index and -1 on the other, a lane keeps the butterfly
+// result times a sign s_L = (-1)^popcount(L) (exactly: rounding to nearest
+// is symmetric), which the caller folds into the row coefficient.
+
+// Logical position of this physical lane inside its 16-lane row.
+__device__ __forceinline__ uint32_t logical_lane(uint32_t lane) {
+    const uint32_t p = lane & 15u;
+    return p ^ (((p >> 2) & 1u) * 3u);
+}
+
 template <int HB>
-__device__ __forceinline__ void fwht_group(float (&v)[8], uint32_t lane) {
-    static_assert(HB == 0 || (HB >= 8 && HB <= 128 && (HB & (HB - 1)) == 0), "block");
+__device__ __forceinline__ void fwht_inlane(float (&v)[8]) {
     if constexpr (HB >= 8) {
 #pragma unroll
         for (int h = 1; h < 8; h <<= 1) {
@@ -100,16 +116,55 @@ __device__ __forceinline__ void fwht_group(float (&v)[8], uint32_t lane) {
                 }
             }
         }
-#pragma unroll
-        for (int m = 1; m < HB / 8; m <<= 1) {
-            const bool low = (lane & m) == 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float other = __shfl_xor(v[i], m, 16);
-                v[i] = low ? (v[i] + other) : (other - v[i]);
-            }
-        }
     }
+}
+
+#define E8Q_BFLY8(PAT, E)                                                        \
+    "v_fmac_f32_dpp %0, %0, " E " " PAT " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %1, %1, " E " " PAT " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %2, %2, " E " " PAT " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %3, %3, " E " " PAT " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %4, %4, " E " " PAT " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %5, %5, " E " " PAT " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %6, %6, " E " " PAT " row_mask:0xf bank_mask:0xf\n"          \
+    "v_fmac_f32_dpp %7, %7, " E " " PAT " row_mask:0xf bank_mask:0xf\n"
+#define E8Q_S0 E8Q_BFLY8("quad_perm:[1,0,3,2]", "%8")
+#define E8Q_S1 E8Q_BFLY8("quad_perm:[2,3,0,1]", "%9")
+#define E8Q_S2 E8Q_BFLY8("row_half_mirror", "%10")
+#define E8Q_S3 E8Q_BFLY8("row_ror:8", "%11")
+// s_nop 4: DPP reads a VGPR that the preceding code may have just written
+// (and EXEC may just have been restored); five wait states cover both.
+#define E8Q_XLANE(BODY)                                                          \
+    asm volatile("s_nop 4\n" BODY                                                 \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]),     \
+                   "+v"(v[5]), "+v"(v[6]), "+v"(v[7])                              \
+                 : "v"(eps[0]), "v"(eps[1]), "v"(eps[2]), "v"(eps[3]))
+
+// Cross-lane stages; must run with all 64 lanes active.
+template <int HB>
+__device__ __forceinline__ void fwht_xlane(float (&v)[8], const float (&eps)[4]) {
+    if constexpr (HB == 16) E8Q_XLANE(E8Q_S0);
+    if constexpr (HB == 32) E8Q_XLANE(E8Q_S0 E8Q_S1);
+    if constexpr (HB == 64) E8Q_XLANE(E8Q_S0 E8Q_S1 E8Q_S2);
+    if constexpr (HB == 128) E8Q_XLANE(E8Q_S0 E8Q_S1 E8Q_S2 E8Q_S3);
+}
+
+// Per-lane constants of the cross-lane stages.
+struct LaneFwht {
+    float eps[4];
+    uint32_t sign;      // bit 31 set when the lane holds minus the transform
+    uint32_t logical;   // logical lane inside the 16-lane row
+};
+
+template <int HB>
+__device__ __forceinline__ LaneFwht lane_fwht(uint32_t lane) {
+    LaneFwht f;
+    f.logical = logical_lane(lane);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f.eps[k] = ((f.logical >> k) & 1u) ? -1.0f : 1.0f;
+    const uint32_t used = HB >= 16 ? uint32_t(HB / 8 - 1) : 0u;
+    f.sign = (uint32_t(__popc(f.logical & used)) & 1u) << 31;
+    return f;
 }
 
 // ------------------------------------------------------------------ E8

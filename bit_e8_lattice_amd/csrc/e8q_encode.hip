@@ -5,13 +5,27 @@
 // per group and a sparse 20-byte record for each group outside the finite
 // core (abstract; Figure 2(c) and Figure 6(c) captions; Table 10).
 //
-// One pass over the weights: each 256-thread block claims tiles of 2048
-// consecutive groups in increasing order (a device-wide counter), computes
-// every lattice point and core index of the tile, counts its escapes (wave
-// ballots, then a block scan), and resolves the tile's output offset with a
-// decoupled look-back over the per-tile status words (aggregate / inclusive
-// prefix, packed with their flag into one 64-bit word).  Escape records thus
-// land in ascending group order whatever the scheduling.
+// One pass over the weights.  Blocks claim tiles of consecutive groups in
+// increasing order from a device-wide counter.  Pass 1 over a tile computes
+// every lattice point and core index, stores the indices and counts escapes
+// (wave ballots); a block scan plus a decoupled look-back over per-tile status
+// words (aggregate / inclusive prefix, packed with their flag in one 64-bit
+// word) gives the tile's first record slot; pass 2 recomputes only the
+// (item, wave) slices that contain escapes -- their weights are still in L2 --
+// and writes the records.  Record order is therefore ascending group order
+// whatever the scheduling.
+//
+// The lattice point of a group is computed on one of two paths that give the
+// same result:
+//  * fast path (bf16 input, core bound <= 31, every |x_i| < 30, no x_i an
+//    integer, coset decision clear of float32 rounding): rint by the magic
+//    constant 1.5*2^23 + 32, whose low byte is then n_i + 32; the candidates
+//    2z + 64 are assembled four coordinates per 32-bit word with v_perm, the
+//    parity fix is located with per-element lane masks (first match = lowest
+//    index) and applied as a +-2 byte delta, and norm, sums and the two table
+//    indices come from v_dot4_u32_u8 on the packed words;
+//  * exact path (everything else, and the escape records): the decoder of
+//    nearest_e8() on eight int32 coordinates, float64 decision when close.
 #include <map>
 #include <mutex>
 #include <utility>
@@ -22,14 +36,18 @@
 
 namespace e8q {
 
+constexpr int kBlock = 512;
+constexpr int kWaves = kBlock / kWave;
 constexpr int kItems = 8;                          // groups per thread per tile
-constexpr int kBlock = 256;
-constexpr uint32_t kTileGroups = kItems * kBlock;  // 2048
+constexpr uint32_t kTileGroups = kItems * kBlock;  // 4096
 constexpr uint64_t kFlagA = 1ull << 62;            // aggregate published
 constexpr uint64_t kFlagP = 2ull << 62;            // inclusive prefix published
 constexpr uint64_t kValMask = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr size_t kWsHeader = 256;
+constexpr size_t kLdsLimit = 60 * 1024;   // dynamic LDS per block (static use is < 1 KB)
+constexpr float kMagic = 12582944.0f;              // 1.5 * 2^23 + 32
+constexpr float kFastXMax = 30.0f;
 
 struct EncodeArgs {
     const void* w;
@@ -37,12 +55,14 @@ struct EncodeArgs {
     uint32_t gpr;
     FastDiv gpr_div;
     FastDiv gpb_div;
-    const float* scale;
-    const int8_t* signs;
-    float kappa;
-    int core_bound;
+    const float* coef;        // per row fl32(kappa * fl32(1/s)), NaN for a bad row
+    const int8_t* signs;      // nullptr: no rotation
+    uint32_t cols;
+    uint32_t core_bound;
     const uint16_t* tab;
     RankParams rp;
+    uint32_t wpk;             // digit weights ub^3, ub^2, ub, 1 as bytes (fast path)
+    uint32_t ka[2], kb[2];    // v_dot4 accumulators giving 2*(F index), 2*(G index base)
     uint16_t* core_idx;
     e8q_escape_t* esc;
     uint64_t esc_cap;
@@ -54,23 +74,21 @@ struct EncodeArgs {
     uint32_t* status;
 };
 
+// Unified-layout rank of a core point (|t_i| <= tm of its class).
 __device__ __forceinline__ uint32_t core_rank(const int (&t)[8], const uint16_t* tab, const RankParams& p) {
-    const int c = t[0] & 1;
+    const uint32_t c = uint32_t(t[0]) & 1u;
     const int tm = c ? p.tm[1] : p.tm[0];
-    const uint32_t base = uint32_t(tm + 1);
     uint32_t ha = 0, hb = 0;
     int na = 0, sa = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        ha = ha * base + uint32_t((t[i] + tm) >> 1);
-        hb = hb * base + uint32_t((t[4 + i] + tm) >> 1);
+        ha = ha * p.ub + uint32_t((t[i] + tm) >> 1);
+        hb = hb * p.ub + uint32_t((t[4 + i] + tm) >> 1);
         na += t[i] * t[i];
         sa += t[i];
     }
-    const uint32_t f = tab[(c ? p.off_f[1] : p.off_f[0]) + ha];
-    const uint32_t nh = c ? p.nh[1] : p.nh[0];
-    const uint32_t g = tab[(c ? p.off_g[1] : p.off_g[0]) + uint32_t((na >> 2) * 2 + ((sa >> 1) & 1)) * nh + hb];
-    return f + g;
+    const uint32_t state = uint32_t(na >> 1) + (uint32_t(sa >> 1) & 1u);
+    return uint32_t(tab[c * p.nh + ha]) + uint32_t(tab[2u * p.nh + (c * p.nstate + state) * p.nh + hb]);
 }
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
@@ -79,31 +97,141 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
     return (uint64_t(hi) << 32) | lo;
 }
 
+// Ballot mask (bit = physical lane) re-ordered by logical group position:
+// logical = physical ^ 3 on lanes whose bit 2 is set, i.e. the bits of every
+// odd nibble are reversed.
+__device__ __forceinline__ uint64_t logical_lane_mask(uint64_t m) {
+    constexpr uint64_t odd = 0xF0F0F0F0F0F0F0F0ull;
+    const uint64_t keep = m & ~odd;
+    const uint64_t x = m & odd;
+    const uint64_t rev = ((x & 0x1010101010101010ull) << 3) | ((x & 0x2020202020202020ull) << 1) |
+                         ((x & 0x4040404040404040ull) >> 1) | ((x & 0x8080808080808080ull) >> 3);
+    return keep | rev;
+}
+
+// Workspace reset and per-row coefficients.
 __global__ void encode_init_kernel(uint32_t* counter, unsigned long long* tile_status, uint32_t num_tiles,
-                                   unsigned long long* esc_count, uint32_t batch) {
+                                   unsigned long long* esc_count, uint32_t batch, const float* scale,
+                                   float* coef, uint32_t rows_total, float kappa) {
     const uint32_t i0 = blockIdx.x * blockDim.x + threadIdx.x;
     const uint32_t stride = gridDim.x * blockDim.x;
     if (i0 == 0) *counter = 0u;
     for (uint32_t i = i0; i < num_tiles; i += stride) tile_status[i] = 0ull;
     for (uint32_t i = i0; i < batch; i += stride) esc_count[i] = 0ull;
+    for (uint32_t i = i0; i < rows_total; i += stride) {
+        bool bad;
+        const float c = row_coef(scale[i], kappa, bad);
+        coef[i] = bad ? __uint_as_float(0x7FC00000u) : c;
+    }
 }
 
-template <typename WT, int HB, bool LDS_TAB>
+// Raw input of one group: 16 bytes of bf16 (or 32 bytes of float32).
+template <typename WT>
+struct Raw {
+    uint4 p;
+    uint4 q;   // second half, float32 input only
+};
+
+template <typename WT>
+__device__ __forceinline__ Raw<WT> load_raw(const EncodeArgs& a, uint32_t g, bool live) {
+    Raw<WT> r;
+    r.p = make_uint4(0u, 0u, 0u, 0u);
+    r.q = make_uint4(0u, 0u, 0u, 0u);
+    if (live) {
+        if constexpr (sizeof(WT) == 2) {
+            r.p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.w) + uint64_t(g) * 8);
+        } else {
+            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.w) + uint64_t(g) * 8);
+            r.p = src[0];
+            r.q = src[1];
+        }
+    }
+    return r;
+}
+
+// Sign flip and Walsh-Hadamard rotation of one group; returns the lane's
+// stored values (the transform times the lane sign) in v.  All lanes of the
+// wave must be active.
+template <typename WT, int HB>
+__device__ __forceinline__ void rotate_raw(const EncodeArgs& a, const uint32_t* s_smask, Raw<WT> r, uint32_t g,
+                                           bool live, uint32_t row, const LaneFwht& lf, float (&v)[8]) {
+    if constexpr (HB > 0) {
+        if (live) {
+            const uint4 m = *reinterpret_cast<const uint4*>(s_smask + ((g - row * a.gpr) * 4u));
+            if constexpr (sizeof(WT) == 2) {
+                r.p.x ^= m.x; r.p.y ^= m.y; r.p.z ^= m.z; r.p.w ^= m.w;
+            } else {
+                r.p.x ^= m.x << 16; r.p.y ^= m.x & 0x80000000u;
+                r.p.z ^= m.y << 16; r.p.w ^= m.y & 0x80000000u;
+                r.q.x ^= m.z << 16; r.q.y ^= m.z & 0x80000000u;
+                r.q.z ^= m.w << 16; r.q.w ^= m.w & 0x80000000u;
+            }
+        }
+    }
+    if constexpr (sizeof(WT) == 2) {
+        v[0] = __uint_as_float(r.p.x << 16); v[1] = __uint_as_float(r.p.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(r.p.y << 16); v[3] = __uint_as_float(r.p.y & 0xFFFF0000u);
+        v[4] = __uint_as_float(r.p.z << 16); v[5] = __uint_as_float(r.p.z & 0xFFFF0000u);
+        v[6] = __uint_as_float(r.p.w << 16); v[7] = __uint_as_float(r.p.w & 0xFFFF0000u);
+    } else {
+        v[0] = __uint_as_float(r.p.x); v[1] = __uint_as_float(r.p.y);
+        v[2] = __uint_as_float(r.p.z); v[3] = __uint_as_float(r.p.w);
+        v[4] = __uint_as_float(r.q.x); v[5] = __uint_as_float(r.q.y);
+        v[6] = __uint_as_float(r.q.z); v[7] = __uint_as_float(r.q.w);
+    }
+    fwht_inlane<HB>(v);
+    fwht_xlane<HB>(v, lf.eps);
+}
+
+// Exact lattice point from normalized coordinates (invalid data -> 0).
+__device__ __forceinline__ uint32_t exact_point(const float (&x)[8], float coef_raw, int (&t)[8]) {
+    uint32_t inv = __builtin_isnan(coef_raw) ? uint32_t(E8Q_STATUS_BAD_SCALE) : group_invalid_bits(x);
+    if (inv) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = 0;
+    } else {
+        nearest_e8(x, t);
+    }
+    return inv;
+}
+
+__device__ __forceinline__ uint32_t norm_u32(const int (&t)[8]) {
+    uint32_t n = 0;   // <= 8 * 16386^2 < 2^32
+#pragma unroll
+    for (int i = 0; i < 8; ++i) n += uint32_t(t[i] * t[i]);
+    return n;
+}
+
+template <typename WT, int HB, bool LDS_TAB, bool FAST>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
-    extern __shared__ uint16_t s_tab[];
+    extern __shared__ uint32_t s_dyn[];
     __shared__ uint32_t s_tile;
-    __shared__ uint32_t s_cnt[kItems][kBlock / kWave];
-    __shared__ unsigned long long s_total;
+    __shared__ uint32_t s_cnt[kItems * kWaves];
+    __shared__ unsigned long long s_ball[kItems][kWaves];
     __shared__ unsigned long long s_excl;
 
     const uint32_t tid = threadIdx.x;
-    const uint32_t lane = __lane_id();
-    const uint32_t wv = tid / kWave;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wv = tid >> 6;
+
+    // LDS: [sign masks: cols/2 words, when rotating][rank table, when LDS_TAB]
+    const uint32_t smask_words = HB > 0 ? a.cols / 2u : 0u;
+    uint32_t* s_smask = s_dyn;
     const uint16_t* tab = a.tab;
-    if constexpr (LDS_TAB) {
-        for (uint32_t i = tid; i < a.rp.entries; i += kBlock) s_tab[i] = a.tab[i];
-        tab = s_tab;
+    if constexpr (HB > 0) {
+        for (uint32_t i = tid; i < smask_words; i += kBlock) {
+            const uint32_t s0 = uint32_t(uint8_t(a.signs[2 * i])) >> 7;
+            const uint32_t s1 = uint32_t(uint8_t(a.signs[2 * i + 1])) >> 7;
+            s_smask[i] = (s0 << 15) | (s1 << 31);
+        }
     }
+    if constexpr (LDS_TAB) {
+        uint16_t* t16 = reinterpret_cast<uint16_t*>(s_dyn + smask_words);
+        for (uint32_t i = tid; i < a.rp.entries; i += kBlock) t16[i] = a.tab[i];
+        tab = t16;
+    }
+    const LaneFwht lf = lane_fwht<HB>(lane);
+    const uint32_t lane_off = (lane & ~15u) + lf.logical;
 
     for (;;) {
         __syncthreads();
@@ -111,63 +239,137 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         __syncthreads();
         const uint32_t tile = s_tile;
         if (tile >= a.num_tiles) break;
+        const uint32_t tbase = tile * kTileGroups + wv * kWave + lane_off;
 
-        uint32_t esc_bits = 0;
-        uint32_t in_wave[kItems];
-        uint32_t rec[kItems][4];
         uint32_t flags = 0;
-
-#pragma unroll
+        // loads run two items ahead of the arithmetic
+        uint32_t g1 = tbase, g2 = tbase + kBlock;
+        bool l1 = g1 < a.groups, l2 = g2 < a.groups;
+        uint32_t r1 = l1 ? fdiv(g1, a.gpr_div) : 0u, r2 = l2 ? fdiv(g2, a.gpr_div) : 0u;
+        Raw<WT> w1 = load_raw<WT>(a, g1, l1), w2 = load_raw<WT>(a, g2, l2);
+        float c1 = a.coef[r1], c2 = a.coef[r2];
         for (int j = 0; j < kItems; ++j) {
-            const uint32_t g = tile * kTileGroups + uint32_t(j) * kBlock + tid;
-            const bool live = g < a.groups;
+            const uint32_t g = g1;
+            const bool live = l1;
+            const uint32_t row = r1;
+            const Raw<WT> raw = w1;
+            const float craw = c1;
+            g1 = g2; l1 = l2; r1 = r2; w1 = w2; c1 = c2;
+            if (j + 2 < kItems) {
+                g2 = g + 2u * kBlock;
+                l2 = g2 < a.groups;
+                r2 = l2 ? fdiv(g2, a.gpr_div) : 0u;
+                w2 = load_raw<WT>(a, g2, l2);
+                c2 = a.coef[r2];
+            }
             float v[8];
-            if (live) {
-                load_group(reinterpret_cast<const WT*>(a.w), g, v);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-            }
-            const uint32_t row = live ? fdiv(g, a.gpr_div) : 0u;
-            if constexpr (HB > 0) {
-                const uint32_t col0 = (g - row * a.gpr) * 8u;
-                if (live) apply_signs(a.signs, col0, v);
-                fwht_group<HB>(v, lane);
-            }
-            bool bad;
-            const float c = row_coef(a.scale[row], a.kappa, bad);
+            rotate_raw<WT, HB>(a, s_smask, raw, g, live, row, lf, v);
+            const float cl = __uint_as_float(__float_as_uint(craw) ^ lf.sign);
             float x[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = v[i] * c;
-            int t[8];
-            uint32_t inv = bad ? uint32_t(E8Q_STATUS_BAD_SCALE) : group_invalid_bits(x);
-            if (inv) {
+            for (int i = 0; i < 8; ++i) x[i] = v[i] * cl;
+
+            bool escaped = false;
+            uint32_t cidx = 0xFFFFu;
+            bool done = false;
+            if constexpr (FAST) {
+                float y[8], d[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = 0;
-                if (live) flags |= inv;
-            } else {
-                nearest_e8(x, t);
+                for (int i = 0; i < 8; ++i) {
+                    y[i] = x[i] + kMagic;
+                    const float nf = y[i] - kMagic;
+                    d[i] = x[i] - nf;
+                }
+                const float sa = ((fabsf(d[0]) + fabsf(d[1])) + (fabsf(d[2]) + fabsf(d[3]))) +
+                                 ((fabsf(d[4]) + fabsf(d[5])) + (fabsf(d[6]) + fabsf(d[7])));
+                const float amax = fmaxf(fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3]))),
+                                         fmaxf(fmaxf(fabsf(d[4]), fabsf(d[5])), fmaxf(fabsf(d[6]), fabsf(d[7]))));
+                const float amin = fminf(fminf(fminf(fabsf(d[0]), fabsf(d[1])), fminf(fabsf(d[2]), fabsf(d[3]))),
+                                         fminf(fminf(fabsf(d[4]), fabsf(d[5])), fminf(fabsf(d[6]), fabsf(d[7]))));
+                const float xmax = fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
+                                         fmaxf(fmaxf(fabsf(x[4]), fabsf(x[5])), fmaxf(fabsf(x[6]), fabsf(x[7]))));
+                uint32_t yb[8], db[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { yb[i] = __float_as_uint(y[i]); db[i] = __float_as_uint(d[i]); }
+                const uint32_t py = ((yb[0] ^ yb[1]) ^ (yb[2] ^ yb[3])) ^ ((yb[4] ^ yb[5]) ^ (yb[6] ^ yb[7]));
+                const uint32_t pd = ((db[0] ^ db[1]) ^ (db[2] ^ db[3])) ^ ((db[4] ^ db[5]) ^ (db[6] ^ db[7]));
+                const bool odd0 = (py & 1u) != 0u;
+                const bool odd1 = odd0 != ((pd >> 31) != 0u);
+                const float tq0 = sa - 2.0f;
+                const float tq1 = odd0 ? tq0 + (1.0f - 2.0f * amax) : tq0;
+                const float tq = odd1 ? tq1 - 2.0f * amin : tq1;
+                const bool fast = (xmax < kFastXMax) && (amin > 0.0f) && (fabsf(tq) > kFastDecision);
+                if (fast) {
+                    const bool d8 = tq < 0.0f;
+                    // n_i + 32 bytes and (d_i < 0 ? 0xFF : 0) bytes, four per word
+                    const uint32_t n0 = __builtin_amdgcn_perm(yb[1], yb[0], 0x0C0C0400u) |
+                                        __builtin_amdgcn_perm(yb[3], yb[2], 0x04000C0Cu);
+                    const uint32_t n1 = __builtin_amdgcn_perm(yb[5], yb[4], 0x0C0C0400u) |
+                                        __builtin_amdgcn_perm(yb[7], yb[6], 0x04000C0Cu);
+                    const uint32_t m0 = __builtin_amdgcn_perm(db[1], db[0], 0x0C0C0B09u) |
+                                        __builtin_amdgcn_perm(db[3], db[2], 0x0B090C0Cu);
+                    const uint32_t m1 = __builtin_amdgcn_perm(db[5], db[4], 0x0C0C0B09u) |
+                                        __builtin_amdgcn_perm(db[7], db[6], 0x0B090C0Cu);
+                    // 2z + 64: D8 -> 2(n + 32); D8+1/2 -> 2(n + 32) + 1 - 2[d < 0]
+                    const uint32_t hb = d8 ? 0u : 0x01010101u;
+                    const uint32_t hn = d8 ? 0u : 0x02020202u;
+                    uint32_t t0 = ((n0 << 1) | hb) - (m0 & hn);
+                    uint32_t t1 = ((n1 << 1) | hb) - (m1 & hn);
+                    // parity fix: first coordinate with |d| equal to the max (D8) or min (D8+1/2)
+                    const float tgt = d8 ? amax : amin;
+                    const bool fixon = d8 ? odd0 : odd1;
+                    bool acc = false, f[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const bool e = fabsf(d[i]) == tgt;
+                        f[i] = e && !acc && fixon;
+                        acc = acc || e;
+                    }
+                    uint32_t sel0 = f[3] ? 0xFF000000u : 0u;
+                    sel0 = f[2] ? 0x00FF0000u : sel0;
+                    sel0 = f[1] ? 0x0000FF00u : sel0;
+                    sel0 = f[0] ? 0x000000FFu : sel0;
+                    uint32_t sel1 = f[7] ? 0xFF000000u : 0u;
+                    sel1 = f[6] ? 0x00FF0000u : sel1;
+                    sel1 = f[5] ? 0x0000FF00u : sel1;
+                    sel1 = f[4] ? 0x000000FFu : sel1;
+                    // D8 moves the coordinate by +2 sgn(d), D8+1/2 by -2 sgn(d)
+                    const uint32_t dm = d8 ? 0u : 0xFFFFFFFFu;
+                    const uint32_t mx0 = m0 ^ dm, mx1 = m1 ^ dm;
+                    t0 = t0 + (sel0 & ~mx0 & 0x02020202u) - (sel0 & mx0 & 0x02020202u);
+                    t1 = t1 + (sel1 & ~mx1 & 0x02020202u) - (sel1 & mx1 & 0x02020202u);
+                    const uint32_t qa = __builtin_amdgcn_udot4(t0, t0, 0u, false);
+                    const uint32_t sa4 = __builtin_amdgcn_udot4(t0, 0x01010101u, 0u, false);
+                    const uint32_t qb = __builtin_amdgcn_udot4(t1, t1, 0u, false);
+                    const uint32_t sb4 = __builtin_amdgcn_udot4(t1, 0x01010101u, 0u, false);
+                    const int na = int(qa) - 128 * int(sa4) + 16384;
+                    const int nb = int(qb) - 128 * int(sb4) + 16384;
+                    escaped = live && uint32_t(na + nb) > a.core_bound;
+                    const uint32_t fi = __builtin_amdgcn_udot4(t0, a.wpk, d8 ? a.ka[0] : a.ka[1], false) >> 1;
+                    const uint32_t gb = __builtin_amdgcn_udot4(t1, a.wpk, d8 ? a.kb[0] : a.kb[1], false) >> 1;
+                    const uint32_t state = uint32_t(na >> 1) + ((sa4 >> 1) & 1u);
+                    if (!escaped) cidx = uint32_t(tab[fi]) + uint32_t(tab[gb + state * a.rp.nh]);
+                    done = true;
+                }
             }
-            uint32_t norm = 0;   // <= 8 * 16386^2 < 2^32
-#pragma unroll
-            for (int i = 0; i < 8; ++i) norm += uint32_t(t[i] * t[i]);
-            const bool escaped = live && norm > uint32_t(a.core_bound);
-            if (live) a.core_idx[g] = escaped ? uint16_t(0xFFFF) : uint16_t(core_rank(t, tab, a.rp));
-            if (a.two_z) {
-                uint32_t f8 = 0;
-                const uint2 p = pack_i8x8(t, f8);
-                if (live) {
-                    *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = p;
+            if (!done) {
+                int t[8];
+                const uint32_t inv = exact_point(x, craw, t);
+                if (live) flags |= inv;
+                escaped = live && norm_u32(t) > a.core_bound;
+                if (!escaped) cidx = core_rank(t, tab, a.rp);
+                if (a.two_z && live) {
+                    uint32_t f8 = 0;
+                    *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = pack_i8x8(t, f8);
                     flags |= f8;
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                rec[j][i] = (uint32_t(t[2 * i]) & 0xFFFFu) | (uint32_t(t[2 * i + 1]) << 16);
+            if (live) a.core_idx[g] = uint16_t(escaped ? 0xFFFFu : cidx);
             const uint64_t mask = __ballot(escaped);
-            in_wave[j] = __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
-            if (lane == 0) s_cnt[j][wv] = uint32_t(__popcll(mask));
-            esc_bits |= escaped ? (1u << j) : 0u;
+            if (lane == 0) {
+                s_cnt[j * kWaves + wv] = uint32_t(__popcll(mask));
+                s_ball[j][wv] = mask;
+            }
             if (mask) {
                 const uint32_t b = live ? fdiv(g, a.gpb_div) : 0u;
                 const uint32_t b0 = __shfl(b, 0, 64);
@@ -182,23 +384,18 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         flush_status(flags, a.status);
         __syncthreads();
 
-        // Exclusive offsets of every (item, wave) inside the tile, item-major:
-        // that is ascending group order.
-        if (tid == 0) {
-            uint32_t run = 0;
-            for (int j = 0; j < kItems; ++j)
-                for (int k = 0; k < kBlock / kWave; ++k) {
-                    const uint32_t c = s_cnt[j][k];
-                    s_cnt[j][k] = run;
-                    run += c;
-                }
-            s_total = run;
-        }
-        __syncthreads();
-
-        // Decoupled look-back (first wave).
+        // First wave: exclusive scan of the (item, wave) counts in ascending
+        // group order, then the decoupled look-back for the tile offset.
         if (wv == 0) {
-            const unsigned long long total = s_total;
+            const uint32_t c = s_cnt[lane];
+            uint32_t incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t o = __shfl_up(incl, off, 64);
+                if (lane >= uint32_t(off)) incl += o;
+            }
+            s_cnt[lane] = incl - c;
+            const unsigned long long total = __shfl(incl, 63, 64);
             unsigned long long excl = 0;
             bool timeout = false;
             if (tile == 0) {
@@ -208,10 +405,10 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
                 if (lane == 0)
                     __hip_atomic_store(a.tile_status + tile, kFlagA | total, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-                int64_t j = int64_t(tile) - 1;
+                int64_t jj = int64_t(tile) - 1;
                 uint32_t spins = 0;
                 for (;;) {
-                    const int64_t idx = j - int64_t(lane);
+                    const int64_t idx = jj - int64_t(lane);
                     const unsigned long long v =
                         idx >= 0 ? __hip_atomic_load(a.tile_status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                  : kFlagP;
@@ -233,7 +430,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
                     for (int off = 32; off >= 1; off >>= 1) val += shfl_xor_u64(val, off);
                     excl += val;
                     if (first_p < 64) break;
-                    j -= 64;
+                    jj -= 64;
                 }
                 if (lane == 0)
                     __hip_atomic_store(a.tile_status + tile, kFlagP | ((excl + total) & kValMask), __ATOMIC_RELAXED,
@@ -246,25 +443,38 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         }
         __syncthreads();
 
+        // Pass 2: records of the slices that have escapes.
         uint32_t oflags = 0;
-        if (esc_bits) {
-            const unsigned long long excl = s_excl;
+        const unsigned long long excl = s_excl;
+        for (int j = 0; j < kItems; ++j) {
+            const uint64_t mask = s_ball[j][wv];
+            if (mask == 0ull) continue;               // wave-uniform
+            const uint32_t g = tbase + uint32_t(j) * kBlock;
+            const bool live = g < a.groups;
+            const uint32_t row = live ? fdiv(g, a.gpr_div) : 0u;
+            float v[8];
+            rotate_raw<WT, HB>(a, s_smask, load_raw<WT>(a, g, live), g, live, row, lf, v);
+            const float craw = a.coef[row];
+            const float cl = __uint_as_float(__float_as_uint(craw) ^ lf.sign);
+            float x[8];
 #pragma unroll
-            for (int j = 0; j < kItems; ++j) {
-                if (esc_bits & (1u << j)) {
-                    const uint32_t g = tile * kTileGroups + uint32_t(j) * kBlock + tid;
-                    const unsigned long long pos = excl + s_cnt[j][wv] + in_wave[j];
-                    if (pos < a.esc_cap) {
-                        const uint32_t grp = g - fdiv(g, a.gpb_div) * a.gpb_div.d;
-                        uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
-                        dst[0] = grp;
-                        dst[1] = rec[j][0];
-                        dst[2] = rec[j][1];
-                        dst[3] = rec[j][2];
-                        dst[4] = rec[j][3];
-                    } else {
-                        oflags |= E8Q_STATUS_ESC_OVERFLOW;
-                    }
+            for (int i = 0; i < 8; ++i) x[i] = v[i] * cl;
+            if ((mask >> lane) & 1ull) {
+                int t[8];
+                exact_point(x, craw, t);
+                // records go in group order: count escapes at lower logical positions
+                const uint64_t lmask = logical_lane_mask(mask);
+                const uint32_t lpos = lane_off;   // 0..63 inside the wave's 64 groups
+                const uint32_t rank_in_wave = uint32_t(__popcll(lmask & ((1ull << lpos) - 1ull)));
+                const unsigned long long pos = excl + s_cnt[j * kWaves + wv] + rank_in_wave;
+                if (pos < a.esc_cap) {
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
+                    dst[0] = g - fdiv(g, a.gpb_div) * a.gpb_div.d;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dst[1 + i] = (uint32_t(t[2 * i]) & 0xFFFFu) | (uint32_t(t[2 * i + 1]) << 16);
+                } else {
+                    oflags |= E8Q_STATUS_ESC_OVERFLOW;
                 }
             }
         }
@@ -308,6 +518,7 @@ const DevTable* get_table(int32_t bound, e8q_status_t& err) {
         return nullptr;
     }
     if (hipMemcpy(t.dptr, t.host.data.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(t.dptr);
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }
@@ -320,15 +531,17 @@ uint32_t tiles_for(int64_t batch, int64_t rows, int64_t cols) {
     return uint32_t((groups + kTileGroups - 1) / kTileGroups);
 }
 
-template <typename WT, bool LDS>
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+template <typename WT, bool LDS, bool FAST>
 void launch_encode(int hb, const EncodeArgs& a, unsigned grid, size_t lds, hipStream_t st) {
     switch (hb) {
-        case 0: hipLaunchKernelGGL((encode_kernel<WT, 0, LDS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 8: hipLaunchKernelGGL((encode_kernel<WT, 8, LDS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((encode_kernel<WT, 16, LDS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((encode_kernel<WT, 32, LDS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 64: hipLaunchKernelGGL((encode_kernel<WT, 64, LDS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 128: hipLaunchKernelGGL((encode_kernel<WT, 128, LDS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 0: hipLaunchKernelGGL((encode_kernel<WT, 0, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 8: hipLaunchKernelGGL((encode_kernel<WT, 8, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 16: hipLaunchKernelGGL((encode_kernel<WT, 16, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 32: hipLaunchKernelGGL((encode_kernel<WT, 32, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 64: hipLaunchKernelGGL((encode_kernel<WT, 64, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 128: hipLaunchKernelGGL((encode_kernel<WT, 128, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
         default: break;
     }
 }
@@ -341,11 +554,16 @@ int64_t core_size_host(int32_t bound) {
     return t.size;
 }
 
+size_t encode_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
+    return kWsHeader + align256(sizeof(unsigned long long) * size_t(tiles_for(batch, rows, cols))) +
+           align256(sizeof(float) * size_t(batch) * size_t(rows));
+}
+
 }  // namespace e8q
 
 extern "C" size_t e8q_encode_workspace_size(int64_t batch, int64_t rows, int64_t cols) {
     if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 8) return 0;
-    return e8q::kWsHeader + sizeof(unsigned long long) * size_t(e8q::tiles_for(batch, rows, cols));
+    return e8q::encode_ws_bytes(batch, rows, cols);
 }
 
 extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtype, int64_t batch,
@@ -373,43 +591,65 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
     }
     const DevTable* tab = get_table(core_bound, st);
     if (!tab) return st;
+    const RankParams& rp = tab->host.p;
 
     const uint32_t gpr = uint32_t(cols / 8);
+    const uint32_t rows_total = uint32_t(batch * rows);
     EncodeArgs a;
     a.w = w;
     a.groups = uint32_t(uint64_t(batch) * uint64_t(rows) * gpr);
     a.gpr = gpr;
     a.gpr_div = make_fastdiv(gpr);
     a.gpb_div = make_fastdiv(uint32_t(uint64_t(rows) * gpr));
-    a.scale = row_scale;
     a.signs = signs;
-    a.kappa = kappa_for(hb);
-    a.core_bound = core_bound;
+    a.cols = uint32_t(cols);
+    a.core_bound = uint32_t(core_bound);
     a.tab = tab->dptr;
-    a.rp = tab->host.p;
+    a.rp = rp;
+    const uint32_t ub = rp.ub;
+    a.wpk = (ub * ub * ub) | ((ub * ub) << 8) | (ub << 16) | (1u << 24);
+    const uint32_t sumw = ub * ub * ub + ub * ub + ub + 1u;
+    for (int c = 0; c < 2; ++c) {
+        const uint32_t bias = uint32_t(int32_t(rp.tm[c]) - 64) * sumw;   // mod 2^32
+        a.ka[c] = bias + 2u * uint32_t(c) * rp.nh;
+        a.kb[c] = bias + 2u * (2u * rp.nh + uint32_t(c) * rp.nstate * rp.nh);
+    }
     a.core_idx = core_idx_out;
     a.esc = esc_out;
     a.esc_cap = uint64_t(esc_capacity);
     a.esc_count = reinterpret_cast<unsigned long long*>(esc_count_out);
     a.two_z = two_z_out;
-    a.tile_counter = reinterpret_cast<uint32_t*>(workspace);
-    a.tile_status = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + kWsHeader);
+    char* ws = static_cast<char*>(workspace);
     a.num_tiles = tiles_for(batch, rows, cols);
+    a.tile_counter = reinterpret_cast<uint32_t*>(ws);
+    a.tile_status = reinterpret_cast<unsigned long long*>(ws + kWsHeader);
+    float* coef = reinterpret_cast<float*>(ws + kWsHeader + align256(sizeof(unsigned long long) * a.num_tiles));
+    a.coef = coef;
     a.status = status_dev;
 
+    const size_t smask_bytes = hb > 0 ? size_t(cols / 2) * 4 : 0;
+    const size_t tab_bytes = size_t(rp.entries) * sizeof(uint16_t);
+    if (smask_bytes > kLdsLimit) return E8Q_ERR_UNSUPPORTED;   // rows too wide for the LDS sign masks
+
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const uint32_t init_items = a.num_tiles > uint32_t(batch) ? a.num_tiles : uint32_t(batch);
-    hipLaunchKernelGGL(encode_init_kernel, dim3(grid_for(init_items, 256, 4)), dim3(256), 0, s,
-                       a.tile_counter, a.tile_status, a.num_tiles, a.esc_count, uint32_t(batch));
-    const unsigned grid = grid_for(a.num_tiles, 1, 4);
-    const bool lds = core_bound <= kLdsTableMaxBound;
-    const size_t lds_bytes = lds ? size_t(a.rp.entries) * sizeof(uint16_t) : 0;
+    uint32_t init_items = a.num_tiles;
+    if (uint32_t(batch) > init_items) init_items = uint32_t(batch);
+    if (rows_total > init_items) init_items = rows_total;
+    hipLaunchKernelGGL(encode_init_kernel, dim3(grid_for(init_items, 256, 4)), dim3(256), 0, s, a.tile_counter,
+                       a.tile_status, a.num_tiles, a.esc_count, uint32_t(batch), row_scale, coef, rows_total,
+                       kappa_for(hb));
+
+    const bool lds_tab = smask_bytes + tab_bytes <= kLdsLimit;
+    const size_t lds = smask_bytes + (lds_tab ? tab_bytes : 0);
+    const bool fast = lds_tab && w_dtype == E8Q_BF16 && !two_z_out && ub <= 6;
+    const unsigned grid = grid_for(a.num_tiles, 1, 2);
     if (w_dtype == E8Q_BF16) {
-        if (lds) launch_encode<uint16_t, true>(hb, a, grid, lds_bytes, s);
-        else launch_encode<uint16_t, false>(hb, a, grid, 0, s);
+        if (fast) launch_encode<uint16_t, true, true>(hb, a, grid, lds, s);
+        else if (lds_tab) launch_encode<uint16_t, true, false>(hb, a, grid, lds, s);
+        else launch_encode<uint16_t, false, false>(hb, a, grid, lds, s);
     } else {
-        if (lds) launch_encode<float, true>(hb, a, grid, lds_bytes, s);
-        else launch_encode<float, false>(hb, a, grid, 0, s);
+        if (lds_tab) launch_encode<float, true, false>(hb, a, grid, lds, s);
+        else launch_encode<float, false, false>(hb, a, grid, lds, s);
     }
     return launch_status();
 }

@@ -35,8 +35,10 @@ __global__ __launch_bounds__(256) void project_kernel(ProjectArgs a) {
     const uint32_t lane = __lane_id();
     const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
     const uint32_t nwaves = gridDim.x * blockDim.x / kWave;
+    const LaneFwht lf = lane_fwht<HB>(lane);
+    const uint32_t lane_off = (lane & ~15u) + lf.logical;
     for (uint64_t base = uint64_t(wave) * kWave; base < a.groups; base += uint64_t(nwaves) * kWave) {
-        const uint32_t g = uint32_t(base) + lane;
+        const uint32_t g = uint32_t(base) + lane_off;
         const bool live = g < a.groups;
         float v[8];
         if (live) {
@@ -47,18 +49,26 @@ __global__ __launch_bounds__(256) void project_kernel(ProjectArgs a) {
         }
         const uint32_t row = live ? fdiv(g, a.gpr_div) : 0u;
         const uint32_t col0 = (g - row * a.gpr) * 8u;
+        float kap = a.kappa;
         if constexpr (HB > 0) {
             if (live) apply_signs(a.signs, col0, v);
-            fwht_group<HB>(v, lane);
+            fwht_inlane<HB>(v);
+            fwht_xlane<HB>(v, lf.eps);
+            // the lane holds the transform times (-1)^popcount(L): fold it in
+            kap = __uint_as_float(__float_as_uint(kap) ^ lf.sign);
             if (a.rotated && live) {
                 float4* dst = reinterpret_cast<float4*>(a.rotated + uint64_t(g) * 8);
-                dst[0] = make_float4(v[0] * a.kappa, v[1] * a.kappa, v[2] * a.kappa, v[3] * a.kappa);
-                dst[1] = make_float4(v[4] * a.kappa, v[5] * a.kappa, v[6] * a.kappa, v[7] * a.kappa);
+                // fma(v, kap, +0) rounds like v * kap and turns an exact -0 into +0
+                dst[0] = make_float4(fmaf(v[0], kap, 0.0f), fmaf(v[1], kap, 0.0f), fmaf(v[2], kap, 0.0f),
+                                     fmaf(v[3], kap, 0.0f));
+                dst[1] = make_float4(fmaf(v[4], kap, 0.0f), fmaf(v[5], kap, 0.0f), fmaf(v[6], kap, 0.0f),
+                                     fmaf(v[7], kap, 0.0f));
             }
         }
         const float s = a.scale[row];
         bool bad;
-        const float c = row_coef(s, a.kappa, bad);
+        const float c0 = row_coef(s, a.kappa, bad);
+        const float c = __uint_as_float(__float_as_uint(c0) ^ (HB > 0 ? lf.sign : 0u));
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = v[i] * c;

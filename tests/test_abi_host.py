@@ -51,8 +51,9 @@ def test_workspace_size(L):
     assert L.e8q_encode_workspace_size(1, 1, 12) == 0
     assert L.e8q_encode_workspace_size(0, 4, 8) == 0
     groups = 128 * 4096 * 4096 // 8
-    tiles = (groups + 2047) // 2048
-    assert L.e8q_encode_workspace_size(128, 4096, 4096) == 256 + 8 * tiles
+    tiles = (groups + 4095) // 4096
+    a256 = lambda v: (v + 255) // 256 * 256
+    assert L.e8q_encode_workspace_size(128, 4096, 4096) == 256 + a256(8 * tiles) + a256(4 * 128 * 4096)
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first

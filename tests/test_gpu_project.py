@@ -1,9 +1,9 @@
 """GPU parity of e8q_project / e8q_project_hadamard against the CPU oracle.
 
-Bit-exact on 2z (int8), bf16 q, float32 q and the rotated values (the
-tolerance allowed by the contract for float32 outputs is 1e-6 relative; the
-canonical operation order makes them equal bit for bit, which is what is
-checked)."""
+Bit-exact on 2z (int8), bf16 q and float32 q.  Rotated values: the contract
+allows 1e-6 relative; they are checked to be equal as values (the canonical
+operation order makes every non-zero value bit-identical; an exact zero may
+differ in sign)."""
 
 import numpy as np
 import pytest
@@ -30,7 +30,9 @@ def _compare(out, ref, q_bf16=True, rotated=False):
         u, v = out["u"].reshape(-1), ref["u"].reshape(-1)
         rel = np.abs(u.astype(np.float64) - v) / np.maximum(np.abs(v.astype(np.float64)), 1e-30)
         assert rel.max() <= 1e-6
-        assert first_mismatch(u.view(np.uint32), v.view(np.uint32)) is None
+        # equal as values (the contract's bar is 1e-6 relative); the sign of an
+        # exact zero is the only freedom left
+        assert np.array_equal(u, v)
     assert out["status"] == ref["status"], (out["status"], ref["status"])
 
 
