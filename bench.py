@@ -169,6 +169,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 4 GiB device copy (known bytes) for counter scaling")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -182,6 +184,13 @@ def main():
     import bit_e8_lattice_amd as e8q
     from bit_e8_lattice_amd import workloads
     e8q.lib()
+    if args.copy_calibration:
+        n = 1 << 30                       # 4 GiB of float32 read, 4 GiB written
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     r = run_dense_decoder(args, torch, e8q, workloads)
     if r["status"] != 0:
         print(f"warning: device status bits {r['status']:#x}", file=sys.stderr)

@@ -232,6 +232,12 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
     }
     const LaneFwht lf = lane_fwht<HB>(lane);
     const uint32_t lane_off = (lane & ~15u) + lf.logical;
+    uint32_t kav[2], kbv[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        asm volatile("v_mov_b32 %0, %1" : "=v"(kav[c]) : "s"(a.ka[c]));
+        asm volatile("v_mov_b32 %0, %1" : "=v"(kbv[c]) : "s"(a.kb[c]));
+    }
 
     for (;;) {
         __syncthreads();
@@ -242,28 +248,30 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         const uint32_t tbase = tile * kTileGroups + wv * kWave + lane_off;
 
         uint32_t flags = 0;
-        // loads run two items ahead of the arithmetic
+        // Loads run two items ahead of the arithmetic; lanes past the end read
+        // the last group instead (nothing is stored for them).
+        const uint32_t glast = a.groups - 1u;
         uint32_t g1 = tbase, g2 = tbase + kBlock;
-        bool l1 = g1 < a.groups, l2 = g2 < a.groups;
-        uint32_t r1 = l1 ? fdiv(g1, a.gpr_div) : 0u, r2 = l2 ? fdiv(g2, a.gpr_div) : 0u;
-        Raw<WT> w1 = load_raw<WT>(a, g1, l1), w2 = load_raw<WT>(a, g2, l2);
+        uint32_t r1 = fdiv(min(g1, glast), a.gpr_div), r2 = fdiv(min(g2, glast), a.gpr_div);
+        Raw<WT> w1 = load_raw<WT>(a, min(g1, glast), true), w2 = load_raw<WT>(a, min(g2, glast), true);
         float c1 = a.coef[r1], c2 = a.coef[r2];
+#pragma unroll
         for (int j = 0; j < kItems; ++j) {
             const uint32_t g = g1;
-            const bool live = l1;
+            const bool live = g < a.groups;
             const uint32_t row = r1;
             const Raw<WT> raw = w1;
             const float craw = c1;
-            g1 = g2; l1 = l2; r1 = r2; w1 = w2; c1 = c2;
+            g1 = g2; r1 = r2; w1 = w2; c1 = c2;
             if (j + 2 < kItems) {
                 g2 = g + 2u * kBlock;
-                l2 = g2 < a.groups;
-                r2 = l2 ? fdiv(g2, a.gpr_div) : 0u;
-                w2 = load_raw<WT>(a, g2, l2);
+                const uint32_t gl = min(g2, glast);
+                r2 = fdiv(gl, a.gpr_div);
+                w2 = load_raw<WT>(a, gl, true);
                 c2 = a.coef[r2];
             }
             float v[8];
-            rotate_raw<WT, HB>(a, s_smask, raw, g, live, row, lf, v);
+            rotate_raw<WT, HB>(a, s_smask, raw, min(g, glast), true, row, lf, v);
             const float cl = __uint_as_float(__float_as_uint(craw) ^ lf.sign);
             float x[8];
 #pragma unroll
@@ -273,43 +281,46 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
             uint32_t cidx = 0xFFFFu;
             bool done = false;
             if constexpr (FAST) {
-                float y[8], d[8];
+                float d[8];
+                uint32_t yb[8], db[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    y[i] = x[i] + kMagic;
-                    const float nf = y[i] - kMagic;
-                    d[i] = x[i] - nf;
+                    const float y = x[i] + kMagic;     // low byte of the bits: rint(x) + 32
+                    d[i] = x[i] - (y - kMagic);
+                    yb[i] = __float_as_uint(y);
+                    db[i] = __float_as_uint(d[i]);
                 }
+                // n_i + 32 bytes and (d_i < 0 ? 0xFF : 0) bytes, four per word
+                const uint32_t n0 = __builtin_amdgcn_perm(yb[1], yb[0], 0x0C0C0400u) |
+                                    __builtin_amdgcn_perm(yb[3], yb[2], 0x04000C0Cu);
+                const uint32_t n1 = __builtin_amdgcn_perm(yb[5], yb[4], 0x0C0C0400u) |
+                                    __builtin_amdgcn_perm(yb[7], yb[6], 0x04000C0Cu);
+                const uint32_t m0 = __builtin_amdgcn_perm(db[1], db[0], 0x0C0C0B09u) |
+                                    __builtin_amdgcn_perm(db[3], db[2], 0x0B090C0Cu);
+                const uint32_t m1 = __builtin_amdgcn_perm(db[5], db[4], 0x0C0C0B09u) |
+                                    __builtin_amdgcn_perm(db[7], db[6], 0x0B090C0Cu);
+                // parity of sum(n) and of sum(floor) = sum(n) - #(d < 0)
+                const uint32_t nsum = __builtin_amdgcn_udot4(n0, 0x01010101u,
+                                                             __builtin_amdgcn_udot4(n1, 0x01010101u, 0u, false), false);
+                const uint32_t negs8 = uint32_t(__builtin_popcount(m0)) + uint32_t(__builtin_popcount(m1));
+                const bool odd0 = (nsum & 1u) != 0u;
+                const bool odd1 = ((nsum + (negs8 >> 3)) & 1u) != 0u;
                 const float sa = ((fabsf(d[0]) + fabsf(d[1])) + (fabsf(d[2]) + fabsf(d[3]))) +
                                  ((fabsf(d[4]) + fabsf(d[5])) + (fabsf(d[6]) + fabsf(d[7])));
                 const float amax = fmaxf(fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3]))),
                                          fmaxf(fmaxf(fabsf(d[4]), fabsf(d[5])), fmaxf(fabsf(d[6]), fabsf(d[7]))));
                 const float amin = fminf(fminf(fminf(fabsf(d[0]), fabsf(d[1])), fminf(fabsf(d[2]), fabsf(d[3]))),
                                          fminf(fminf(fabsf(d[4]), fabsf(d[5])), fminf(fabsf(d[6]), fabsf(d[7]))));
-                const float xmax = fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
-                                         fmaxf(fmaxf(fabsf(x[4]), fabsf(x[5])), fmaxf(fabsf(x[6]), fabsf(x[7]))));
-                uint32_t yb[8], db[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { yb[i] = __float_as_uint(y[i]); db[i] = __float_as_uint(d[i]); }
-                const uint32_t py = ((yb[0] ^ yb[1]) ^ (yb[2] ^ yb[3])) ^ ((yb[4] ^ yb[5]) ^ (yb[6] ^ yb[7]));
-                const uint32_t pd = ((db[0] ^ db[1]) ^ (db[2] ^ db[3])) ^ ((db[4] ^ db[5]) ^ (db[6] ^ db[7]));
-                const bool odd0 = (py & 1u) != 0u;
-                const bool odd1 = odd0 != ((pd >> 31) != 0u);
+                const float xmax = fmaxf(fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fabsf(x[2])),
+                                               fmaxf(fmaxf(fabsf(x[3]), fabsf(x[4])), fabsf(x[5]))),
+                                         fmaxf(fabsf(x[6]), fabsf(x[7])));
+                // coset decision in float32 (trusted when clear of its rounding error)
                 const float tq0 = sa - 2.0f;
-                const float tq1 = odd0 ? tq0 + (1.0f - 2.0f * amax) : tq0;
-                const float tq = odd1 ? tq1 - 2.0f * amin : tq1;
+                const float tq1 = odd0 ? tq0 + fmaf(-2.0f, amax, 1.0f) : tq0;
+                const float tq = odd1 ? fmaf(-2.0f, amin, tq1) : tq1;
                 const bool fast = (xmax < kFastXMax) && (amin > 0.0f) && (fabsf(tq) > kFastDecision);
                 if (fast) {
                     const bool d8 = tq < 0.0f;
-                    // n_i + 32 bytes and (d_i < 0 ? 0xFF : 0) bytes, four per word
-                    const uint32_t n0 = __builtin_amdgcn_perm(yb[1], yb[0], 0x0C0C0400u) |
-                                        __builtin_amdgcn_perm(yb[3], yb[2], 0x04000C0Cu);
-                    const uint32_t n1 = __builtin_amdgcn_perm(yb[5], yb[4], 0x0C0C0400u) |
-                                        __builtin_amdgcn_perm(yb[7], yb[6], 0x04000C0Cu);
-                    const uint32_t m0 = __builtin_amdgcn_perm(db[1], db[0], 0x0C0C0B09u) |
-                                        __builtin_amdgcn_perm(db[3], db[2], 0x0B090C0Cu);
-                    const uint32_t m1 = __builtin_amdgcn_perm(db[5], db[4], 0x0C0C0B09u) |
-                                        __builtin_amdgcn_perm(db[7], db[6], 0x0B090C0Cu);
                     // 2z + 64: D8 -> 2(n + 32); D8+1/2 -> 2(n + 32) + 1 - 2[d < 0]
                     const uint32_t hb = d8 ? 0u : 0x01010101u;
                     const uint32_t hn = d8 ? 0u : 0x02020202u;
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
                     uint32_t t1 = ((n1 << 1) | hb) - (m1 & hn);
                     // parity fix: first coordinate with |d| equal to the max (D8) or min (D8+1/2)
                     const float tgt = d8 ? amax : amin;
-                    const bool fixon = d8 ? odd0 : odd1;
+                    const bool fixon = (d8 && odd0) || (!d8 && odd1);
                     bool acc = false, f[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -336,19 +347,22 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
                     // D8 moves the coordinate by +2 sgn(d), D8+1/2 by -2 sgn(d)
                     const uint32_t dm = d8 ? 0u : 0xFFFFFFFFu;
                     const uint32_t mx0 = m0 ^ dm, mx1 = m1 ^ dm;
-                    t0 = t0 + (sel0 & ~mx0 & 0x02020202u) - (sel0 & mx0 & 0x02020202u);
-                    t1 = t1 + (sel1 & ~mx1 & 0x02020202u) - (sel1 & mx1 & 0x02020202u);
+                    t0 = t0 + __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x20) -
+                         __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x80);
+                    t1 = t1 + __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x20) -
+                         __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x80);
                     const uint32_t qa = __builtin_amdgcn_udot4(t0, t0, 0u, false);
                     const uint32_t sa4 = __builtin_amdgcn_udot4(t0, 0x01010101u, 0u, false);
-                    const uint32_t qb = __builtin_amdgcn_udot4(t1, t1, 0u, false);
-                    const uint32_t sb4 = __builtin_amdgcn_udot4(t1, 0x01010101u, 0u, false);
-                    const int na = int(qa) - 128 * int(sa4) + 16384;
-                    const int nb = int(qb) - 128 * int(sb4) + 16384;
-                    escaped = live && uint32_t(na + nb) > a.core_bound;
-                    const uint32_t fi = __builtin_amdgcn_udot4(t0, a.wpk, d8 ? a.ka[0] : a.ka[1], false) >> 1;
-                    const uint32_t gb = __builtin_amdgcn_udot4(t1, a.wpk, d8 ? a.kb[0] : a.kb[1], false) >> 1;
-                    const uint32_t state = uint32_t(na >> 1) + ((sa4 >> 1) & 1u);
-                    if (!escaped) cidx = uint32_t(tab[fi]) + uint32_t(tab[gb + state * a.rp.nh]);
+                    const uint32_t qt = __builtin_amdgcn_udot4(t1, t1, qa, false);
+                    const uint32_t st = __builtin_amdgcn_udot4(t1, 0x01010101u, sa4, false);
+                    // sum (t + 64)^2 - 128 sum (t + 64) + 8 * 64^2 = ||2z||^2
+                    const uint32_t norm = qt - (st << 7) + 32768u;
+                    escaped = live && norm > a.core_bound;
+                    const uint32_t na = qa - (sa4 << 7) + 16384u;
+                    const uint32_t fi = __builtin_amdgcn_udot4(t0, a.wpk, d8 ? kav[0] : kav[1], false) >> 1;
+                    const uint32_t gb = __builtin_amdgcn_udot4(t1, a.wpk, d8 ? kbv[0] : kbv[1], false) >> 1;
+                    const uint32_t state = (na >> 1) + ((sa4 >> 1) & 1u);
+                    if (!escaped) cidx = uint32_t(tab[fi]) + uint32_t(tab[__umul24(state, a.rp.nh) + gb]);
                     done = true;
                 }
             }
@@ -642,7 +656,7 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
     const bool lds_tab = smask_bytes + tab_bytes <= kLdsLimit;
     const size_t lds = smask_bytes + (lds_tab ? tab_bytes : 0);
     const bool fast = lds_tab && w_dtype == E8Q_BF16 && !two_z_out && ub <= 6;
-    const unsigned grid = grid_for(a.num_tiles, 1, 2);
+    const unsigned grid = grid_for(a.num_tiles, 1, lds <= 50 * 1024 ? 3 : 2);
     if (w_dtype == E8Q_BF16) {
         if (fast) launch_encode<uint16_t, true, true>(hb, a, grid, lds, s);
         else if (lds_tab) launch_encode<uint16_t, true, false>(hb, a, grid, lds, s);
