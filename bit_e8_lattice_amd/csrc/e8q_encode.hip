@@ -33,21 +33,16 @@
 #include "e8q_core_table.hpp"
 #include "e8q_device.hpp"
 #include "e8q_host.hpp"
+#include "e8q_point.hpp"
 
 namespace e8q {
 
-constexpr int kBlock = 512;
-constexpr int kWaves = kBlock / kWave;
-constexpr int kItems = 8;                          // groups per thread per tile
-constexpr uint32_t kTileGroups = kItems * kBlock;  // 4096
 constexpr uint64_t kFlagA = 1ull << 62;            // aggregate published
 constexpr uint64_t kFlagP = 2ull << 62;            // inclusive prefix published
 constexpr uint64_t kValMask = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr size_t kWsHeader = 256;
 constexpr size_t kLdsLimit = 60 * 1024;   // dynamic LDS per block (static use is < 1 KB)
-constexpr float kMagic = 12582944.0f;              // 1.5 * 2^23 + 32
-constexpr float kFastXMax = 30.0f;
 
 struct EncodeArgs {
     const void* w;
@@ -73,23 +68,6 @@ struct EncodeArgs {
     uint32_t num_tiles;
     uint32_t* status;
 };
-
-// Unified-layout rank of a core point (|t_i| <= tm of its class).
-__device__ __forceinline__ uint32_t core_rank(const int (&t)[8], const uint16_t* tab, const RankParams& p) {
-    const uint32_t c = uint32_t(t[0]) & 1u;
-    const int tm = c ? p.tm[1] : p.tm[0];
-    uint32_t ha = 0, hb = 0;
-    int na = 0, sa = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ha = ha * p.ub + uint32_t((t[i] + tm) >> 1);
-        hb = hb * p.ub + uint32_t((t[4 + i] + tm) >> 1);
-        na += t[i] * t[i];
-        sa += t[i];
-    }
-    const uint32_t state = uint32_t(na >> 1) + (uint32_t(sa >> 1) & 1u);
-    return uint32_t(tab[c * p.nh + ha]) + uint32_t(tab[2u * p.nh + (c * p.nstate + state) * p.nh + hb]);
-}
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
     const uint32_t lo = __shfl_xor(uint32_t(v), m, 64);
@@ -125,83 +103,6 @@ __global__ void encode_init_kernel(uint32_t* counter, unsigned long long* tile_s
     }
 }
 
-// Raw input of one group: 16 bytes of bf16 (or 32 bytes of float32).
-template <typename WT>
-struct Raw {
-    uint4 p;
-    uint4 q;   // second half, float32 input only
-};
-
-template <typename WT>
-__device__ __forceinline__ Raw<WT> load_raw(const EncodeArgs& a, uint32_t g, bool live) {
-    Raw<WT> r;
-    r.p = make_uint4(0u, 0u, 0u, 0u);
-    r.q = make_uint4(0u, 0u, 0u, 0u);
-    if (live) {
-        if constexpr (sizeof(WT) == 2) {
-            r.p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.w) + uint64_t(g) * 8);
-        } else {
-            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(a.w) + uint64_t(g) * 8);
-            r.p = src[0];
-            r.q = src[1];
-        }
-    }
-    return r;
-}
-
-// Sign flip and Walsh-Hadamard rotation of one group; returns the lane's
-// stored values (the transform times the lane sign) in v.  All lanes of the
-// wave must be active.
-template <typename WT, int HB>
-__device__ __forceinline__ void rotate_raw(const EncodeArgs& a, const uint32_t* s_smask, Raw<WT> r, uint32_t g,
-                                           bool live, uint32_t row, const LaneFwht& lf, float (&v)[8]) {
-    if constexpr (HB > 0) {
-        if (live) {
-            const uint4 m = *reinterpret_cast<const uint4*>(s_smask + ((g - row * a.gpr) * 4u));
-            if constexpr (sizeof(WT) == 2) {
-                r.p.x ^= m.x; r.p.y ^= m.y; r.p.z ^= m.z; r.p.w ^= m.w;
-            } else {
-                r.p.x ^= m.x << 16; r.p.y ^= m.x & 0x80000000u;
-                r.p.z ^= m.y << 16; r.p.w ^= m.y & 0x80000000u;
-                r.q.x ^= m.z << 16; r.q.y ^= m.z & 0x80000000u;
-                r.q.z ^= m.w << 16; r.q.w ^= m.w & 0x80000000u;
-            }
-        }
-    }
-    if constexpr (sizeof(WT) == 2) {
-        v[0] = __uint_as_float(r.p.x << 16); v[1] = __uint_as_float(r.p.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(r.p.y << 16); v[3] = __uint_as_float(r.p.y & 0xFFFF0000u);
-        v[4] = __uint_as_float(r.p.z << 16); v[5] = __uint_as_float(r.p.z & 0xFFFF0000u);
-        v[6] = __uint_as_float(r.p.w << 16); v[7] = __uint_as_float(r.p.w & 0xFFFF0000u);
-    } else {
-        v[0] = __uint_as_float(r.p.x); v[1] = __uint_as_float(r.p.y);
-        v[2] = __uint_as_float(r.p.z); v[3] = __uint_as_float(r.p.w);
-        v[4] = __uint_as_float(r.q.x); v[5] = __uint_as_float(r.q.y);
-        v[6] = __uint_as_float(r.q.z); v[7] = __uint_as_float(r.q.w);
-    }
-    fwht_inlane<HB>(v);
-    fwht_xlane<HB>(v, lf.eps);
-}
-
-// Exact lattice point from normalized coordinates (invalid data -> 0).
-__device__ __forceinline__ uint32_t exact_point(const float (&x)[8], float coef_raw, int (&t)[8]) {
-    uint32_t inv = __builtin_isnan(coef_raw) ? uint32_t(E8Q_STATUS_BAD_SCALE) : group_invalid_bits(x);
-    if (inv) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = 0;
-    } else {
-        nearest_e8(x, t);
-    }
-    return inv;
-}
-
-__device__ __forceinline__ uint32_t norm_u32(const int (&t)[8]) {
-    uint32_t n = 0;   // <= 8 * 16386^2 < 2^32
-#pragma unroll
-    for (int i = 0; i < 8; ++i) n += uint32_t(t[i] * t[i]);
-    return n;
-}
-
 template <typename WT, int HB, bool LDS_TAB, bool FAST>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
     extern __shared__ uint32_t s_dyn[];
@@ -214,9 +115,11 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
     const uint32_t lane = tid & 63u;
     const uint32_t wv = tid >> 6;
 
-    // LDS: [sign masks: cols/2 words, when rotating][rank table, when LDS_TAB]
+    // LDS: [sign masks: cols/2 words][wide-block buffer: 8*kBlock floats][rank table]
     const uint32_t smask_words = HB > 0 ? a.cols / 2u : 0u;
+    const uint32_t wide_words = HB > 128 ? 8u * kBlock : 0u;
     uint32_t* s_smask = s_dyn;
+    float* s_wide = reinterpret_cast<float*>(s_dyn + smask_words);
     const uint16_t* tab = a.tab;
     if constexpr (HB > 0) {
         for (uint32_t i = tid; i < smask_words; i += kBlock) {
@@ -226,18 +129,20 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         }
     }
     if constexpr (LDS_TAB) {
-        uint16_t* t16 = reinterpret_cast<uint16_t*>(s_dyn + smask_words);
+        uint16_t* t16 = reinterpret_cast<uint16_t*>(s_dyn + smask_words + wide_words);
         for (uint32_t i = tid; i < a.rp.entries; i += kBlock) t16[i] = a.tab[i];
         tab = t16;
     }
-    const LaneFwht lf = lane_fwht<HB>(lane);
+    const LaneFwht lf = lane_fwht<(HB > 128 ? 128 : HB)>(lane);
     const uint32_t lane_off = (lane & ~15u) + lf.logical;
+    const uint32_t lpos = wv * kWave + lane_off;
     uint32_t kav[2], kbv[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         asm volatile("v_mov_b32 %0, %1" : "=v"(kav[c]) : "s"(a.ka[c]));
         asm volatile("v_mov_b32 %0, %1" : "=v"(kbv[c]) : "s"(a.kb[c]));
     }
+    const uint32_t glast = a.groups - 1u;
 
     for (;;) {
         __syncthreads();
@@ -245,34 +150,34 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         __syncthreads();
         const uint32_t tile = s_tile;
         if (tile >= a.num_tiles) break;
-        const uint32_t tbase = tile * kTileGroups + wv * kWave + lane_off;
+        const uint32_t tbase = tile * kTileGroups + lpos;
 
         uint32_t flags = 0;
         // Loads run two items ahead of the arithmetic; lanes past the end read
         // the last group instead (nothing is stored for them).
-        const uint32_t glast = a.groups - 1u;
         uint32_t g1 = tbase, g2 = tbase + kBlock;
         uint32_t r1 = fdiv(min(g1, glast), a.gpr_div), r2 = fdiv(min(g2, glast), a.gpr_div);
-        Raw<WT> w1 = load_raw<WT>(a, min(g1, glast), true), w2 = load_raw<WT>(a, min(g2, glast), true);
+        Raw w1 = load_raw<WT>(a.w, min(g1, glast)), w2 = load_raw<WT>(a.w, min(g2, glast));
         float c1 = a.coef[r1], c2 = a.coef[r2];
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
             const uint32_t g = g1;
             const bool live = g < a.groups;
+            const uint32_t gl = min(g, glast);
             const uint32_t row = r1;
-            const Raw<WT> raw = w1;
+            const Raw raw = w1;
             const float craw = c1;
             g1 = g2; r1 = r2; w1 = w2; c1 = c2;
             if (j + 2 < kItems) {
                 g2 = g + 2u * kBlock;
-                const uint32_t gl = min(g2, glast);
-                r2 = fdiv(gl, a.gpr_div);
-                w2 = load_raw<WT>(a, gl, true);
+                const uint32_t gn = min(g2, glast);
+                r2 = fdiv(gn, a.gpr_div);
+                w2 = load_raw<WT>(a.w, gn);
                 c2 = a.coef[r2];
             }
             float v[8];
-            rotate_raw<WT, HB>(a, s_smask, raw, min(g, glast), true, row, lf, v);
-            const float cl = __uint_as_float(__float_as_uint(craw) ^ lf.sign);
+            const uint32_t vsign = rotate_group<WT, HB>(s_smask, s_wide, raw, gl - row * a.gpr, lf, lpos, tid, v);
+            const float cl = __uint_as_float(__float_as_uint(craw) ^ vsign);
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = v[i] * cl;
@@ -281,76 +186,9 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
             uint32_t cidx = 0xFFFFu;
             bool done = false;
             if constexpr (FAST) {
-                float d[8];
-                uint32_t yb[8], db[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float y = x[i] + kMagic;     // low byte of the bits: rint(x) + 32
-                    d[i] = x[i] - (y - kMagic);
-                    yb[i] = __float_as_uint(y);
-                    db[i] = __float_as_uint(d[i]);
-                }
-                // n_i + 32 bytes and (d_i < 0 ? 0xFF : 0) bytes, four per word
-                const uint32_t n0 = __builtin_amdgcn_perm(yb[1], yb[0], 0x0C0C0400u) |
-                                    __builtin_amdgcn_perm(yb[3], yb[2], 0x04000C0Cu);
-                const uint32_t n1 = __builtin_amdgcn_perm(yb[5], yb[4], 0x0C0C0400u) |
-                                    __builtin_amdgcn_perm(yb[7], yb[6], 0x04000C0Cu);
-                const uint32_t m0 = __builtin_amdgcn_perm(db[1], db[0], 0x0C0C0B09u) |
-                                    __builtin_amdgcn_perm(db[3], db[2], 0x0B090C0Cu);
-                const uint32_t m1 = __builtin_amdgcn_perm(db[5], db[4], 0x0C0C0B09u) |
-                                    __builtin_amdgcn_perm(db[7], db[6], 0x0B090C0Cu);
-                // parity of sum(n) and of sum(floor) = sum(n) - #(d < 0)
-                const uint32_t nsum = __builtin_amdgcn_udot4(n0, 0x01010101u,
-                                                             __builtin_amdgcn_udot4(n1, 0x01010101u, 0u, false), false);
-                const uint32_t negs8 = uint32_t(__builtin_popcount(m0)) + uint32_t(__builtin_popcount(m1));
-                const bool odd0 = (nsum & 1u) != 0u;
-                const bool odd1 = ((nsum + (negs8 >> 3)) & 1u) != 0u;
-                const float sa = ((fabsf(d[0]) + fabsf(d[1])) + (fabsf(d[2]) + fabsf(d[3]))) +
-                                 ((fabsf(d[4]) + fabsf(d[5])) + (fabsf(d[6]) + fabsf(d[7])));
-                const float amax = fmaxf(fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3]))),
-                                         fmaxf(fmaxf(fabsf(d[4]), fabsf(d[5])), fmaxf(fabsf(d[6]), fabsf(d[7]))));
-                const float amin = fminf(fminf(fminf(fabsf(d[0]), fabsf(d[1])), fminf(fabsf(d[2]), fabsf(d[3]))),
-                                         fminf(fminf(fabsf(d[4]), fabsf(d[5])), fminf(fabsf(d[6]), fabsf(d[7]))));
-                const float xmax = fmaxf(fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fabsf(x[2])),
-                                               fmaxf(fmaxf(fabsf(x[3]), fabsf(x[4])), fabsf(x[5]))),
-                                         fmaxf(fabsf(x[6]), fabsf(x[7])));
-                // coset decision in float32 (trusted when clear of its rounding error)
-                const float tq0 = sa - 2.0f;
-                const float tq1 = odd0 ? tq0 + fmaf(-2.0f, amax, 1.0f) : tq0;
-                const float tq = odd1 ? fmaf(-2.0f, amin, tq1) : tq1;
-                const bool fast = (xmax < kFastXMax) && (amin > 0.0f) && (fabsf(tq) > kFastDecision);
-                if (fast) {
-                    const bool d8 = tq < 0.0f;
-                    // 2z + 64: D8 -> 2(n + 32); D8+1/2 -> 2(n + 32) + 1 - 2[d < 0]
-                    const uint32_t hb = d8 ? 0u : 0x01010101u;
-                    const uint32_t hn = d8 ? 0u : 0x02020202u;
-                    uint32_t t0 = ((n0 << 1) | hb) - (m0 & hn);
-                    uint32_t t1 = ((n1 << 1) | hb) - (m1 & hn);
-                    // parity fix: first coordinate with |d| equal to the max (D8) or min (D8+1/2)
-                    const float tgt = d8 ? amax : amin;
-                    const bool fixon = (d8 && odd0) || (!d8 && odd1);
-                    bool acc = false, f[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const bool e = fabsf(d[i]) == tgt;
-                        f[i] = e && !acc && fixon;
-                        acc = acc || e;
-                    }
-                    uint32_t sel0 = f[3] ? 0xFF000000u : 0u;
-                    sel0 = f[2] ? 0x00FF0000u : sel0;
-                    sel0 = f[1] ? 0x0000FF00u : sel0;
-                    sel0 = f[0] ? 0x000000FFu : sel0;
-                    uint32_t sel1 = f[7] ? 0xFF000000u : 0u;
-                    sel1 = f[6] ? 0x00FF0000u : sel1;
-                    sel1 = f[5] ? 0x0000FF00u : sel1;
-                    sel1 = f[4] ? 0x000000FFu : sel1;
-                    // D8 moves the coordinate by +2 sgn(d), D8+1/2 by -2 sgn(d)
-                    const uint32_t dm = d8 ? 0u : 0xFFFFFFFFu;
-                    const uint32_t mx0 = m0 ^ dm, mx1 = m1 ^ dm;
-                    t0 = t0 + __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x20) -
-                         __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x80);
-                    t1 = t1 + __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x20) -
-                         __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x80);
+                uint32_t t0, t1;
+                bool d8;
+                if (fast_point(x, t0, t1, d8)) {
                     const uint32_t qa = __builtin_amdgcn_udot4(t0, t0, 0u, false);
                     const uint32_t sa4 = __builtin_amdgcn_udot4(t0, 0x01010101u, 0u, false);
                     const uint32_t qt = __builtin_amdgcn_udot4(t1, t1, qa, false);
@@ -368,7 +206,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
             }
             if (!done) {
                 int t[8];
-                const uint32_t inv = exact_point(x, craw, t);
+                const uint32_t inv = exact_point(x, __builtin_isnan(craw), t);
                 if (live) flags |= inv;
                 escaped = live && norm_u32(t) > a.core_bound;
                 if (!escaped) cidx = core_rank(t, tab, a.rp);
@@ -457,29 +295,40 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         }
         __syncthreads();
 
-        // Pass 2: records of the slices that have escapes.
+        // Pass 2: records of the slices that have escapes (recomputed on the
+        // exact path; wide blocks need the whole block, so the condition is
+        // block-uniform for them and wave-uniform otherwise).
         uint32_t oflags = 0;
         const unsigned long long excl = s_excl;
         for (int j = 0; j < kItems; ++j) {
             const uint64_t mask = s_ball[j][wv];
-            if (mask == 0ull) continue;               // wave-uniform
+            bool any;
+            if constexpr (HB > 128) {
+                uint64_t all = 0;
+#pragma unroll
+                for (int k = 0; k < kWaves; ++k) all |= s_ball[j][k];
+                any = all != 0ull;
+            } else {
+                any = mask != 0ull;
+            }
+            if (!any) continue;
             const uint32_t g = tbase + uint32_t(j) * kBlock;
-            const bool live = g < a.groups;
-            const uint32_t row = live ? fdiv(g, a.gpr_div) : 0u;
+            const uint32_t gl = min(g, glast);
+            const uint32_t row = fdiv(gl, a.gpr_div);
             float v[8];
-            rotate_raw<WT, HB>(a, s_smask, load_raw<WT>(a, g, live), g, live, row, lf, v);
+            const uint32_t vsign = rotate_group<WT, HB>(s_smask, s_wide, load_raw<WT>(a.w, gl), gl - row * a.gpr,
+                                                        lf, lpos, tid, v);
             const float craw = a.coef[row];
-            const float cl = __uint_as_float(__float_as_uint(craw) ^ lf.sign);
+            const float cl = __uint_as_float(__float_as_uint(craw) ^ vsign);
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = v[i] * cl;
             if ((mask >> lane) & 1ull) {
                 int t[8];
-                exact_point(x, craw, t);
+                exact_point(x, __builtin_isnan(craw), t);
                 // records go in group order: count escapes at lower logical positions
                 const uint64_t lmask = logical_lane_mask(mask);
-                const uint32_t lpos = lane_off;   // 0..63 inside the wave's 64 groups
-                const uint32_t rank_in_wave = uint32_t(__popcll(lmask & ((1ull << lpos) - 1ull)));
+                const uint32_t rank_in_wave = uint32_t(__popcll(lmask & ((1ull << lane_off) - 1ull)));
                 const unsigned long long pos = excl + s_cnt[j * kWaves + wv] + rank_in_wave;
                 if (pos < a.esc_cap) {
                     uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
@@ -556,6 +405,11 @@ void launch_encode(int hb, const EncodeArgs& a, unsigned grid, size_t lds, hipSt
         case 32: hipLaunchKernelGGL((encode_kernel<WT, 32, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
         case 64: hipLaunchKernelGGL((encode_kernel<WT, 64, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
         case 128: hipLaunchKernelGGL((encode_kernel<WT, 128, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 256: hipLaunchKernelGGL((encode_kernel<WT, 256, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 512: hipLaunchKernelGGL((encode_kernel<WT, 512, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 1024: hipLaunchKernelGGL((encode_kernel<WT, 1024, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 2048: hipLaunchKernelGGL((encode_kernel<WT, 2048, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 4096: hipLaunchKernelGGL((encode_kernel<WT, 4096, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
         default: break;
     }
 }
@@ -601,7 +455,6 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
         st = check_block(signs, had_block, cols);
         if (st != E8Q_OK) return st;
         hb = had_block;
-        if (hb > 128) return E8Q_ERR_UNSUPPORTED;   // wider blocks: not in this build
     }
     const DevTable* tab = get_table(core_bound, st);
     if (!tab) return st;
@@ -641,7 +494,7 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
     a.coef = coef;
     a.status = status_dev;
 
-    const size_t smask_bytes = hb > 0 ? size_t(cols / 2) * 4 : 0;
+    const size_t smask_bytes = (hb > 0 ? size_t(cols / 2) * 4 : 0) + (hb > 128 ? size_t(8 * kBlock) * 4 : 0);
     const size_t tab_bytes = size_t(rp.entries) * sizeof(uint16_t);
     if (smask_bytes > kLdsLimit) return E8Q_ERR_UNSUPPORTED;   // rows too wide for the LDS sign masks
 

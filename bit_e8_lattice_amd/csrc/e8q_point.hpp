@@ -1,0 +1,268 @@
+// Per-group pipeline shared by the projection and encode kernels: load,
+// randomized Walsh-Hadamard rotation (any block 8..4096), and the nearest E8
+// point on a fast packed path or the exact path.
+//
+// Both kernels run 512-thread blocks over tiles of 4096 consecutive groups:
+// item j of a tile is the 512 groups tile*4096 + j*512 + [0, 512); inside an
+// item, thread (wave w, lane l) owns group w*64 + (l & ~15) + logical(l).
+// Blocks up to 128 columns are rotated in registers (in-lane + DPP stages);
+// wider blocks finish their stages after an LDS transpose, which needs every
+// thread of the block to call the rotation together.
+#pragma once
+
+#include "e8q_core_table.hpp"
+#include "e8q_device.hpp"
+
+namespace e8q {
+
+constexpr int kBlock = 512;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kItems = 8;                          // groups per thread per tile
+constexpr uint32_t kTileGroups = kItems * kBlock;  // 4096
+constexpr float kMagic = 12582944.0f;              // 1.5 * 2^23 + 32
+constexpr float kFastXMax = 30.0f;
+
+// Raw input of one group: 16 bytes of bf16 (or 32 bytes of float32).
+struct Raw {
+    uint4 p;
+    uint4 q;   // second half, float32 input only
+};
+
+template <typename WT>
+__device__ __forceinline__ Raw load_raw(const void* w, uint32_t g) {
+    Raw r;
+    if constexpr (sizeof(WT) == 2) {
+        r.p = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(w) + uint64_t(g) * 8);
+        r.q = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(w) + uint64_t(g) * 8);
+        r.p = src[0];
+        r.q = src[1];
+    }
+    return r;
+}
+
+// Remaining butterfly stages of blocks wider than 128 columns: stride
+// 128 * 2^k for k = 0 .. log2(HB/128) - 1, in that order.  v holds the true
+// values (lane sign already removed) of this thread's group; lpos is the
+// group's position inside the item.  s_wide: 8 * kBlock floats of LDS.
+template <int HB>
+__device__ __forceinline__ void wide_stages(float (&v)[8], float* s_wide, uint32_t lpos, uint32_t tid) {
+    constexpr int M = HB / 128;          // 128-column sub-blocks per block
+    constexpr int TPB = HB / 8;          // threads per block
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_wide[lpos * 8 + i] = v[i];
+    __syncthreads();
+    const uint32_t bi = tid / TPB, r = tid % TPB;
+    float* blk = s_wide + bi * HB;
+    float u[8];
+    if constexpr (M <= 8) {
+        // 8/M positions per thread, all M sub-blocks of each
+        constexpr int P = 8 / M;
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+            for (int s = 0; s < M; ++s) u[pp * M + s] = blk[s * 128 + r * P + pp];
+#pragma unroll
+        for (int h = 1; h < M; h <<= 1)
+#pragma unroll
+            for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+                for (int s = 0; s < M; ++s)
+                    if ((s & h) == 0) {
+                        const float p = u[pp * M + s], q = u[pp * M + s + h];
+                        u[pp * M + s] = p + q;
+                        u[pp * M + s + h] = p - q;
+                    }
+        __syncthreads();
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+            for (int s = 0; s < M; ++s) blk[s * 128 + r * P + pp] = u[pp * M + s];
+    } else {
+        // one position, sub-blocks qt*8 .. qt*8+7 in-thread, qt across M/8 adjacent lanes
+        constexpr int T = M / 8;
+        const uint32_t pos = r / T, qt = r % T;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = blk[(qt * 8 + i) * 128 + pos];
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((i & h) == 0) {
+                    const float p = u[i], q = u[i + h];
+                    u[i] = p + q;
+                    u[i + h] = p - q;
+                }
+#pragma unroll
+        for (int m = 1; m < T; m <<= 1) {
+            const bool low = (qt & m) == 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float o = __shfl_xor(u[i], m, 64);
+                u[i] = low ? (u[i] + o) : (o - u[i]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) blk[(qt * 8 + i) * 128 + pos] = u[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = s_wide[lpos * 8 + i];
+    __syncthreads();   // the buffer is reused by the next item
+}
+
+// Sign flip, widen and Walsh-Hadamard rotation of one group.  Returns in v
+// the rotated values times (-1)^vsign-bit: multiply by the coefficient with
+// that sign bit applied.  All threads of the block must call this together
+// (wide blocks) and all lanes of each wave must be active (DPP stages).
+template <typename WT, int HB>
+__device__ __forceinline__ uint32_t rotate_group(const uint32_t* s_smask, float* s_wide, Raw r, uint32_t col_group,
+                                                 const LaneFwht& lf, uint32_t lpos, uint32_t tid, float (&v)[8]) {
+    if constexpr (HB > 0) {
+        const uint4 m = *reinterpret_cast<const uint4*>(s_smask + col_group * 4u);
+        if constexpr (sizeof(WT) == 2) {
+            r.p.x ^= m.x; r.p.y ^= m.y; r.p.z ^= m.z; r.p.w ^= m.w;
+        } else {
+            r.p.x ^= m.x << 16; r.p.y ^= m.x & 0x80000000u;
+            r.p.z ^= m.y << 16; r.p.w ^= m.y & 0x80000000u;
+            r.q.x ^= m.z << 16; r.q.y ^= m.z & 0x80000000u;
+            r.q.z ^= m.w << 16; r.q.w ^= m.w & 0x80000000u;
+        }
+    }
+    if constexpr (sizeof(WT) == 2) {
+        v[0] = __uint_as_float(r.p.x << 16); v[1] = __uint_as_float(r.p.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(r.p.y << 16); v[3] = __uint_as_float(r.p.y & 0xFFFF0000u);
+        v[4] = __uint_as_float(r.p.z << 16); v[5] = __uint_as_float(r.p.z & 0xFFFF0000u);
+        v[6] = __uint_as_float(r.p.w << 16); v[7] = __uint_as_float(r.p.w & 0xFFFF0000u);
+    } else {
+        v[0] = __uint_as_float(r.p.x); v[1] = __uint_as_float(r.p.y);
+        v[2] = __uint_as_float(r.p.z); v[3] = __uint_as_float(r.p.w);
+        v[4] = __uint_as_float(r.q.x); v[5] = __uint_as_float(r.q.y);
+        v[6] = __uint_as_float(r.q.z); v[7] = __uint_as_float(r.q.w);
+    }
+    constexpr int RB = HB > 128 ? 128 : HB;
+    fwht_inlane<RB>(v);
+    fwht_xlane<RB>(v, lf.eps);
+    if constexpr (HB > 128) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ lf.sign);
+        wide_stages<HB>(v, s_wide, lpos, tid);
+        return 0u;
+    } else {
+        return HB >= 16 ? lf.sign : 0u;
+    }
+}
+
+// Exact lattice point from normalized coordinates (invalid data -> 0).
+__device__ __forceinline__ uint32_t exact_point(const float (&x)[8], bool bad_row, int (&t)[8]) {
+    const uint32_t inv = bad_row ? uint32_t(E8Q_STATUS_BAD_SCALE) : group_invalid_bits(x);
+    if (inv) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = 0;
+    } else {
+        nearest_e8(x, t);
+    }
+    return inv;
+}
+
+__device__ __forceinline__ uint32_t norm_u32(const int (&t)[8]) {
+    uint32_t n = 0;   // <= 8 * 16386^2 < 2^32
+#pragma unroll
+    for (int i = 0; i < 8; ++i) n += uint32_t(t[i] * t[i]);
+    return n;
+}
+
+// Rank of a core point (|t_i| <= tm of its class) in the unified table layout.
+__device__ __forceinline__ uint32_t core_rank(const int (&t)[8], const uint16_t* tab, const RankParams& p) {
+    const uint32_t c = uint32_t(t[0]) & 1u;
+    const int tm = c ? p.tm[1] : p.tm[0];
+    uint32_t ha = 0, hb = 0;
+    int na = 0, sa = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ha = ha * p.ub + uint32_t((t[i] + tm) >> 1);
+        hb = hb * p.ub + uint32_t((t[4 + i] + tm) >> 1);
+        na += t[i] * t[i];
+        sa += t[i];
+    }
+    const uint32_t state = uint32_t(na >> 1) + (uint32_t(sa >> 1) & 1u);
+    return uint32_t(tab[c * p.nh + ha]) + uint32_t(tab[2u * p.nh + (c * p.nstate + state) * p.nh + hb]);
+}
+
+// Fast path for one group (see the encode kernel's header for the method).
+// Returns false when the group must take the exact path.  On success t0/t1
+// hold 2z + 64 as bytes (coordinates 0-3 in t0, 4-7 in t1) and d8 tells the
+// coset (D8 when true).
+__device__ __forceinline__ bool fast_point(const float (&x)[8], uint32_t& t0, uint32_t& t1, bool& d8) {
+    float d[8];
+    uint32_t yb[8], db[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float y = x[i] + kMagic;     // low byte of the bits: rint(x) + 32
+        d[i] = x[i] - (y - kMagic);
+        yb[i] = __float_as_uint(y);
+        db[i] = __float_as_uint(d[i]);
+    }
+    // n_i + 32 bytes and (d_i < 0 ? 0xFF : 0) bytes, four per word
+    const uint32_t n0 = __builtin_amdgcn_perm(yb[1], yb[0], 0x0C0C0400u) | __builtin_amdgcn_perm(yb[3], yb[2], 0x04000C0Cu);
+    const uint32_t n1 = __builtin_amdgcn_perm(yb[5], yb[4], 0x0C0C0400u) | __builtin_amdgcn_perm(yb[7], yb[6], 0x04000C0Cu);
+    const uint32_t m0 = __builtin_amdgcn_perm(db[1], db[0], 0x0C0C0B09u) | __builtin_amdgcn_perm(db[3], db[2], 0x0B090C0Cu);
+    const uint32_t m1 = __builtin_amdgcn_perm(db[5], db[4], 0x0C0C0B09u) | __builtin_amdgcn_perm(db[7], db[6], 0x0B090C0Cu);
+    // parity of sum(n) and of sum(floor) = sum(n) - #(d < 0)
+    const uint32_t nsum =
+        __builtin_amdgcn_udot4(n0, 0x01010101u, __builtin_amdgcn_udot4(n1, 0x01010101u, 0u, false), false);
+    const uint32_t negs8 = uint32_t(__builtin_popcount(m0)) + uint32_t(__builtin_popcount(m1));
+    const bool odd0 = (nsum & 1u) != 0u;
+    const bool odd1 = ((nsum + (negs8 >> 3)) & 1u) != 0u;
+    const float sa = ((fabsf(d[0]) + fabsf(d[1])) + (fabsf(d[2]) + fabsf(d[3]))) +
+                     ((fabsf(d[4]) + fabsf(d[5])) + (fabsf(d[6]) + fabsf(d[7])));
+    const float amax = fmaxf(fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3]))),
+                             fmaxf(fmaxf(fabsf(d[4]), fabsf(d[5])), fmaxf(fabsf(d[6]), fabsf(d[7]))));
+    const float amin = fminf(fminf(fminf(fabsf(d[0]), fabsf(d[1])), fminf(fabsf(d[2]), fabsf(d[3]))),
+                             fminf(fminf(fabsf(d[4]), fabsf(d[5])), fminf(fabsf(d[6]), fabsf(d[7]))));
+    const float xmax = fmaxf(fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fabsf(x[2])),
+                                   fmaxf(fmaxf(fabsf(x[3]), fabsf(x[4])), fabsf(x[5]))),
+                             fmaxf(fabsf(x[6]), fabsf(x[7])));
+    // coset decision in float32 (trusted when clear of its rounding error)
+    const float tq0 = sa - 2.0f;
+    const float tq1 = odd0 ? tq0 + fmaf(-2.0f, amax, 1.0f) : tq0;
+    const float tq = odd1 ? fmaf(-2.0f, amin, tq1) : tq1;
+    const bool fast = (xmax < kFastXMax) && (amin > 0.0f) && (fabsf(tq) > kFastDecision);
+    if (!fast) return false;
+    d8 = tq < 0.0f;
+    // 2z + 64: D8 -> 2(n + 32); D8+1/2 -> 2(n + 32) + 1 - 2[d < 0]
+    const uint32_t hb = d8 ? 0u : 0x01010101u;
+    const uint32_t hn = d8 ? 0u : 0x02020202u;
+    t0 = ((n0 << 1) | hb) - (m0 & hn);
+    t1 = ((n1 << 1) | hb) - (m1 & hn);
+    // parity fix: first coordinate with |d| equal to the max (D8) or min (D8+1/2)
+    const float tgt = d8 ? amax : amin;
+    const bool fixon = (d8 && odd0) || (!d8 && odd1);
+    bool acc = false, f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bool e = fabsf(d[i]) == tgt;
+        f[i] = e && !acc && fixon;
+        acc = acc || e;
+    }
+    uint32_t sel0 = f[3] ? 0xFF000000u : 0u;
+    sel0 = f[2] ? 0x00FF0000u : sel0;
+    sel0 = f[1] ? 0x0000FF00u : sel0;
+    sel0 = f[0] ? 0x000000FFu : sel0;
+    uint32_t sel1 = f[7] ? 0xFF000000u : 0u;
+    sel1 = f[6] ? 0x00FF0000u : sel1;
+    sel1 = f[5] ? 0x0000FF00u : sel1;
+    sel1 = f[4] ? 0x000000FFu : sel1;
+    // D8 moves the coordinate by +2 sgn(d), D8+1/2 by -2 sgn(d)
+    const uint32_t dm = d8 ? 0u : 0xFFFFFFFFu;
+    const uint32_t mx0 = m0 ^ dm, mx1 = m1 ^ dm;
+    t0 = t0 + __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x20) -
+         __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x80);
+    t1 = t1 + __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x20) -
+         __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x80);
+    return true;
+}
+
+}  // namespace e8q

@@ -3,23 +3,28 @@
 // E8-QAT maps every group of eight normalized weights to its nearest E8 point
 // by arithmetic in every training forward pass (abstract; Figure 1(c) and
 // Figure 2(b) captions), after a Hadamard transform and with reconstruction
-// scales that the overview figure leaves out (Figure 2 caption).  This kernel
-// is a streaming map: one 16-byte load and one 16-byte store per lane per
-// group (bf16), Walsh-Hadamard butterflies in registers and across the lanes
-// of one 16-lane DPP row, and the round-and-fix-parity decoder per lane.
+// scales that the overview figure leaves out (Figure 2 caption).
+//
+// A streaming map over tiles of 4096 groups (512-thread blocks, 8 groups per
+// thread, loads two groups ahead).  Rotation and the nearest point are the
+// shared per-group pipeline (e8q_point.hpp); the fast path writes q = s z
+// straight from the packed 2z + 64 bytes: q_i = fma(byte_i, s/2, -32 s), which
+// is the single rounding of the exact product s z_i.
 #include "e8q_device.hpp"
 #include "e8q_host.hpp"
+#include "e8q_point.hpp"
 
 namespace e8q {
 
 struct ProjectArgs {
     const void* w;
-    uint32_t groups;          // batch*rows*cols/8
+    uint32_t groups;
     uint32_t gpr;             // groups per row
     FastDiv gpr_div;
     FastDiv gpb_div;          // groups per batch item
     const float* scale;
     const int8_t* signs;
+    uint32_t cols;
     float kappa;
     void* q;
     int q_bf16;
@@ -28,109 +33,170 @@ struct ProjectArgs {
     int core_bound;
     unsigned long long* esc;
     uint32_t* status;
+    uint32_t num_tiles;
 };
 
-template <typename WT, int HB>
-__global__ __launch_bounds__(256) void project_kernel(ProjectArgs a) {
-    const uint32_t lane = __lane_id();
-    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-    const uint32_t nwaves = gridDim.x * blockDim.x / kWave;
-    const LaneFwht lf = lane_fwht<HB>(lane);
-    const uint32_t lane_off = (lane & ~15u) + lf.logical;
-    for (uint64_t base = uint64_t(wave) * kWave; base < a.groups; base += uint64_t(nwaves) * kWave) {
-        const uint32_t g = uint32_t(base) + lane_off;
-        const bool live = g < a.groups;
-        float v[8];
-        if (live) {
-            load_group(reinterpret_cast<const WT*>(a.w), g, v);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    // v_cvt_pk_bf16_f32: round to nearest even (q is never NaN)
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    const float2_t f = {lo, hi};
+    const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// 2z + 64 bytes -> signed 2z bytes (values are within [-64, 63])
+__device__ __forceinline__ uint32_t unbias_i8x4(uint32_t t) {
+    const uint32_t x = t ^ 0x40404040u;
+    return x | ((x & 0x40404040u) << 1);
+}
+
+template <typename WT, int HB, bool FAST>
+__global__ __launch_bounds__(kBlock) void project_kernel(ProjectArgs a) {
+    extern __shared__ uint32_t s_dyn[];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wv = tid >> 6;
+    const uint32_t smask_words = HB > 0 ? a.cols / 2u : 0u;
+    uint32_t* s_smask = s_dyn;
+    float* s_wide = reinterpret_cast<float*>(s_dyn + smask_words);
+    if constexpr (HB > 0) {
+        for (uint32_t i = tid; i < smask_words; i += kBlock) {
+            const uint32_t s0 = uint32_t(uint8_t(a.signs[2 * i])) >> 7;
+            const uint32_t s1 = uint32_t(uint8_t(a.signs[2 * i + 1])) >> 7;
+            s_smask[i] = (s0 << 15) | (s1 << 31);
         }
-        const uint32_t row = live ? fdiv(g, a.gpr_div) : 0u;
-        const uint32_t col0 = (g - row * a.gpr) * 8u;
-        float kap = a.kappa;
-        if constexpr (HB > 0) {
-            if (live) apply_signs(a.signs, col0, v);
-            fwht_inlane<HB>(v);
-            fwht_xlane<HB>(v, lf.eps);
-            // the lane holds the transform times (-1)^popcount(L): fold it in
-            kap = __uint_as_float(__float_as_uint(kap) ^ lf.sign);
-            if (a.rotated && live) {
+        __syncthreads();
+    }
+    const LaneFwht lf = lane_fwht<(HB > 128 ? 128 : HB)>(lane);
+    const uint32_t lane_off = (lane & ~15u) + lf.logical;
+    const uint32_t lpos = wv * kWave + lane_off;
+    const uint32_t glast = a.groups - 1u;
+
+    for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
+        const uint32_t tbase = tile * kTileGroups + lpos;
+        uint32_t g1 = tbase, g2 = tbase + kBlock;
+        uint32_t r1 = fdiv(min(g1, glast), a.gpr_div), r2 = fdiv(min(g2, glast), a.gpr_div);
+        Raw w1 = load_raw<WT>(a.w, min(g1, glast)), w2 = load_raw<WT>(a.w, min(g2, glast));
+        float s1 = a.scale[r1], s2 = a.scale[r2];
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const uint32_t g = g1;
+            const bool live = g < a.groups;
+            const uint32_t gl = min(g, glast);
+            const uint32_t row = r1;
+            const Raw raw = w1;
+            const float s = s1;
+            g1 = g2; r1 = r2; w1 = w2; s1 = s2;
+            if (j + 2 < kItems) {
+                g2 = g + 2u * kBlock;
+                const uint32_t gn = min(g2, glast);
+                r2 = fdiv(gn, a.gpr_div);
+                w2 = load_raw<WT>(a.w, gn);
+                s2 = a.scale[r2];
+            }
+            float v[8];
+            const uint32_t vsign = rotate_group<WT, HB>(s_smask, s_wide, raw, gl - row * a.gpr, lf, lpos, tid, v);
+            if (HB > 0 && a.rotated && live) {
+                // fma(v, kappa, +0) rounds like v * kappa and turns an exact -0 into +0
+                const float kap = __uint_as_float(__float_as_uint(a.kappa) ^ vsign);
                 float4* dst = reinterpret_cast<float4*>(a.rotated + uint64_t(g) * 8);
-                // fma(v, kap, +0) rounds like v * kap and turns an exact -0 into +0
                 dst[0] = make_float4(fmaf(v[0], kap, 0.0f), fmaf(v[1], kap, 0.0f), fmaf(v[2], kap, 0.0f),
                                      fmaf(v[3], kap, 0.0f));
                 dst[1] = make_float4(fmaf(v[4], kap, 0.0f), fmaf(v[5], kap, 0.0f), fmaf(v[6], kap, 0.0f),
                                      fmaf(v[7], kap, 0.0f));
             }
-        }
-        const float s = a.scale[row];
-        bool bad;
-        const float c0 = row_coef(s, a.kappa, bad);
-        const float c = __uint_as_float(__float_as_uint(c0) ^ (HB > 0 ? lf.sign : 0u));
-        float x[8];
+            bool bad;
+            const float c0 = row_coef(s, a.kappa, bad);
+            const float c = __uint_as_float(__float_as_uint(c0) ^ vsign);
+            float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = v[i] * c;
-        uint32_t flags = 0;
-        int t[8];
-        if (bad) {
-            flags = live ? uint32_t(E8Q_STATUS_BAD_SCALE) : 0u;
+            for (int i = 0; i < 8; ++i) x[i] = v[i] * c;
+            uint32_t flags = 0;
+            bool done = false;
+            uint32_t norm = 0;
+            if constexpr (FAST) {
+                uint32_t t0, t1;
+                bool d8;
+                // s/2 and 32 s must be exact for the fma form of s * z
+                const bool s_ok = !bad && s > 0x1p-100f && s < 0x1p100f;
+                if (s_ok && fast_point(x, t0, t1, d8)) {
+                    if (live && a.q) {
+                        const float sh = 0.5f * s, sm = -32.0f * s;
+                        float q[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) t[i] = 0;
-        } else {
-            const uint32_t inv = group_invalid_bits(x);
-            if (inv) {
-                flags = live ? inv : 0u;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = 0;
-            } else {
-                nearest_e8(x, t);
-            }
-        }
-        if (live && a.q) {
-            float q[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = bad ? 0.0f : s * (float(t[i]) * 0.5f);
-            if (a.q_bf16) {
-                uint4 p;
-                p.x = pack_bf16x2(q[0], q[1]);
-                p.y = pack_bf16x2(q[2], q[3]);
-                p.z = pack_bf16x2(q[4], q[5]);
-                p.w = pack_bf16x2(q[6], q[7]);
-                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q) + uint64_t(g) * 8) = p;
-            } else {
-                float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.q) + uint64_t(g) * 8);
-                dst[0] = make_float4(q[0], q[1], q[2], q[3]);
-                dst[1] = make_float4(q[4], q[5], q[6], q[7]);
-            }
-        }
-        if (a.two_z) {
-            uint32_t f8 = 0;
-            const uint2 p = pack_i8x8(t, f8);
-            if (live) {
-                *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = p;
-                flags |= f8;
-            }
-        }
-        if (a.esc) {
-            uint32_t norm = 0;   // <= 8 * 16386^2 < 2^32
-#pragma unroll
-            for (int i = 0; i < 8; ++i) norm += uint32_t(t[i] * t[i]);
-            const bool escaped = live && norm > uint32_t(a.core_bound);
-            const uint64_t mask = __ballot(escaped);
-            if (mask) {
-                const uint32_t b = live ? fdiv(g, a.gpb_div) : 0u;
-                const uint32_t b0 = __shfl(b, 0, 64);
-                const bool uniform = __ballot(live && b != b0) == 0;
-                if (uniform) {
-                    if (lane == 0) atomicAdd(a.esc + b0, (unsigned long long)__popcll(mask));
-                } else if (escaped) {
-                    atomicAdd(a.esc + b, 1ull);
+                        for (int i = 0; i < 4; ++i) {
+                            q[i] = fmaf(float((t0 >> (8 * i)) & 0xFFu), sh, sm);
+                            q[4 + i] = fmaf(float((t1 >> (8 * i)) & 0xFFu), sh, sm);
+                        }
+                        if (a.q_bf16) {
+                            uint4 p;
+                            p.x = bf16x2_rne(q[0], q[1]);
+                            p.y = bf16x2_rne(q[2], q[3]);
+                            p.z = bf16x2_rne(q[4], q[5]);
+                            p.w = bf16x2_rne(q[6], q[7]);
+                            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q) + uint64_t(g) * 8) = p;
+                        } else {
+                            float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.q) + uint64_t(g) * 8);
+                            dst[0] = make_float4(q[0], q[1], q[2], q[3]);
+                            dst[1] = make_float4(q[4], q[5], q[6], q[7]);
+                        }
+                    }
+                    if (a.two_z && live)
+                        *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = make_uint2(unbias_i8x4(t0), unbias_i8x4(t1));
+                    if (a.esc) {
+                        const uint32_t qt = __builtin_amdgcn_udot4(t1, t1, __builtin_amdgcn_udot4(t0, t0, 0u, false), false);
+                        const uint32_t st = __builtin_amdgcn_udot4(
+                            t1, 0x01010101u, __builtin_amdgcn_udot4(t0, 0x01010101u, 0u, false), false);
+                        norm = qt - (st << 7) + 32768u;
+                    }
+                    done = true;
                 }
             }
+            if (!done) {
+                int t[8];
+                const uint32_t inv = exact_point(x, bad, t);
+                if (live) flags |= inv;
+                if (live && a.q) {
+                    float q[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) q[i] = bad ? 0.0f : s * (float(t[i]) * 0.5f);
+                    if (a.q_bf16) {
+                        uint4 p;
+                        p.x = pack_bf16x2(q[0], q[1]);
+                        p.y = pack_bf16x2(q[2], q[3]);
+                        p.z = pack_bf16x2(q[4], q[5]);
+                        p.w = pack_bf16x2(q[6], q[7]);
+                        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.q) + uint64_t(g) * 8) = p;
+                    } else {
+                        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.q) + uint64_t(g) * 8);
+                        dst[0] = make_float4(q[0], q[1], q[2], q[3]);
+                        dst[1] = make_float4(q[4], q[5], q[6], q[7]);
+                    }
+                }
+                if (a.two_z && live) {
+                    uint32_t f8 = 0;
+                    *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = pack_i8x8(t, f8);
+                    flags |= f8;
+                }
+                norm = norm_u32(t);
+            }
+            if (a.esc) {
+                const bool escaped = live && norm > uint32_t(a.core_bound);
+                const uint64_t mask = __ballot(escaped);
+                if (mask) {
+                    const uint32_t b = live ? fdiv(g, a.gpb_div) : 0u;
+                    const uint32_t b0 = __shfl(b, 0, 64);
+                    const bool uniform = __ballot(live && b != b0) == 0;
+                    if (uniform) {
+                        if (lane == 0) atomicAdd(a.esc + b0, (unsigned long long)__popcll(mask));
+                    } else if (escaped) {
+                        atomicAdd(a.esc + b, 1ull);
+                    }
+                }
+            }
+            flush_status(flags, a.status);
         }
-        flush_status(flags, a.status);
     }
 }
 
@@ -138,15 +204,20 @@ __global__ void zero_u64_kernel(unsigned long long* p, uint32_t n) {
     for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0ull;
 }
 
-template <typename WT>
-static void launch_project(int hb, const ProjectArgs& a, unsigned grid, hipStream_t st) {
+template <typename WT, bool FAST>
+static void launch_project(int hb, const ProjectArgs& a, unsigned grid, size_t lds, hipStream_t st) {
     switch (hb) {
-        case 0: hipLaunchKernelGGL((project_kernel<WT, 0>), dim3(grid), dim3(256), 0, st, a); break;
-        case 8: hipLaunchKernelGGL((project_kernel<WT, 8>), dim3(grid), dim3(256), 0, st, a); break;
-        case 16: hipLaunchKernelGGL((project_kernel<WT, 16>), dim3(grid), dim3(256), 0, st, a); break;
-        case 32: hipLaunchKernelGGL((project_kernel<WT, 32>), dim3(grid), dim3(256), 0, st, a); break;
-        case 64: hipLaunchKernelGGL((project_kernel<WT, 64>), dim3(grid), dim3(256), 0, st, a); break;
-        case 128: hipLaunchKernelGGL((project_kernel<WT, 128>), dim3(grid), dim3(256), 0, st, a); break;
+        case 0: hipLaunchKernelGGL((project_kernel<WT, 0, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 8: hipLaunchKernelGGL((project_kernel<WT, 8, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 16: hipLaunchKernelGGL((project_kernel<WT, 16, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 32: hipLaunchKernelGGL((project_kernel<WT, 32, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 64: hipLaunchKernelGGL((project_kernel<WT, 64, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 128: hipLaunchKernelGGL((project_kernel<WT, 128, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 256: hipLaunchKernelGGL((project_kernel<WT, 256, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 512: hipLaunchKernelGGL((project_kernel<WT, 512, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 1024: hipLaunchKernelGGL((project_kernel<WT, 1024, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 2048: hipLaunchKernelGGL((project_kernel<WT, 2048, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 4096: hipLaunchKernelGGL((project_kernel<WT, 4096, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
         default: break;
     }
 }
@@ -161,7 +232,8 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
     if (!q_out && !two_z_out && !esc_count_out && !rotated_out) return E8Q_ERR_INVALID;
     if (q_out && q_dtype != E8Q_F32 && q_dtype != E8Q_BF16) return E8Q_ERR_INVALID;
     if (esc_count_out && core_bound < 0) return E8Q_ERR_INVALID;
-    if (had_block > 128) return E8Q_ERR_UNSUPPORTED;   // wider blocks: not in this build
+    const size_t lds = (had_block > 0 ? size_t(cols / 2) * 4 : 0) + (had_block > 128 ? size_t(8 * kBlock) * 4 : 0);
+    if (lds > 60 * 1024) return E8Q_ERR_UNSUPPORTED;   // rows too wide for the LDS sign masks
 
     const uint32_t gpr = uint32_t(cols / 8);
     const uint64_t groups = uint64_t(batch) * uint64_t(rows) * gpr;
@@ -173,6 +245,7 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
     a.gpb_div = make_fastdiv(uint32_t(uint64_t(rows) * gpr));
     a.scale = row_scale;
     a.signs = signs;
+    a.cols = uint32_t(cols);
     a.kappa = kappa_for(had_block);
     a.q = q_out;
     a.q_bf16 = q_dtype == E8Q_BF16;
@@ -181,17 +254,18 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
     a.core_bound = core_bound;
     a.esc = reinterpret_cast<unsigned long long*>(esc_count_out);
     a.status = status_dev;
+    a.num_tiles = uint32_t((groups + kTileGroups - 1) / kTileGroups);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (esc_count_out) {
         hipLaunchKernelGGL(zero_u64_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, s,
                            a.esc, uint32_t(batch));
     }
-    const unsigned grid = grid_for(groups, 256, 8);
+    const unsigned grid = grid_for(a.num_tiles, 1, lds <= 40 * 1024 ? 3 : 2);
     if (w_dtype == E8Q_BF16)
-        launch_project<uint16_t>(had_block, a, grid, s);
+        launch_project<uint16_t, true>(had_block, a, grid, lds, s);
     else
-        launch_project<float>(had_block, a, grid, s);
+        launch_project<float, false>(had_block, a, grid, lds, s);
     return launch_status();
 }
 

@@ -141,3 +141,29 @@ def test_deterministic_order_repeat():
     assert np.array_equal(a1["records"], a2["records"])
     assert np.array_equal(a1["core_idx"], a2["core_idx"])
     assert a1["counts"].sum() > 0.5 * a1["core_idx"].size
+
+
+@pytest.mark.parametrize("hb", [256, 1024, 4096])
+@pytest.mark.parametrize("alpha", [1.0, 3.0])
+def test_wide_blocks_encode(hb, alpha):
+    """Encode with blocks wider than 128 columns: LDS stages in both passes
+    (records are recomputed block-wide)."""
+    d = device()
+    w = workloads.normal((3, 7, 4096), 5000 + hb, d)
+    s = workloads.rms_scale(w, alpha)
+    sg = workloads.signs(4096, 6000 + hb, d)
+    out = run_encode(w, s, 16, sg, hb)
+    ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), hb, 16)
+    _compare(out, ref)
+
+
+def test_decoder_secondary_reading_encode():
+    """Dense-decoder rows encoded with whole-row power-of-two blocks."""
+    d = device()
+    for rows, cols, hb in ((48, 4096, 4096), (20, 11008, 256)):
+        w = workloads.normal((2, rows, cols), 7 * rows + cols, d)
+        s = workloads.rms_scale(w, 3.0)
+        sg = workloads.signs(cols, 4001 if cols == 4096 else 4002, d)
+        out = run_encode(w, s, 16, sg, hb)
+        ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), hb, 16)
+        _compare(out, ref)

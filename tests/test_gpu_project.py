@@ -157,3 +157,33 @@ def test_deterministic_repeat():
     a2 = run_project(b.w, b.scale, b.signs, 128)
     assert first_mismatch(a1["q"], a2["q"]) is None
     assert first_mismatch(a1["two_z_i8"], a2["two_z_i8"]) is None
+
+
+@pytest.mark.parametrize("hb", [256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("wdtype", [torch.bfloat16, torch.float32])
+def test_wide_blocks_lds_stages(hb, wdtype):
+    """Blocks wider than 128 columns (LDS stages): 2 x 9 x 4096, a ragged last
+    tile, rotated values, q and 2z."""
+    d = device()
+    w = workloads.normal((2, 9, 4096), 3000 + hb, d, dtype=wdtype)
+    s = workloads.rms_scale(w, 1.0)
+    sg = workloads.signs(4096, 4000 + hb, d)
+    out = run_project(w, s, sg, hb, rotated=True, core_bound=16)
+    ref = oracle.project(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), hb, core_bound=16,
+                         w_is_bf16=wdtype == torch.bfloat16)
+    _compare(out, ref, rotated=True)
+    assert out["esc_count"].tolist() == ref["esc_count"].tolist()
+
+
+def test_decoder_shapes_full_row_blocks():
+    """The secondary reading of the dense decoder: the largest power-of-two block
+    dividing each row (4096 for 4096-column rows, 256 for 11008-column rows)."""
+    d = device()
+    for rows, cols, hb in ((64, 4096, 4096), (24, 11008, 256)):
+        w = workloads.normal((2, rows, cols), rows + cols, d)
+        s = workloads.rms_scale(w, 3.0)
+        sg = workloads.signs(cols, 4001 if cols == 4096 else 4002, d)
+        out = run_project(w, s, sg, hb, core_bound=16)
+        ref = oracle.project(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), hb, core_bound=16)
+        _compare(out, ref)
+        assert out["esc_count"].tolist() == ref["esc_count"].tolist()
