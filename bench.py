@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_dense_decoder_traffic.json")
-KERNEL_SOURCES = ["e8q_device.hpp", "e8q_encode.hip", "e8q_core_table.cpp", "e8q_core_table.hpp"]
+KERNEL_SOURCES = ["e8q_device.hpp", "e8q_point.hpp", "e8q_encode.hip", "e8q_core_table.cpp", "e8q_core_table.hpp"]
 
 
 def kernel_hash():
@@ -58,26 +58,29 @@ def _oracle_chunk(job):
     return w.size, time.perf_counter() - t0
 
 
-def cpu_baseline(rows_per_shape=2048, chunk_rows=256):
-    """Oracle Gweights/s on a bounded sample: the first ``rows_per_shape`` rows
-    of layer 0's q (4096 cols), gate (4096 cols) and down (11008 cols)
-    matrices, encoded by the numpy oracle in forked single-threaded workers
-    (one per core, at most 16).  Runs before the GPU is initialised."""
+def cpu_baseline(blocks=1, chunk_rows=512):
+    """Oracle Gweights/s on a bounded sample of the same workload: every
+    matrix of the first ``blocks`` decoder block(s) (q, k, v, o, gate, up,
+    down: 202 M weights per block), same seeds, scales and signs, encoded by
+    the numpy oracle in forked single-threaded workers (one per core, at most
+    16) over chunks of rows.  Runs before the GPU is initialised."""
     import multiprocessing as mp
     import numpy as np
     import torch
     from bit_e8_lattice_amd import workloads
 
-    torch.set_num_threads(1)
+    torch.set_num_threads(min(16, len(os.sched_getaffinity(0))))
     jobs = []
-    for name, seed, rows, cols, sseed in (("q", 4100, 4096, 4096, 4001), ("gate", 4104, 11008, 4096, 4001),
-                                          ("down", 4106, 4096, 11008, 4002)):
-        w = workloads.normal((rows, cols), seed, "cpu")[:rows_per_shape]
-        s = workloads.rms_scale(w, 3.0).numpy()
-        sg = workloads.signs(cols, sseed, "cpu").numpy()
-        wb = w.contiguous().view(torch.int16).numpy().view(np.uint16)
-        for lo in range(0, rows_per_shape, chunk_rows):
-            jobs.append((wb[lo:lo + chunk_rows].copy(), s[lo:lo + chunk_rows].copy(), sg))
+    for blk in range(blocks):
+        for j, (name, rows, cols) in enumerate(workloads.DECODER_MATS):
+            seed = 4100 + blk * len(workloads.DECODER_MATS) + j
+            w = workloads.normal((rows, cols), seed, "cpu")
+            s = workloads.rms_scale(w, 3.0).numpy()
+            sg = workloads.signs(cols, 4001 if cols == 4096 else 4002, "cpu").numpy()
+            wb = w.contiguous().view(torch.int16).numpy().view(np.uint16)
+            for lo in range(0, rows, chunk_rows):
+                jobs.append((wb[lo:lo + chunk_rows].copy(), s[lo:lo + chunk_rows].copy(), sg))
+    torch.set_num_threads(1)
     cores = min(16, len(os.sched_getaffinity(0)), len(jobs))
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
@@ -91,9 +94,8 @@ def cpu_baseline(rows_per_shape=2048, chunk_rows=256):
         "unit": "Gweights/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"{weights} weights: first {rows_per_shape} rows of layer-0 q, gate and down "
-                   f"matrices, {len(jobs)} chunks of {chunk_rows} rows, {cpu_s:.1f} s of CPU time "
-                   f"over {wall:.1f} s wall"),
+        "sample": (f"{weights} weights: all 7 matrices of decoder block 0 (same seeds, scales, signs), "
+                   f"{len(jobs)} chunks of {chunk_rows} rows, {cpu_s:.1f} s of CPU time over {wall:.1f} s wall"),
     }
 
 
@@ -268,7 +270,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder", choices=["decoder", "linear", "moe", "qat"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=6144)
+    ap.add_argument("--cpu-blocks", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (known bytes) for counter scaling")
     args = ap.parse_args()
@@ -278,7 +280,7 @@ def main():
               "(the encode shards by matrix with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
-    cpu = None if (args.no_cpu_baseline or args.config != "decoder") else cpu_baseline(args.cpu_rows)
+    cpu = None if (args.no_cpu_baseline or args.config != "decoder") else cpu_baseline(args.cpu_blocks)
 
     import torch
     import bit_e8_lattice_amd as e8q
