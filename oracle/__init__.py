@@ -59,4 +59,11 @@ from .pipeline import (  # noqa: F401
     payload_bits,
     rms_scale,
 )
+from .restore import (  # noqa: F401
+    restore_coefficients,
+    restore_original,
+    project_restore,
+    rotate_grad,
+    ste_backward_hadamard,
+)
 from .brute import brute_nearest_e8  # noqa: F401
