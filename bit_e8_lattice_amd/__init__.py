@@ -14,8 +14,9 @@ import torch
 
 __all__ = [
     "E8QError", "lib", "library_path",
-    "e8q_project", "e8q_project_hadamard", "e8q_encode_core_escape",
-    "e8q_encode_workspace_size", "e8q_ste_backward", "e8q_core_size",
+    "e8q_project", "e8q_project_hadamard", "e8q_project_hadamard_restore",
+    "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_ste_backward",
+    "e8q_ste_backward_hadamard", "e8q_core_size",
     "e8q_status_string", "e8q_version",
     "ESCAPE_RECORD_BYTES", "STATUS_BITS", "F32", "BF16",
 ]
@@ -53,6 +54,10 @@ def lib():
     L.e8q_project.restype = e
     L.e8q_project_hadamard.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, vp, e, vp, vp, i32, vp, vp, vp]
     L.e8q_project_hadamard.restype = e
+    L.e8q_project_hadamard_restore.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, vp, e, vp, i32, vp, vp, vp]
+    L.e8q_project_hadamard_restore.restype = e
+    L.e8q_ste_backward_hadamard.argtypes = [vp, e, i64, i64, vp, i32, vp, vp, f32, vp]
+    L.e8q_ste_backward_hadamard.restype = e
     L.e8q_encode_core_escape.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
                                          vp, sz, vp, vp]
     L.e8q_encode_core_escape.restype = e
@@ -142,6 +147,24 @@ def e8q_project_hadamard(w, row_scale, signs, had_block, status, q_out=None, two
     _check("e8q_project_hadamard", code)
 
 
+def e8q_project_hadamard_restore(w, row_scale, signs, had_block, w_hat_out, status, two_z_out=None,
+                                 core_bound=-1, esc_count_out=None, stream=None):
+    """``e8q_project_hadamard_restore``: the projection rotated back to the
+    original basis (``w_hat_out`` float32 or bf16, shaped like ``w``)."""
+    _dev(w, "w", _WDT); _dev(row_scale, "row_scale", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,)); _dev(w_hat_out, "w_hat_out", _WDT)
+    _dev(two_z_out, "two_z_out", (torch.int8,))
+    _dev(esc_count_out, "esc_count_out", (torch.int64,)); _dev(status, "status", (torch.int32,))
+    if w_hat_out is None:
+        raise ValueError("w_hat_out is required")
+    b, r, c = _shape3(w)
+    code = lib().e8q_project_hadamard_restore(_ptr(w), _dtype_code(w), b, r, c, _ptr(row_scale),
+                                              _ptr(signs), int(had_block), _ptr(w_hat_out),
+                                              _dtype_code(w_hat_out), _ptr(two_z_out), int(core_bound),
+                                              _ptr(esc_count_out), _ptr(status), _stream(w, stream))
+    _check("e8q_project_hadamard_restore", code)
+
+
 def e8q_encode_workspace_size(batch, rows, cols):
     return int(lib().e8q_encode_workspace_size(batch, rows, cols))
 
@@ -172,6 +195,19 @@ def e8q_ste_backward(grad_q, grad_w=None, w_latent=None, lr=1.0, stream=None):
     code = lib().e8q_ste_backward(_ptr(grad_q), _ptr(grad_w), _ptr(w_latent), float(lr),
                                   _dtype_code(grad_q), grad_q.numel(), _stream(grad_q, stream))
     _check("e8q_ste_backward", code)
+
+
+def e8q_ste_backward_hadamard(grad_q, signs, had_block, grad_w=None, w_latent=None, lr=1.0, stream=None):
+    """``e8q_ste_backward_hadamard``: gradient of the latents for a rotated-basis
+    projection (R^T applied to ``grad_q``), and/or the fused SGD step."""
+    _dev(grad_q, "grad_q", _WDT); _dev(signs, "signs", (torch.int8,))
+    _dev(grad_w, "grad_w", (grad_q.dtype,)); _dev(w_latent, "w_latent", (grad_q.dtype,))
+    cols = grad_q.shape[-1]
+    rows = grad_q.numel() // cols
+    code = lib().e8q_ste_backward_hadamard(_ptr(grad_q), _dtype_code(grad_q), rows, cols, _ptr(signs),
+                                           int(had_block), _ptr(grad_w), _ptr(w_latent), float(lr),
+                                           _stream(grad_q, stream))
+    _check("e8q_ste_backward_hadamard", code)
 
 
 def e8q_core_size(core_bound):

@@ -113,6 +113,67 @@ __device__ __forceinline__ void wide_stages(float (&v)[8], float* s_wide, uint32
     __syncthreads();   // the buffer is reused by the next item
 }
 
+// Butterfly stages of stride >= 8 (across lanes, then through LDS for blocks
+// wider than 128 columns) on values whose in-lane stages are done.  Returns
+// the sign bit that the lane's results carry (see fwht_xlane).  Same calling
+// rules as rotate_group.
+template <int HB>
+__device__ __forceinline__ uint32_t fwht_cross(float (&v)[8], const LaneFwht& lf, float* s_wide, uint32_t lpos,
+                                               uint32_t tid) {
+    constexpr int RB = HB > 128 ? 128 : HB;
+    fwht_xlane<RB>(v, lf.eps);
+    if constexpr (HB > 128) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ lf.sign);
+        wide_stages<HB>(v, s_wide, lpos, tid);
+        return 0u;
+    } else {
+        return HB >= 16 ? lf.sign : 0u;
+    }
+}
+
+// Whole Walsh-Hadamard transform of the block holding this thread's group.
+template <int HB>
+__device__ __forceinline__ uint32_t fwht_group(float (&v)[8], const LaneFwht& lf, float* s_wide, uint32_t lpos,
+                                               uint32_t tid) {
+    fwht_inlane<(HB > 128 ? 128 : HB)>(v);
+    return fwht_cross<HB>(v, lf, s_wide, lpos, tid);
+}
+
+// Widen one group's raw input to float32 (no sign flip).
+template <typename WT>
+__device__ __forceinline__ void widen_raw(const Raw& r, float (&v)[8]) {
+    if constexpr (sizeof(WT) == 2) {
+        v[0] = __uint_as_float(r.p.x << 16); v[1] = __uint_as_float(r.p.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(r.p.y << 16); v[3] = __uint_as_float(r.p.y & 0xFFFF0000u);
+        v[4] = __uint_as_float(r.p.z << 16); v[5] = __uint_as_float(r.p.z & 0xFFFF0000u);
+        v[6] = __uint_as_float(r.p.w << 16); v[7] = __uint_as_float(r.p.w & 0xFFFF0000u);
+    } else {
+        v[0] = __uint_as_float(r.p.x); v[1] = __uint_as_float(r.p.y);
+        v[2] = __uint_as_float(r.p.z); v[3] = __uint_as_float(r.p.w);
+        v[4] = __uint_as_float(r.q.x); v[5] = __uint_as_float(r.q.y);
+        v[6] = __uint_as_float(r.q.z); v[7] = __uint_as_float(r.q.w);
+    }
+}
+
+// Flip the float32 sign bits of one group by its column signs (mask words as
+// stored in LDS: bit 15 / bit 31 of word k for columns 2k / 2k+1).
+__device__ __forceinline__ void flip_f32(float (&y)[8], const uint4& m) {
+    y[0] = __uint_as_float(__float_as_uint(y[0]) ^ (m.x << 16)); y[1] = __uint_as_float(__float_as_uint(y[1]) ^ (m.x & 0x80000000u));
+    y[2] = __uint_as_float(__float_as_uint(y[2]) ^ (m.y << 16)); y[3] = __uint_as_float(__float_as_uint(y[3]) ^ (m.y & 0x80000000u));
+    y[4] = __uint_as_float(__float_as_uint(y[4]) ^ (m.z << 16)); y[5] = __uint_as_float(__float_as_uint(y[5]) ^ (m.z & 0x80000000u));
+    y[6] = __uint_as_float(__float_as_uint(y[6]) ^ (m.w << 16)); y[7] = __uint_as_float(__float_as_uint(y[7]) ^ (m.w & 0x80000000u));
+}
+
+// Column-sign mask words of LDS for `cols` columns (signs: +-1 int8).
+__device__ __forceinline__ void load_sign_masks(uint32_t* s_smask, const int8_t* signs, uint32_t cols, uint32_t tid) {
+    for (uint32_t i = tid; i < cols / 2u; i += kBlock) {
+        const uint32_t s0 = uint32_t(uint8_t(signs[2 * i])) >> 7;
+        const uint32_t s1 = uint32_t(uint8_t(signs[2 * i + 1])) >> 7;
+        s_smask[i] = (s0 << 15) | (s1 << 31);
+    }
+}
+
 // Sign flip, widen and Walsh-Hadamard rotation of one group.  Returns in v
 // the rotated values times (-1)^vsign-bit: multiply by the coefficient with
 // that sign bit applied.  All threads of the block must call this together
@@ -131,28 +192,8 @@ __device__ __forceinline__ uint32_t rotate_group(const uint32_t* s_smask, float*
             r.q.z ^= m.w << 16; r.q.w ^= m.w & 0x80000000u;
         }
     }
-    if constexpr (sizeof(WT) == 2) {
-        v[0] = __uint_as_float(r.p.x << 16); v[1] = __uint_as_float(r.p.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(r.p.y << 16); v[3] = __uint_as_float(r.p.y & 0xFFFF0000u);
-        v[4] = __uint_as_float(r.p.z << 16); v[5] = __uint_as_float(r.p.z & 0xFFFF0000u);
-        v[6] = __uint_as_float(r.p.w << 16); v[7] = __uint_as_float(r.p.w & 0xFFFF0000u);
-    } else {
-        v[0] = __uint_as_float(r.p.x); v[1] = __uint_as_float(r.p.y);
-        v[2] = __uint_as_float(r.p.z); v[3] = __uint_as_float(r.p.w);
-        v[4] = __uint_as_float(r.q.x); v[5] = __uint_as_float(r.q.y);
-        v[6] = __uint_as_float(r.q.z); v[7] = __uint_as_float(r.q.w);
-    }
-    constexpr int RB = HB > 128 ? 128 : HB;
-    fwht_inlane<RB>(v);
-    fwht_xlane<RB>(v, lf.eps);
-    if constexpr (HB > 128) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ lf.sign);
-        wide_stages<HB>(v, s_wide, lpos, tid);
-        return 0u;
-    } else {
-        return HB >= 16 ? lf.sign : 0u;
-    }
+    widen_raw<WT>(r, v);
+    return fwht_group<HB>(v, lf, s_wide, lpos, tid);
 }
 
 // Exact lattice point from normalized coordinates (invalid data -> 0).

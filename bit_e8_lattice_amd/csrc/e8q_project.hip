@@ -10,6 +10,15 @@
 // shared per-group pipeline (e8q_point.hpp); the fast path writes q = s z
 // straight from the packed 2z + 64 bytes: q_i = fma(byte_i, s/2, -32 s), which
 // is the single rounding of the exact product s z_i.
+//
+// e8q_project_hadamard_restore writes the projection back in the original
+// basis instead: w_hat = sigma * fl32(T * c2), T = H_b (2z) with float32
+// butterflies in the forward stage order, c2 = fl32(fl32(s kappa_b) / 2).  The
+// inverse transform runs on the same lanes as the forward one (the rotation is
+// orthogonal and H_b symmetric, so it is the same butterfly network followed
+// by the sign flip).  On the fast path 2z + 64 is transformed instead: its
+// three in-lane stages are exact and leave the offset only in element 0 (as
+// 8 * 64), which is removed before the cross-lane stages.
 #include "e8q_device.hpp"
 #include "e8q_host.hpp"
 #include "e8q_point.hpp"
@@ -34,6 +43,8 @@ struct ProjectArgs {
     unsigned long long* esc;
     uint32_t* status;
     uint32_t num_tiles;
+    void* w_hat;              // restored weights (original basis), or null
+    int w_hat_bf16;
 };
 
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
@@ -51,7 +62,7 @@ __device__ __forceinline__ uint32_t unbias_i8x4(uint32_t t) {
     return x | ((x & 0x40404040u) << 1);
 }
 
-template <typename WT, int HB, bool FAST>
+template <typename WT, int HB, bool FAST, bool RESTORE>
 __global__ __launch_bounds__(kBlock) void project_kernel(ProjectArgs a) {
     extern __shared__ uint32_t s_dyn[];
     const uint32_t tid = threadIdx.x;
@@ -61,11 +72,7 @@ __global__ __launch_bounds__(kBlock) void project_kernel(ProjectArgs a) {
     uint32_t* s_smask = s_dyn;
     float* s_wide = reinterpret_cast<float*>(s_dyn + smask_words);
     if constexpr (HB > 0) {
-        for (uint32_t i = tid; i < smask_words; i += kBlock) {
-            const uint32_t s0 = uint32_t(uint8_t(a.signs[2 * i])) >> 7;
-            const uint32_t s1 = uint32_t(uint8_t(a.signs[2 * i + 1])) >> 7;
-            s_smask[i] = (s0 << 15) | (s1 << 31);
-        }
+        load_sign_masks(s_smask, a.signs, a.cols, tid);
         __syncthreads();
     }
     const LaneFwht lf = lane_fwht<(HB > 128 ? 128 : HB)>(lane);
@@ -115,6 +122,8 @@ __global__ __launch_bounds__(kBlock) void project_kernel(ProjectArgs a) {
             uint32_t flags = 0;
             bool done = false;
             uint32_t norm = 0;
+            float r[8];          // 2z for the restore (+64 on the fast path)
+            float rcorr = 0.0f;
             if constexpr (FAST) {
                 uint32_t t0, t1;
                 bool d8;
@@ -144,6 +153,14 @@ __global__ __launch_bounds__(kBlock) void project_kernel(ProjectArgs a) {
                     }
                     if (a.two_z && live)
                         *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = make_uint2(unbias_i8x4(t0), unbias_i8x4(t1));
+                    if constexpr (RESTORE) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            r[i] = float((t0 >> (8 * i)) & 0xFFu);
+                            r[4 + i] = float((t1 >> (8 * i)) & 0xFFu);
+                        }
+                        rcorr = 512.0f;
+                    }
                     if (a.esc) {
                         const uint32_t qt = __builtin_amdgcn_udot4(t1, t1, __builtin_amdgcn_udot4(t0, t0, 0u, false), false);
                         const uint32_t st = __builtin_amdgcn_udot4(
@@ -180,6 +197,37 @@ __global__ __launch_bounds__(kBlock) void project_kernel(ProjectArgs a) {
                     flags |= f8;
                 }
                 norm = norm_u32(t);
+                if constexpr (RESTORE) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) r[i] = float(t[i]);
+                }
+            }
+            if constexpr (RESTORE) {
+                // inverse rotation across the block; every lane takes part
+                fwht_inlane<8>(r);
+                r[0] -= rcorr;
+                const uint32_t rs = fwht_cross<HB>(r, lf, s_wide, lpos, tid);
+                const float c2 = bad ? 0.0f : (s * a.kappa) * 0.5f;
+                const float c2s = __uint_as_float(__float_as_uint(c2) ^ rs);
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = fmaf(r[i], c2s, 0.0f);   // every zero becomes +0
+                if (live) {
+                    const uint4 m = *reinterpret_cast<const uint4*>(s_smask + (gl - row * a.gpr) * 4u);
+                    if (a.w_hat_bf16) {
+                        uint4 p;
+                        p.x = bf16x2_rne(y[0], y[1]) ^ m.x;
+                        p.y = bf16x2_rne(y[2], y[3]) ^ m.y;
+                        p.z = bf16x2_rne(y[4], y[5]) ^ m.z;
+                        p.w = bf16x2_rne(y[6], y[7]) ^ m.w;
+                        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.w_hat) + uint64_t(g) * 8) = p;
+                    } else {
+                        flip_f32(y, m);
+                        float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.w_hat) + uint64_t(g) * 8);
+                        dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+                        dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+                    }
+                }
             }
             if (a.esc) {
                 const bool escaped = live && norm > uint32_t(a.core_bound);
@@ -204,20 +252,23 @@ __global__ void zero_u64_kernel(unsigned long long* p, uint32_t n) {
     for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0ull;
 }
 
-template <typename WT, bool FAST>
+template <typename WT, bool FAST, bool RESTORE>
 static void launch_project(int hb, const ProjectArgs& a, unsigned grid, size_t lds, hipStream_t st) {
     switch (hb) {
-        case 0: hipLaunchKernelGGL((project_kernel<WT, 0, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 8: hipLaunchKernelGGL((project_kernel<WT, 8, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((project_kernel<WT, 16, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((project_kernel<WT, 32, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 64: hipLaunchKernelGGL((project_kernel<WT, 64, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 128: hipLaunchKernelGGL((project_kernel<WT, 128, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 256: hipLaunchKernelGGL((project_kernel<WT, 256, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 512: hipLaunchKernelGGL((project_kernel<WT, 512, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 1024: hipLaunchKernelGGL((project_kernel<WT, 1024, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 2048: hipLaunchKernelGGL((project_kernel<WT, 2048, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 4096: hipLaunchKernelGGL((project_kernel<WT, 4096, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 0:
+            if constexpr (!RESTORE)
+                hipLaunchKernelGGL((project_kernel<WT, 0, FAST, false>), dim3(grid), dim3(kBlock), lds, st, a);
+            break;
+        case 8: hipLaunchKernelGGL((project_kernel<WT, 8, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 16: hipLaunchKernelGGL((project_kernel<WT, 16, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 32: hipLaunchKernelGGL((project_kernel<WT, 32, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 64: hipLaunchKernelGGL((project_kernel<WT, 64, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 128: hipLaunchKernelGGL((project_kernel<WT, 128, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 256: hipLaunchKernelGGL((project_kernel<WT, 256, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 512: hipLaunchKernelGGL((project_kernel<WT, 512, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 1024: hipLaunchKernelGGL((project_kernel<WT, 1024, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 2048: hipLaunchKernelGGL((project_kernel<WT, 2048, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 4096: hipLaunchKernelGGL((project_kernel<WT, 4096, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
         default: break;
     }
 }
@@ -226,10 +277,13 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
                                  int64_t cols, const float* row_scale, const int8_t* signs,
                                  int32_t had_block, void* q_out, e8q_dtype_t q_dtype,
                                  int8_t* two_z_out, float* rotated_out, int32_t core_bound,
-                                 int64_t* esc_count_out, uint32_t* status_dev, void* stream) {
+                                 int64_t* esc_count_out, uint32_t* status_dev, void* stream,
+                                 void* w_hat_out = nullptr, e8q_dtype_t w_hat_dtype = E8Q_F32) {
     e8q_status_t st = check_shape(w, w_dtype, batch, rows, cols, row_scale, status_dev);
     if (st != E8Q_OK) return st;
-    if (!q_out && !two_z_out && !esc_count_out && !rotated_out) return E8Q_ERR_INVALID;
+    if (!q_out && !two_z_out && !esc_count_out && !rotated_out && !w_hat_out) return E8Q_ERR_INVALID;
+    if (w_hat_out && (had_block < 8 || (w_hat_dtype != E8Q_F32 && w_hat_dtype != E8Q_BF16)))
+        return E8Q_ERR_INVALID;
     if (q_out && q_dtype != E8Q_F32 && q_dtype != E8Q_BF16) return E8Q_ERR_INVALID;
     if (esc_count_out && core_bound < 0) return E8Q_ERR_INVALID;
     const size_t lds = (had_block > 0 ? size_t(cols / 2) * 4 : 0) + (had_block > 128 ? size_t(8 * kBlock) * 4 : 0);
@@ -255,6 +309,8 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
     a.esc = reinterpret_cast<unsigned long long*>(esc_count_out);
     a.status = status_dev;
     a.num_tiles = uint32_t((groups + kTileGroups - 1) / kTileGroups);
+    a.w_hat = w_hat_out;
+    a.w_hat_bf16 = w_hat_dtype == E8Q_BF16;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (esc_count_out) {
@@ -262,10 +318,16 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
                            a.esc, uint32_t(batch));
     }
     const unsigned grid = grid_for(a.num_tiles, 1, lds <= 40 * 1024 ? 3 : 2);
-    if (w_dtype == E8Q_BF16)
-        launch_project<uint16_t, true>(had_block, a, grid, lds, s);
-    else
-        launch_project<float, false>(had_block, a, grid, lds, s);
+    if (w_hat_out) {
+        if (w_dtype == E8Q_BF16)
+            launch_project<uint16_t, true, true>(had_block, a, grid, lds, s);
+        else
+            launch_project<float, false, true>(had_block, a, grid, lds, s);
+    } else if (w_dtype == E8Q_BF16) {
+        launch_project<uint16_t, true, false>(had_block, a, grid, lds, s);
+    } else {
+        launch_project<float, false, false>(had_block, a, grid, lds, s);
+    }
     return launch_status();
 }
 
@@ -291,4 +353,18 @@ extern "C" e8q_status_t e8q_project_hadamard(const void* w, e8q_dtype_t w_dtype,
     return e8q::project_impl(w, w_dtype, batch, rows, cols, row_scale, signs, had_block, q_out,
                              q_dtype, two_z_out, rotated_out, core_bound, esc_count_out, status_dev,
                              stream);
+}
+
+extern "C" e8q_status_t e8q_project_hadamard_restore(const void* w, e8q_dtype_t w_dtype, int64_t batch,
+                                                     int64_t rows, int64_t cols, const float* row_scale,
+                                                     const int8_t* signs, int32_t had_block, void* w_hat_out,
+                                                     e8q_dtype_t w_hat_dtype, int8_t* two_z_out,
+                                                     int32_t core_bound, int64_t* esc_count_out,
+                                                     uint32_t* status_dev, void* stream) {
+    e8q_status_t st = e8q::check_block(signs, had_block, cols);
+    if (st != E8Q_OK) return st;
+    if (!w_hat_out) return E8Q_ERR_INVALID;
+    return e8q::project_impl(w, w_dtype, batch, rows, cols, row_scale, signs, had_block, nullptr, E8Q_F32,
+                             two_z_out, nullptr, core_bound, esc_count_out, status_dev, stream, w_hat_out,
+                             w_hat_dtype);
 }

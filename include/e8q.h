@@ -136,6 +136,31 @@ e8q_status_t e8q_project_hadamard(const void* w, e8q_dtype_t w_dtype,
                                   uint32_t* status_dev, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * e8q_project_hadamard_restore -- e8q_project_hadamard with the projection
+ * rotated back to the original weight basis, the form a QAT forward feeds to
+ * its matmul (E8-QAT Figure 2 caption: the Hadamard transforms surround the
+ * projection but are not drawn; undoing the rotation is a reading).
+ *   w_hat = R^T (s z) = sigma * fl32(T * c2), T = H_b (2z) (float32
+ *   butterflies in the forward stage order, exact for every |2z| <= 2^24 / b),
+ *   c2 = fl32(fl32(s * kappa_b) * 0.5); every zero is sigma * (+0).
+ * Arguments as e8q_project_hadamard, except:
+ *   w_hat_out    [batch, rows, cols] restored weights in w_hat_dtype (F32, or
+ *                BF16 rounded to nearest even) (required)
+ *   two_z_out, core_bound, esc_count_out   as e8q_project (optional)
+ * A row with an invalid scale (E8Q_STATUS_BAD_SCALE) restores to sigma * (+0).
+ * Its identity STE is exact: the composite w -> w_hat has Jacobian I through
+ * the rounding, so e8q_ste_backward applies unchanged.
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_project_hadamard_restore(const void* w, e8q_dtype_t w_dtype,
+                                          int64_t batch, int64_t rows, int64_t cols,
+                                          const float* row_scale,
+                                          const int8_t* signs, int32_t had_block,
+                                          void* w_hat_out, e8q_dtype_t w_hat_dtype,
+                                          int8_t* two_z_out,
+                                          int32_t core_bound, int64_t* esc_count_out,
+                                          uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
  * e8q_encode_core_escape -- export encoding (E8-QAT Figure 2(c): core indices
  * plus sparse escape records keep the final lattice points exactly).
  *
@@ -187,6 +212,27 @@ size_t e8q_encode_workspace_size(int64_t batch, int64_t rows, int64_t cols);
  * ------------------------------------------------------------------------- */
 e8q_status_t e8q_ste_backward(const void* grad_q, void* grad_w, void* w_latent,
                               float lr, e8q_dtype_t dtype, int64_t n, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * e8q_ste_backward_hadamard -- the identity STE (E8-QAT Figure 2(b) caption)
+ * for a projection whose output q stays in the rotated basis: the gradient of
+ * the latent weights is R^T dL/dq = sigma * fl32(kappa_b * H_b g) per block
+ * (every zero as sigma * (+0)), optionally fused with the SGD step
+ * w <- fl32(w - fl32(lr * g_w)) on the float32 g_w.
+ *   grad_q    [rows, cols] gradient with respect to q, dtype `dtype` (required)
+ *   signs, had_block   the forward's (had_block a power of two in [8, 4096]
+ *             dividing cols; cols <= 30720, or 22528 when had_block > 128)
+ *   grad_w    [rows, cols] receives g_w in `dtype` (BF16: nearest even, NaN ->
+ *             0x7FC0), or NULL; it may be grad_q itself (in place)
+ *   w_latent  [rows, cols] updated in place (BF16 rounded as grad_w), or NULL;
+ *             it may alias neither grad_q nor grad_w
+ * At least one of grad_w, w_latent must be non-NULL.
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_ste_backward_hadamard(const void* grad_q, e8q_dtype_t dtype,
+                                       int64_t rows, int64_t cols,
+                                       const int8_t* signs, int32_t had_block,
+                                       void* grad_w, void* w_latent, float lr,
+                                       void* stream);
 
 /* |C(core_bound)|, the number of core points; -1 if core_bound is outside [0, 40].
  * Host-only. */

@@ -94,3 +94,32 @@ def first_mismatch(a, b):
         return None
     i = bad[0]
     return f"{len(bad)} mismatches, first at flat {i}: {a.reshape(-1)[i]} vs {b.reshape(-1)[i]}"
+
+
+def run_restore(w, s, signs, hb, out_dtype=torch.bfloat16, two_z=True, core_bound=-1):
+    d = w.device
+    st = torch.zeros(1, dtype=torch.int32, device=d)
+    wh = torch.empty(w.shape, dtype=out_dtype, device=d)
+    tz = torch.empty(w.shape, dtype=torch.int8, device=d) if two_z else None
+    batch = 1 if w.dim() == 2 else w.shape[0]
+    esc = torch.empty(batch, dtype=torch.int64, device=d) if core_bound >= 0 else None
+    e8q.e8q_project_hadamard_restore(w, s, signs, hb, wh, st, two_z_out=tz, core_bound=core_bound,
+                                     esc_count_out=esc)
+    torch.cuda.synchronize()
+    out = {"status": int(st.item()) & 0xFFFFFFFF,
+           "w_hat": u16(wh) if out_dtype == torch.bfloat16 else wh.cpu().numpy()}
+    if tz is not None:
+        out["two_z_i8"] = tz.cpu().numpy()
+    if esc is not None:
+        out["esc_count"] = esc.cpu().numpy()
+    return out
+
+
+def same_bits_or_nan(a, b):
+    """float32 arrays equal bit for bit, except that NaN matches any NaN."""
+    a = np.asarray(a, np.float32).reshape(-1)
+    b = np.asarray(b, np.float32).reshape(-1)
+    na, nb = np.isnan(a), np.isnan(b)
+    if not np.array_equal(na, nb):
+        return f"NaN positions differ ({na.sum()} vs {nb.sum()})"
+    return first_mismatch(a[~na].view(np.uint32), b[~nb].view(np.uint32))

@@ -109,3 +109,35 @@ def test_ste_rejects(L):
     assert L.e8q_ste_backward(FAKE, FAKE, None, 1.0, 1, 0, None) == 1
     assert L.e8q_ste_backward(FAKE, FAKE, None, 1.0, 5, 10, None) == 1
     assert L.e8q_ste_backward(FAKE, FAKE, None, 1.0, 1, 10, None) == 1     # grad_w aliases grad_q
+
+
+def test_restore_rejects(L):
+    # (w, dt, batch, rows, cols, scale, signs, block, w_hat, w_hat_dt, two_z, bound, esc, status, stream)
+    base = [FAKE, 1, 1, 4, 256, FAKE, FAKE, 128, FAKE, 1, None, -1, None, FAKE, None]
+    bad = []
+    b = list(base); b[8] = None; bad.append(b)                    # w_hat required
+    b = list(base); b[9] = 3; bad.append(b)                       # w_hat dtype
+    b = list(base); b[6] = None; bad.append(b)                    # signs required
+    b = list(base); b[7] = 0; bad.append(b)                       # a block is required
+    b = list(base); b[7] = 96; bad.append(b)
+    b = list(base); b[4] = 200; bad.append(b)                     # block does not divide cols
+    b = list(base); b[12] = FAKE; bad.append(b)                   # counts without a bound
+    for args in bad:
+        assert L.e8q_project_hadamard_restore(*args) == 1, args
+
+
+def test_ste_hadamard_rejects(L):
+    # (grad_q, dt, rows, cols, signs, block, grad_w, w_latent, lr, stream)
+    base = [FAKE, 1, 4, 256, FAKE, 128, FAKE, None, 1.0, None]
+    bad = []
+    b = list(base); b[0] = None; bad.append(b)
+    b = list(base); b[6] = None; bad.append(b)                    # no output
+    b = list(base); b[1] = 4; bad.append(b)                       # dtype
+    b = list(base); b[2] = 0; bad.append(b)
+    b = list(base); b[4] = None; bad.append(b)                    # signs
+    b = list(base); b[5] = 24; bad.append(b)                      # block
+    b = list(base); b[7] = FAKE; bad.append(b)                    # latent aliases grad_w
+    for args in bad:
+        assert L.e8q_ste_backward_hadamard(*args) == 1, args
+    # rows wider than the LDS sign table
+    assert L.e8q_ste_backward_hadamard(FAKE, 1, 4, 65536, FAKE, 128, FAKE, None, 1.0, None) == 2
