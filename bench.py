@@ -219,10 +219,17 @@ def run_moe(args, torch, e8q, workloads):
     return r
 
 
-def run_qat(args, torch, e8q, workloads):
-    """One step of the simulated QAT loop on 4096x14336 bf16 latents: rotated
-    projection (q bf16 + escape count) then identity STE fused with SGD (lr 1).
-    Gradients are drawn before timing (one per step)."""
+def run_qat(args, torch, e8q, workloads, mode="qat"):
+    """One step of the simulated QAT loop on 4096x14336 bf16 latents (lr 1,
+    gradients N(0, 1e-4^2) drawn before timing, one per step):
+
+    * ``qat``: projection in the rotated basis (q bf16 + escape count), identity
+      STE fused with SGD;
+    * ``qat_restore``: projection restored to the original basis, identity STE
+      (exact for the composite) fused with SGD;
+    * ``qat_rotated_grad``: rotated projection, gradient taken back through the
+      rotation (R^T) fused with SGD.
+    """
     dev = torch.device("cuda:0")
     b = workloads.qat_loop(dev)
     w = b.w[0].clone()
@@ -232,31 +239,58 @@ def run_qat(args, torch, e8q, workloads):
     nsteps = args.steps + args.warmup
     grads = [workloads.qat_grad(k, w.shape, dev) for k in range(nsteps)]
 
-    def launch(k):
+    def fwd_rotated(k):
         e8q.e8q_project_hadamard(w, b.scale, b.signs, 128, status, q_out=q, core_bound=16, esc_count_out=esc)
+
+    def fwd_restore(k):
+        e8q.e8q_project_hadamard_restore(w, b.scale, b.signs, 128, q, status, core_bound=16, esc_count_out=esc)
+
+    def bwd_identity(k):
         e8q.e8q_ste_backward(grads[k], w_latent=w, lr=1.0)
 
+    def bwd_rotated(k):
+        e8q.e8q_ste_backward_hadamard(grads[k], b.signs, 128, w_latent=w, lr=1.0)
+
+    parts, desc = {
+        "qat": ([("project_hadamard", fwd_rotated, 4), ("ste_backward", bwd_identity, 6)],
+                "128-wide rotated projection + escape count, identity STE fused with SGD"),
+        "qat_restore": ([("project_hadamard_restore", fwd_restore, 4), ("ste_backward", bwd_identity, 6)],
+                        "128-wide projection restored to the original basis + escape count, "
+                        "identity STE fused with SGD"),
+        "qat_rotated_grad": ([("project_hadamard", fwd_rotated, 4), ("ste_backward_hadamard", bwd_rotated, 6)],
+                             "128-wide rotated projection + escape count, gradient through R^T "
+                             "fused with SGD"),
+    }[mode]
     n = w.numel()
-    return _time_launches(args, torch, launch, n, 10 * n, status,
-                          "qat step 4096x14336 bf16 latents: 128-wide rotated projection + escape count, "
-                          "identity STE fused with SGD lr 1 (grad N(0,1e-4^2))", steps_offset=True)
+    return _time_launches(args, torch, parts, n, 10 * n, status,
+                          f"qat step 4096x14336 bf16 latents: {desc} (lr 1, grad N(0,1e-4^2))",
+                          steps_offset=True)
 
 
-def _time_launches(args, torch, launch, weights, bytes_per_step, status, workload, steps_offset=False):
+def _time_launches(args, torch, parts, weights, bytes_per_step, status, workload, steps_offset=False):
+    """``parts``: [(name, launch(k), algorithmic bytes per weight)], run in order
+    each step; events around each part give per-part kernel time."""
+    if callable(parts):
+        parts = [("step", parts, None if bytes_per_step is None else bytes_per_step / weights)]
     for k in range(args.warmup):
-        launch(k)
+        for _, fn, _ in parts:
+            fn(k)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
         evs[k][0].record()
-        launch(k + args.warmup if steps_offset else k)
-        evs[k][1].record()
+        for i, (_, fn, _) in enumerate(parts):
+            fn(k + args.warmup if steps_offset else k)
+            evs[k][i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    return {"weights": weights, "wall": wall, "kernel_ms": sum(ms) / len(ms), "alg_bytes": bytes_per_step,
-            "status": int(status.item()), "workload": workload}
+    part_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(len(parts))]
+    detail = {name: {"ms": round(m, 4), "alg_bytes_per_weight": bpw,
+                     "hbm_gbs": None if bpw is None else round(bpw * weights / (m * 1e-3) / 1e9, 1)}
+              for (name, _, bpw), m in zip(parts, part_ms)}
+    return {"weights": weights, "wall": wall, "kernel_ms": sum(part_ms), "alg_bytes": bytes_per_step,
+            "status": int(status.item()), "workload": workload, "parts": detail}
 
 
 ALG_OPS_PER_WEIGHT = 15        # 7 butterfly adds (b = 128), 1 scale multiply, ~7 decoder ops
@@ -268,7 +302,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="decoder", choices=["decoder", "linear", "moe", "qat"])
+    ap.add_argument("--config", default="decoder",
+                    choices=["decoder", "linear", "moe", "qat", "qat_restore", "qat_rotated_grad"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -295,8 +330,10 @@ def main():
         del src, dst
 
     if args.config != "decoder":
-        fn = {"linear": run_linear, "moe": run_moe, "qat": run_qat}[args.config]
-        r = fn(args, torch, e8q, workloads)
+        if args.config.startswith("qat"):
+            r = run_qat(args, torch, e8q, workloads, args.config)
+        else:
+            r = {"linear": run_linear, "moe": run_moe}[args.config](args, torch, e8q, workloads)
         gbs = r["alg_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
         out = {
             "metric": f"{args.config}: Gweights/s and % of HBM peak BW, 1xMI355X",
@@ -309,7 +346,7 @@ def main():
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "cpu_baseline": None,
             "detail": {"kernel_ms_per_step": round(r["kernel_ms"], 4), "alg_bytes_per_step": r["alg_bytes"],
-                       "escapes": r.get("escapes"), "status": r["status"]},
+                       "escapes": r.get("escapes"), "status": r["status"], "parts": r.get("parts")},
         }
         print(json.dumps(out), flush=True)
         return
