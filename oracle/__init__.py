@@ -44,6 +44,8 @@ from .pipeline import (  # noqa: F401
     STATUS_INT8_RANGE,
     STATUS_ESC_OVERFLOW,
     STATUS_X_RANGE,
+    STATUS_BAD_INDEX,
+    STATUS_ESC_MISSING,
     X_LIMIT,
     ESCAPE_RECORD_DTYPE,
     bf16_to_f32,
@@ -53,6 +55,7 @@ from .pipeline import (  # noqa: F401
     project,
     encode_core_escape,
     decode_core_escape,
+    dequantize,
     ste_backward,
     sgd_update,
     escape_fraction,
@@ -66,4 +69,5 @@ from .restore import (  # noqa: F401
     rotate_grad,
     ste_backward_hadamard,
 )
+from .decode import decode_outputs  # noqa: F401
 from .brute import brute_nearest_e8  # noqa: F401

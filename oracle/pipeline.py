@@ -30,7 +30,7 @@ every stored ``2z`` fits an int16 escape field.  Such groups count as core.
 
 import numpy as np
 
-from .core import ESCAPE_SLOT, core_rank, core_unrank
+from .core import ESCAPE_SLOT, core_rank, core_size, core_unrank
 from .hadamard import fwht_blocks, kappa
 from .lattice import nearest_e8_two_z
 
@@ -39,6 +39,9 @@ STATUS_BAD_SCALE = 2
 STATUS_INT8_RANGE = 4
 STATUS_ESC_OVERFLOW = 8
 STATUS_X_RANGE = 16
+
+STATUS_BAD_INDEX = 64
+STATUS_ESC_MISSING = 128
 
 X_LIMIT = np.float32(8192.0)
 
@@ -225,11 +228,17 @@ def encode_core_escape(w, s, signs=None, had_block=0, core_bound=16,
             "two_z": two_z, "status": status}
 
 
-def decode_core_escape(core_idx, records, counts, core_bound):
-    """Rebuild every ``2z`` from core indices and escape records.
+def decode_core_escape(core_idx, records, counts, core_bound, with_status=False):
+    """Rebuild every ``2z`` from core indices and escape records
+    [E8-QAT, Figure 2(c) caption; Table 3: core decoding agreement].
 
     Records of batch item ``b`` are ``records[off_b : off_b + counts[b]]`` with
-    ``off`` the exclusive prefix sum of ``counts``.
+    ``off`` the exclusive prefix sum of ``counts`` (only the records actually
+    present count: a list cut short by the encoder's capacity is shorter).  A
+    slot holding ``ESCAPE_SLOT`` takes the record of its group; a record whose
+    slot is not ``ESCAPE_SLOT`` is ignored.  Malformed input (a reading): an
+    index ``>= |C(B)|`` decodes to 0 and sets ``STATUS_BAD_INDEX``; an escape
+    slot with no record decodes to 0 and sets ``STATUS_ESC_MISSING``.
     """
     core_idx = np.asarray(core_idx, dtype=np.uint16)
     counts = np.asarray(counts, dtype=np.int64)
@@ -237,13 +246,42 @@ def decode_core_escape(core_idx, records, counts, core_bound):
     g_total = core_idx.shape[0]
     gpb = g_total // batch
     out = np.zeros((g_total, 8), dtype=np.int64)
-    core = core_idx != ESCAPE_SLOT
-    out[core] = core_unrank(core_idx[core].astype(np.int64), core_bound)
+    status = 0
+    n_core = core_size(core_bound)
+    esc_slot = core_idx == ESCAPE_SLOT
+    ok = ~esc_slot & (core_idx.astype(np.int64) < n_core)
+    if (~esc_slot & ~ok).any():
+        status |= STATUS_BAD_INDEX
+    out[ok] = core_unrank(core_idx[ok].astype(np.int64), core_bound)
     off = np.concatenate([[0], np.cumsum(counts)])
+    have = np.zeros(g_total, dtype=bool)
     for b in range(batch):
-        r = records[off[b]:off[b + 1]]
-        out[b * gpb + r["group"].astype(np.int64)] = r["two_z"].astype(np.int64)
-    return out
+        r = records[min(off[b], len(records)):min(off[b + 1], len(records))]
+        gid = b * gpb + r["group"].astype(np.int64)
+        inside = (r["group"].astype(np.int64) < gpb)
+        gid, r = gid[inside], r[inside]
+        take = esc_slot[gid]
+        out[gid[take]] = r["two_z"][take].astype(np.int64)
+        have[gid[take]] = True
+    if (esc_slot & ~have).any():
+        status |= STATUS_ESC_MISSING
+    return (out, status) if with_status else out
+
+
+def dequantize(two_z, s, shape):
+    """``q = fl32(s_r * z)`` from ``2z`` (the projection's dequantization);
+    rows whose scale is not a positive finite number give +0 and
+    ``STATUS_BAD_SCALE``.  Returns (q float32 [shape], status)."""
+    batch, rows, cols = shape
+    s_rows = np.asarray(s, dtype=np.float32).reshape(batch * rows)
+    bad = ~(s_rows > 0) | np.isinf(s_rows)
+    gpr = cols // 8
+    row = np.repeat(np.arange(batch * rows), gpr)
+    z = np.asarray(two_z).reshape(-1, 8).astype(np.float32) * np.float32(0.5)
+    with np.errstate(over="ignore", invalid="ignore"):
+        q = s_rows[row][:, None] * z
+    q = np.where(bad[row][:, None], np.float32(0.0), q).astype(np.float32)
+    return q.reshape(shape), (STATUS_BAD_SCALE if bad.any() else 0)
 
 
 # ---------------------------------------------------------------- backward / SGD
