@@ -16,7 +16,8 @@ __all__ = [
     "E8QError", "lib", "library_path",
     "e8q_project", "e8q_project_hadamard", "e8q_project_hadamard_restore",
     "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_ste_backward",
-    "e8q_ste_backward_hadamard", "e8q_core_size",
+    "e8q_ste_backward_hadamard", "e8q_decode_core_escape", "e8q_decode_workspace_size",
+    "e8q_core_size",
     "e8q_status_string", "e8q_version",
     "ESCAPE_RECORD_BYTES", "STATUS_BITS", "F32", "BF16",
 ]
@@ -25,7 +26,7 @@ F32, BF16 = 0, 1
 ESCAPE_RECORD_BYTES = 20
 STATUS_BITS = {
     "NONFINITE": 1, "BAD_SCALE": 2, "INT8_RANGE": 4, "ESC_OVERFLOW": 8,
-    "X_RANGE": 16, "LOOKBACK_TIMEOUT": 32,
+    "X_RANGE": 16, "LOOKBACK_TIMEOUT": 32, "BAD_INDEX": 64, "ESC_MISSING": 128,
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +59,11 @@ def lib():
     L.e8q_project_hadamard_restore.restype = e
     L.e8q_ste_backward_hadamard.argtypes = [vp, e, i64, i64, vp, i32, vp, vp, f32, vp]
     L.e8q_ste_backward_hadamard.restype = e
+    L.e8q_decode_core_escape.argtypes = [vp, vp, i64, vp, i64, i64, i64, i32, vp, vp, i32, vp, vp, e, vp, e,
+                                         vp, sz, vp, vp]
+    L.e8q_decode_core_escape.restype = e
+    L.e8q_decode_workspace_size.argtypes = [i64]
+    L.e8q_decode_workspace_size.restype = sz
     L.e8q_encode_core_escape.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
                                          vp, sz, vp, vp]
     L.e8q_encode_core_escape.restype = e
@@ -208,6 +214,35 @@ def e8q_ste_backward_hadamard(grad_q, signs, had_block, grad_w=None, w_latent=No
                                            int(had_block), _ptr(grad_w), _ptr(w_latent), float(lr),
                                            _stream(grad_q, stream))
     _check("e8q_ste_backward_hadamard", code)
+
+
+def e8q_decode_workspace_size(batch):
+    return int(lib().e8q_decode_workspace_size(batch))
+
+
+def e8q_decode_core_escape(core_idx, esc, esc_count, shape, core_bound, workspace, status, row_scale=None,
+                           signs=None, had_block=0, two_z_out=None, q_out=None, w_hat_out=None,
+                           esc_records=None, stream=None):
+    """``e8q_decode_core_escape``: core indices (int16 tensor of uint16 values)
+    and escape records (uint8 tensor of 20-byte records) back to 2z, q
+    (rotated basis) and/or w_hat (original basis), for ``shape = (batch, rows,
+    cols)``.  ``esc_records`` overrides the record count taken from ``esc``."""
+    _dev(core_idx, "core_idx", (torch.int16,)); _dev(esc, "esc", (torch.uint8,))
+    _dev(esc_count, "esc_count", (torch.int64,)); _dev(workspace, "workspace", (torch.uint8,))
+    _dev(status, "status", (torch.int32,)); _dev(row_scale, "row_scale", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,)); _dev(two_z_out, "two_z_out", (torch.int8,))
+    _dev(q_out, "q_out", _WDT); _dev(w_hat_out, "w_hat_out", _WDT)
+    b, r, c = shape
+    cap = 0 if esc is None else esc.numel() // ESCAPE_RECORD_BYTES
+    if esc_records is not None:
+        cap = min(cap, int(esc_records))
+    code = lib().e8q_decode_core_escape(
+        _ptr(core_idx), _ptr(esc), cap, _ptr(esc_count), b, r, c, int(core_bound), _ptr(row_scale),
+        _ptr(signs), int(had_block), _ptr(two_z_out), _ptr(q_out),
+        _dtype_code(q_out) if q_out is not None else F32, _ptr(w_hat_out),
+        _dtype_code(w_hat_out) if w_hat_out is not None else F32, _ptr(workspace), workspace.numel(),
+        _ptr(status), _stream(core_idx, stream))
+    _check("e8q_decode_core_escape", code)
 
 
 def e8q_core_size(core_bound):

@@ -1,5 +1,6 @@
 // Host-only entry points and shared host state.
 #include <atomic>
+#include <map>
 #include <mutex>
 
 #include "e8q_core_table.hpp"
@@ -8,6 +9,48 @@
 namespace e8q {
 
 int64_t core_size_host(int32_t bound);
+
+namespace {
+std::mutex g_tab_mu;
+std::map<std::pair<int, int>, DevTable>* g_tabs = nullptr;
+
+template <typename T>
+bool upload(const std::vector<T>& v, T*& dptr) {
+    const size_t bytes = v.size() * sizeof(T);
+    if (hipMalloc(&dptr, bytes) != hipSuccess) return false;
+    if (hipMemcpy(dptr, v.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(dptr);
+        dptr = nullptr;
+        return false;
+    }
+    return true;
+}
+}  // namespace
+
+const DevTable* get_table(int32_t bound, e8q_status_t& err) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        err = E8Q_ERR_DEVICE;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_tab_mu);
+    if (!g_tabs) g_tabs = new std::map<std::pair<int, int>, DevTable>();
+    auto key = std::make_pair(dev, int(bound));
+    auto it = g_tabs->find(key);
+    if (it != g_tabs->end()) return &it->second;
+    DevTable t;
+    if (!build_core_table(bound, t.host) || !upload(t.host.data, t.dptr)) {
+        err = E8Q_ERR_DEVICE;
+        return nullptr;
+    }
+    if (!upload(t.host.points, t.dpoints)) {
+        (void)hipFree(t.dptr);
+        err = E8Q_ERR_DEVICE;
+        return nullptr;
+    }
+    auto res = g_tabs->emplace(key, std::move(t));
+    return &res.first->second;
+}
 
 int device_cu_count() {
     static std::mutex mu;

@@ -66,6 +66,10 @@ bool build_core_table(int32_t bound, CoreTable& out) {
     enumerate(bound, te > to ? te : to, pts);
     out.size = int64_t(pts.size());
     if (pts.size() > 0xFFFF) return false;
+    out.points.assign(2 * pts.size(), 0u);
+    for (size_t i = 0; i < pts.size(); ++i)
+        for (int k = 0; k < 8; ++k)
+            out.points[2 * i + k / 4] |= uint32_t(pts[i][k] + 64) << (8 * (k % 4));
 
     // F: index of the first core point with each first half.
     for (size_t i = 0; i < pts.size(); ++i) {

@@ -39,6 +39,9 @@ struct CoreTable {
     int64_t size = 0;            // |C(B)|
     RankParams p{};
     std::vector<uint16_t> data;
+    // Points in rank order, two words each: bytes 2z_i + 64, coordinates 0-3
+    // in the first word and 4-7 in the second (low byte first).
+    std::vector<uint32_t> points;
 };
 
 // Build (and self-check) the table for 0 <= bound <= 40.  Returns false if the

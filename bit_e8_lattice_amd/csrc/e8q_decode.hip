@@ -1,0 +1,350 @@
+// e8q_decode_core_escape: the exported form (16-bit core indices plus sparse
+// escape records) back to lattice points, dequantized weights in the rotated
+// basis, and restored weights in the original basis.
+//
+// E8-QAT keeps the selected lattice points exactly through its core indices
+// and escape records (Figure 2(c) caption) and checks that its decoding paths
+// agree on every core codeword (Table 3).  Decoding is a streaming map: each
+// thread owns whole groups on the projection's tile layout (so the restore
+// can reuse the lane-level inverse transform), a core index is one read of the
+// point table (2z + 64 bytes, in LDS when it fits), and an escaped slot finds
+// its record by binary search among the records of its batch item (records are
+// in ascending group order).  A one-block prologue turns the per-batch counts
+// into record offsets, clipped to the records actually present.
+#include "e8q_device.hpp"
+#include "e8q_host.hpp"
+#include "e8q_point.hpp"
+
+namespace e8q {
+
+struct DecodeArgs {
+    const uint16_t* core_idx;
+    const uint32_t* esc;          // records as 32-bit words, 5 per record
+    const uint64_t* offsets;      // [batch + 1] record offsets (workspace)
+    uint32_t groups;
+    uint32_t gpr;
+    uint32_t gpb;                 // groups per batch item
+    FastDiv gpr_div;
+    FastDiv gpb_div;
+    const float* scale;
+    float kappa;
+    const int8_t* signs;
+    uint32_t cols;
+    const uint32_t* pts;          // point table (global copy)
+    uint32_t npts;
+    int8_t* two_z;
+    void* q;
+    int q_bf16;
+    void* w_hat;
+    int w_hat_bf16;
+    uint32_t* status;
+    uint32_t num_tiles;
+};
+
+// Exclusive scan of the per-batch counts, each offset clipped to the capacity
+// (negative counts count as 0).  One block of 1024 threads, any batch size.
+__global__ __launch_bounds__(1024) void decode_offsets_kernel(const int64_t* counts, uint32_t batch,
+                                                              uint64_t capacity, uint64_t* offsets) {
+    __shared__ uint64_t part[1024];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t chunk = (batch + 1023u) / 1024u;
+    const uint32_t lo = min(tid * chunk, batch), hi = min(lo + chunk, batch);
+    uint64_t sum = 0;
+    for (uint32_t i = lo; i < hi; ++i) sum += counts[i] > 0 ? uint64_t(counts[i]) : 0ull;
+    part[tid] = sum;
+    __syncthreads();
+    for (uint32_t d = 1; d < 1024u; d <<= 1) {
+        const uint64_t v = tid >= d ? part[tid - d] : 0ull;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    uint64_t run = part[tid] - sum;
+    for (uint32_t i = lo; i < hi; ++i) {
+        offsets[i] = min(run, capacity);
+        run += counts[i] > 0 ? uint64_t(counts[i]) : 0ull;
+    }
+    if (tid == 1023u) offsets[batch] = min(part[1023], capacity);
+}
+
+// 2z of an escaped slot from its record; false when there is none.
+__device__ __forceinline__ bool find_record(const DecodeArgs& a, uint32_t b, uint32_t gib, int (&t)[8]) {
+    uint64_t lo = a.offsets[b], hi = a.offsets[b + 1];
+    // at most 64 halvings: the range never exceeds 2^64 records
+    for (int it = 0; it < 64 && lo < hi; ++it) {
+        const uint64_t mid = lo + ((hi - lo) >> 1);
+        const uint32_t key = a.esc[mid * 5];
+        if (key == gib) {
+            const uint32_t* r = a.esc + mid * 5 + 1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t wv = r[k];
+                t[2 * k] = int(int16_t(uint16_t(wv & 0xFFFFu)));
+                t[2 * k + 1] = int(int16_t(uint16_t(wv >> 16)));
+            }
+            return true;
+        }
+        if (key < gib) lo = mid + 1; else hi = mid;
+    }
+    return false;
+}
+
+__device__ __forceinline__ uint32_t bf16x2_rne_dec(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    const float2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+template <int HB, bool RESTORE, bool LDS_PTS>
+__global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
+    extern __shared__ uint32_t s_dyn[];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wv = tid >> 6;
+    const uint32_t smask_words = RESTORE ? a.cols / 2u : 0u;
+    const uint32_t wide_words = (RESTORE && HB > 128) ? uint32_t(8 * kBlock) : 0u;
+    uint32_t* s_smask = s_dyn;
+    float* s_wide = reinterpret_cast<float*>(s_dyn + smask_words);
+    uint32_t* s_pts = s_dyn + smask_words + wide_words;
+    if constexpr (RESTORE) load_sign_masks(s_smask, a.signs, a.cols, tid);
+    if constexpr (LDS_PTS) {
+        for (uint32_t i = tid; i < 2u * a.npts; i += kBlock) s_pts[i] = a.pts[i];
+    }
+    if constexpr (RESTORE || LDS_PTS) __syncthreads();
+    const uint32_t* pts = LDS_PTS ? s_pts : a.pts;
+    const LaneFwht lf = lane_fwht<(HB > 128 ? 128 : (HB < 8 ? 8 : HB))>(lane);
+    const uint32_t lpos = wv * kWave + (lane & ~15u) + lf.logical;
+    const uint32_t glast = a.groups - 1u;
+
+    for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
+        const uint32_t tbase = tile * kTileGroups + lpos;
+        uint32_t g1 = tbase, g2 = tbase + kBlock;
+        uint32_t i1 = a.core_idx[min(g1, glast)], i2 = a.core_idx[min(g2, glast)];
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const uint32_t g = g1;
+            const bool live = g < a.groups;
+            const uint32_t gl = min(g, glast);
+            const uint32_t idx = i1;
+            g1 = g2; i1 = i2;
+            if (j + 2 < kItems) {
+                g2 = g + 2u * kBlock;
+                i2 = a.core_idx[min(g2, glast)];
+            }
+            const uint32_t row = fdiv(gl, a.gpr_div);
+            uint32_t flags = 0;
+            uint32_t t0 = 0x40404040u, t1 = 0x40404040u;   // 2z + 64 bytes (z = 0)
+            bool big = false;
+            int tb[8];
+            if (idx < a.npts) {
+                t0 = pts[2u * idx];
+                t1 = pts[2u * idx + 1u];
+            } else if (idx == 0xFFFFu) {
+                const uint32_t b = fdiv(gl, a.gpb_div);
+                if (find_record(a, b, gl - b * a.gpb, tb)) {
+                    big = true;
+                } else if (live) {
+                    flags |= E8Q_STATUS_ESC_MISSING;
+                }
+            } else if (live) {
+                flags |= E8Q_STATUS_BAD_INDEX;
+            }
+            float s = 0.0f;
+            bool bad = true;
+            if (a.q || RESTORE) {
+                s = a.scale[row];
+                bad = !(s > 0.0f) || __builtin_isinf(s);
+            }
+            if (live && a.two_z) {
+                uint2 o;
+                if (big) {
+                    o = pack_i8x8(tb, flags);
+                } else {
+                    // bytes 2z + 64 in [58, 70] -> signed 2z bytes
+                    const uint32_t x0 = t0 ^ 0x40404040u, x1 = t1 ^ 0x40404040u;
+                    o = make_uint2(x0 | ((x0 & 0x40404040u) << 1), x1 | ((x1 & 0x40404040u) << 1));
+                }
+                *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = o;
+            }
+            if (live && a.q) {
+                float q[8];
+                if (!big && s > 0x1p-100f && s < 0x1p100f) {
+                    const float sh = 0.5f * s, sm = -32.0f * s;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        q[i] = fmaf(float((t0 >> (8 * i)) & 0xFFu), sh, sm);
+                        q[4 + i] = fmaf(float((t1 >> (8 * i)) & 0xFFu), sh, sm);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int ti = big ? tb[i] : int((((i < 4 ? t0 : t1) >> (8 * (i & 3))) & 0xFFu)) - 64;
+                        q[i] = bad ? 0.0f : s * (float(ti) * 0.5f);
+                    }
+                }
+                if (a.q_bf16) {
+                    uint4 p;
+                    p.x = pack_bf16x2(q[0], q[1]);
+                    p.y = pack_bf16x2(q[2], q[3]);
+                    p.z = pack_bf16x2(q[4], q[5]);
+                    p.w = pack_bf16x2(q[6], q[7]);
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.q) + uint64_t(g) * 8) = p;
+                } else {
+                    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.q) + uint64_t(g) * 8);
+                    dst[0] = make_float4(q[0], q[1], q[2], q[3]);
+                    dst[1] = make_float4(q[4], q[5], q[6], q[7]);
+                }
+            }
+            if constexpr (RESTORE) {
+                // inverse rotation across the block; every lane takes part
+                float r[8];
+                float rcorr;
+                if (big) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) r[i] = float(tb[i]);
+                    rcorr = 0.0f;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        r[i] = float((t0 >> (8 * i)) & 0xFFu);
+                        r[4 + i] = float((t1 >> (8 * i)) & 0xFFu);
+                    }
+                    rcorr = 512.0f;
+                }
+                fwht_inlane<8>(r);
+                r[0] -= rcorr;
+                const uint32_t rs = fwht_cross<HB>(r, lf, s_wide, lpos, tid);
+                const float c2 = bad ? 0.0f : (s * a.kappa) * 0.5f;
+                const float c2s = __uint_as_float(__float_as_uint(c2) ^ rs);
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = fmaf(r[i], c2s, 0.0f);   // every zero becomes +0
+                if (live) {
+                    const uint4 m = *reinterpret_cast<const uint4*>(s_smask + (gl - row * a.gpr) * 4u);
+                    if (a.w_hat_bf16) {
+                        uint4 p;
+                        p.x = bf16x2_rne_dec(y[0], y[1]) ^ m.x;
+                        p.y = bf16x2_rne_dec(y[2], y[3]) ^ m.y;
+                        p.z = bf16x2_rne_dec(y[4], y[5]) ^ m.z;
+                        p.w = bf16x2_rne_dec(y[6], y[7]) ^ m.w;
+                        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.w_hat) + uint64_t(g) * 8) = p;
+                    } else {
+                        flip_f32(y, m);
+                        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.w_hat) + uint64_t(g) * 8);
+                        dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+                        dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+                    }
+                }
+            }
+            if (live && (a.q || RESTORE) && bad) flags |= E8Q_STATUS_BAD_SCALE;
+            flush_status(flags, a.status);
+        }
+    }
+}
+
+template <bool RESTORE, bool LDS_PTS>
+static void launch_decode(int hb, const DecodeArgs& a, unsigned grid, size_t lds, hipStream_t st) {
+    if constexpr (!RESTORE) {
+        // without the restore the block size plays no part
+        hipLaunchKernelGGL((decode_kernel<8, false, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a);
+        return;
+    }
+    switch (hb) {
+        case 8: hipLaunchKernelGGL((decode_kernel<8, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 16: hipLaunchKernelGGL((decode_kernel<16, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 32: hipLaunchKernelGGL((decode_kernel<32, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 64: hipLaunchKernelGGL((decode_kernel<64, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 128: hipLaunchKernelGGL((decode_kernel<128, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 256: hipLaunchKernelGGL((decode_kernel<256, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 512: hipLaunchKernelGGL((decode_kernel<512, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 1024: hipLaunchKernelGGL((decode_kernel<1024, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 2048: hipLaunchKernelGGL((decode_kernel<2048, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 4096: hipLaunchKernelGGL((decode_kernel<4096, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        default: break;
+    }
+}
+
+static size_t decode_ws_bytes(int64_t batch) { return (size_t(batch + 1) * 8 + 255) & ~size_t(255); }
+
+}  // namespace e8q
+
+extern "C" size_t e8q_decode_workspace_size(int64_t batch) {
+    if (batch <= 0 || batch >= (int64_t(1) << 32)) return 0;
+    return e8q::decode_ws_bytes(batch);
+}
+
+extern "C" e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx, const e8q_escape_t* esc,
+                                               int64_t esc_capacity, const int64_t* esc_count,
+                                               int64_t batch, int64_t rows, int64_t cols,
+                                               int32_t core_bound, const float* row_scale,
+                                               const int8_t* signs, int32_t had_block, int8_t* two_z_out,
+                                               void* q_out, e8q_dtype_t q_dtype, void* w_hat_out,
+                                               e8q_dtype_t w_hat_dtype, void* workspace,
+                                               size_t workspace_bytes, uint32_t* status_dev, void* stream) {
+    using namespace e8q;
+    if (!core_idx || !esc_count || !status_dev || !workspace) return E8Q_ERR_INVALID;
+    if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 8) return E8Q_ERR_INVALID;
+    if (core_bound < 0 || core_bound > 40) return E8Q_ERR_INVALID;
+    if (esc_capacity < 0 || (esc_capacity > 0 && !esc)) return E8Q_ERR_INVALID;
+    if (reinterpret_cast<uintptr_t>(esc) & 3u) return E8Q_ERR_INVALID;   // records are read as 32-bit words
+    if (!two_z_out && !q_out && !w_hat_out) return E8Q_ERR_INVALID;
+    if ((q_out || w_hat_out) && !row_scale) return E8Q_ERR_INVALID;
+    if (q_out && q_dtype != E8Q_F32 && q_dtype != E8Q_BF16) return E8Q_ERR_INVALID;
+    if (w_hat_out) {
+        if (w_hat_dtype != E8Q_F32 && w_hat_dtype != E8Q_BF16) return E8Q_ERR_INVALID;
+        const e8q_status_t st = check_block(signs, had_block, cols);
+        if (st != E8Q_OK) return st;
+    }
+    if (batch >= (int64_t(1) << 32)) return E8Q_ERR_UNSUPPORTED;
+    if (workspace_bytes < decode_ws_bytes(batch) || (reinterpret_cast<uintptr_t>(workspace) & 7u))
+        return E8Q_ERR_INVALID;
+    const double groups = double(batch) * double(rows) * double(cols / 8);
+    if (groups >= 4294967295.0 || double(rows) * double(cols / 8) >= 4294967295.0) return E8Q_ERR_UNSUPPORTED;
+    const bool restore = w_hat_out != nullptr;
+    const size_t base_lds = restore ? size_t(cols / 2) * 4 + (had_block > 128 ? size_t(8 * kBlock) * 4 : 0) : 0;
+    if (base_lds > 60 * 1024) return E8Q_ERR_UNSUPPORTED;
+
+    e8q_status_t err = E8Q_OK;
+    const DevTable* tab = get_table(core_bound, err);
+    if (!tab) return err;
+
+    DecodeArgs a;
+    a.core_idx = core_idx;
+    a.esc = reinterpret_cast<const uint32_t*>(esc);
+    a.offsets = static_cast<const uint64_t*>(workspace);
+    a.gpr = uint32_t(cols / 8);
+    a.gpb = uint32_t(uint64_t(rows) * a.gpr);
+    a.groups = uint32_t(uint64_t(batch) * a.gpb);
+    a.gpr_div = make_fastdiv(a.gpr);
+    a.gpb_div = make_fastdiv(a.gpb);
+    a.scale = row_scale;
+    a.kappa = kappa_for(had_block);
+    a.signs = signs;
+    a.cols = uint32_t(cols);
+    a.pts = tab->dpoints;
+    a.npts = uint32_t(tab->host.size);
+    a.two_z = two_z_out;
+    a.q = q_out;
+    a.q_bf16 = q_dtype == E8Q_BF16;
+    a.w_hat = w_hat_out;
+    a.w_hat_bf16 = w_hat_dtype == E8Q_BF16;
+    a.status = status_dev;
+    a.num_tiles = uint32_t((uint64_t(a.groups) + kTileGroups - 1) / kTileGroups);
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
+                       uint64_t(esc_capacity), static_cast<uint64_t*>(workspace));
+    const size_t pts_lds = size_t(a.npts) * 8;
+    const bool lds_pts = base_lds + pts_lds <= 60 * 1024;
+    const size_t lds = base_lds + (lds_pts ? pts_lds : 0);
+    const unsigned grid = grid_for(a.num_tiles, 1, lds <= 40 * 1024 ? 3 : 2);
+    if (restore) {
+        if (lds_pts) launch_decode<true, true>(had_block, a, grid, lds, s);
+        else launch_decode<true, false>(had_block, a, grid, lds, s);
+    } else {
+        if (lds_pts) launch_decode<false, true>(0, a, grid, lds, s);
+        else launch_decode<false, false>(0, a, grid, lds, s);
+    }
+    return launch_status();
+}

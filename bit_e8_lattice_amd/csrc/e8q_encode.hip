@@ -349,46 +349,6 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
 
 namespace {
 
-struct DevTable {
-    uint16_t* dptr = nullptr;
-    CoreTable host;
-};
-
-std::mutex g_tab_mu;
-std::map<std::pair<int, int>, DevTable>* g_tabs = nullptr;
-
-// Rank table for (current device, bound), uploaded once and kept for the
-// life of the process.
-const DevTable* get_table(int32_t bound, e8q_status_t& err) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        err = E8Q_ERR_DEVICE;
-        return nullptr;
-    }
-    std::lock_guard<std::mutex> lk(g_tab_mu);
-    if (!g_tabs) g_tabs = new std::map<std::pair<int, int>, DevTable>();
-    auto key = std::make_pair(dev, int(bound));
-    auto it = g_tabs->find(key);
-    if (it != g_tabs->end()) return &it->second;
-    DevTable t;
-    if (!build_core_table(bound, t.host)) {
-        err = E8Q_ERR_DEVICE;
-        return nullptr;
-    }
-    const size_t bytes = t.host.data.size() * sizeof(uint16_t);
-    if (hipMalloc(&t.dptr, bytes) != hipSuccess) {
-        err = E8Q_ERR_DEVICE;
-        return nullptr;
-    }
-    if (hipMemcpy(t.dptr, t.host.data.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
-        (void)hipFree(t.dptr);
-        err = E8Q_ERR_DEVICE;
-        return nullptr;
-    }
-    auto res = g_tabs->emplace(key, std::move(t));
-    return &res.first->second;
-}
-
 uint32_t tiles_for(int64_t batch, int64_t rows, int64_t cols) {
     const uint64_t groups = uint64_t(batch) * uint64_t(rows) * uint64_t(cols / 8);
     return uint32_t((groups + kTileGroups - 1) / kTileGroups);

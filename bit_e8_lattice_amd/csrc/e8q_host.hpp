@@ -6,8 +6,21 @@
 #include <stdint.h>
 
 #include "e8q.h"
+#include "e8q_core_table.hpp"
 
 namespace e8q {
+
+// Core tables of one core bound on one device: the rank table (uint16) and the
+// points in rank order (two uint32 words per point), uploaded on first use
+// and kept for the life of the process.
+struct DevTable {
+    uint16_t* dptr = nullptr;
+    uint32_t* dpoints = nullptr;
+    CoreTable host;
+};
+
+// Tables for (current device, bound); nullptr with err set on failure.
+const DevTable* get_table(int32_t bound, e8q_status_t& err);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -81,7 +81,9 @@ enum {
     E8Q_STATUS_INT8_RANGE = 4u,      /* a 2z value was saturated in an int8 output       */
     E8Q_STATUS_ESC_OVERFLOW = 8u,    /* more escapes than esc_capacity; records cut      */
     E8Q_STATUS_X_RANGE = 16u,        /* a group had |x_i| >= 8192                        */
-    E8Q_STATUS_LOOKBACK_TIMEOUT = 32u /* escape offsets not resolved in time (outputs invalid) */
+    E8Q_STATUS_LOOKBACK_TIMEOUT = 32u, /* escape offsets not resolved in time (outputs invalid) */
+    E8Q_STATUS_BAD_INDEX = 64u,      /* decode: a core index >= |C(B)| (decoded as 0)    */
+    E8Q_STATUS_ESC_MISSING = 128u    /* decode: an escaped slot had no record (decoded as 0) */
 };
 
 typedef enum { E8Q_F32 = 0, E8Q_BF16 = 1 } e8q_dtype_t;
@@ -233,6 +235,53 @@ e8q_status_t e8q_ste_backward_hadamard(const void* grad_q, e8q_dtype_t dtype,
                                        const int8_t* signs, int32_t had_block,
                                        void* grad_w, void* w_latent, float lr,
                                        void* stream);
+
+/* ---------------------------------------------------------------------------
+ * e8q_decode_core_escape -- the exported form back to lattice points and
+ * weights (E8-QAT Figure 2(c) caption: core indices and escape records keep
+ * the final lattice points exactly; Table 3: every core codeword decodes the
+ * same on each decoding path).
+ *
+ *   core_idx     [batch*rows*cols/8] uint16 as written by e8q_encode_core_escape
+ *   esc, esc_capacity   the records array and how many records it holds
+ *                (4-byte aligned; NULL only with esc_capacity == 0)
+ *   esc_count    [batch] int64 per-batch escape counts; the records of batch
+ *                item i start at the sum of the earlier counts (clipped to
+ *                esc_capacity: a list the encoder cut short decodes with
+ *                E8Q_STATUS_ESC_MISSING for the groups whose record is gone)
+ *   core_bound   the encoder's B
+ *   row_scale    [batch*rows] float32 s_r; required with q_out or w_hat_out
+ *   signs, had_block   the encoder's rotation; required with w_hat_out
+ *   two_z_out    [batch, rows, cols] int8 2z (saturated, E8Q_STATUS_INT8_RANGE), or NULL
+ *   q_out        [batch, rows, cols] q = fl32(s z) in the rotated basis (the
+ *                projection's dequantization, bit for bit), q_dtype F32 or BF16, or NULL
+ *   w_hat_out    [batch, rows, cols] w_hat = R^T (s z) in the original basis
+ *                (as e8q_project_hadamard_restore), w_hat_dtype F32 or BF16, or NULL
+ *   workspace    device scratch of e8q_decode_workspace_size(batch) bytes,
+ *                8-byte aligned; clobbered; not shared by concurrent calls
+ * At least one output must be non-NULL.  A slot that holds 0xFFFF takes the
+ * record of its group (binary search: the records of a batch item must be in
+ * ascending group order, as the encoder writes them); records of slots that
+ * are not escaped are ignored.  An index >= |C(B)| other than 0xFFFF decodes
+ * to 0 (E8Q_STATUS_BAD_INDEX); an escaped slot with no record decodes to 0
+ * (E8Q_STATUS_ESC_MISSING).  A row whose scale is not a positive finite
+ * number gives q = +0 and w_hat = sigma * (+0) (E8Q_STATUS_BAD_SCALE).
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx,
+                                    const e8q_escape_t* esc, int64_t esc_capacity,
+                                    const int64_t* esc_count,
+                                    int64_t batch, int64_t rows, int64_t cols,
+                                    int32_t core_bound,
+                                    const float* row_scale,
+                                    const int8_t* signs, int32_t had_block,
+                                    int8_t* two_z_out,
+                                    void* q_out, e8q_dtype_t q_dtype,
+                                    void* w_hat_out, e8q_dtype_t w_hat_dtype,
+                                    void* workspace, size_t workspace_bytes,
+                                    uint32_t* status_dev, void* stream);
+
+/* Workspace bytes e8q_decode_core_escape needs (0 on a bad batch count). */
+size_t e8q_decode_workspace_size(int64_t batch);
 
 /* |C(core_bound)|, the number of core points; -1 if core_bound is outside [0, 40].
  * Host-only. */

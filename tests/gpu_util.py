@@ -123,3 +123,34 @@ def same_bits_or_nan(a, b):
     if not np.array_equal(na, nb):
         return f"NaN positions differ ({na.sum()} vs {nb.sum()})"
     return first_mismatch(a[~na].view(np.uint32), b[~nb].view(np.uint32))
+
+
+def upload_export(enc, d):
+    """The oracle's exported form (core indices, records, counts) as device tensors."""
+    core = torch.from_numpy(enc["core_idx"].view(np.int16).copy()).to(d)
+    rec = enc["records"]
+    esc = torch.from_numpy(rec.view(np.uint8).reshape(-1).copy()).to(d) if len(rec) else None
+    cnt = torch.from_numpy(np.asarray(enc["counts"], np.int64).copy()).to(d)
+    return core, esc, cnt
+
+
+def run_decode(core, esc, cnt, shape, bound, s=None, signs=None, hb=0, two_z=True, q_dtype=None,
+               w_hat_dtype=None, esc_records=None):
+    d = core.device
+    batch = shape[0]
+    st = torch.zeros(1, dtype=torch.int32, device=d)
+    ws = torch.empty(e8q.e8q_decode_workspace_size(batch), dtype=torch.uint8, device=d)
+    tz = torch.empty(shape, dtype=torch.int8, device=d) if two_z else None
+    q = torch.empty(shape, dtype=q_dtype, device=d) if q_dtype is not None else None
+    wh = torch.empty(shape, dtype=w_hat_dtype, device=d) if w_hat_dtype is not None else None
+    e8q.e8q_decode_core_escape(core, esc, cnt, shape, bound, ws, st, row_scale=s, signs=signs,
+                               had_block=hb, two_z_out=tz, q_out=q, w_hat_out=wh, esc_records=esc_records)
+    torch.cuda.synchronize()
+    out = {"status": int(st.item()) & 0xFFFFFFFF}
+    if tz is not None:
+        out["two_z_i8"] = tz.cpu().numpy()
+    if q is not None:
+        out["q"] = u16(q) if q_dtype == torch.bfloat16 else q.cpu().numpy()
+    if wh is not None:
+        out["w_hat"] = u16(wh) if w_hat_dtype == torch.bfloat16 else wh.cpu().numpy()
+    return out
