@@ -171,6 +171,62 @@ def run_dense_decoder(args, torch, e8q, workloads):
     }
 
 
+def run_decode(args, torch, e8q, workloads, kind):
+    """Decode of the whole dense decoder's exported form (encoded once,
+    untimed; the weights are then freed): ``decode`` writes the restored bf16
+    weights in the original basis, ``decode_q`` the bf16 q in the rotated basis.
+    Three launches per step, one per matrix shape."""
+    dev = torch.device("cuda:0")
+    batches = workloads.dense_decoder(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    enc = []
+    for b in batches:
+        nb, rows, cols = b.w.shape
+        groups = nb * rows * cols // 8
+        core = torch.empty(groups, dtype=torch.int16, device=dev)
+        esc = torch.empty((groups // 16) * e8q.ESCAPE_RECORD_BYTES, dtype=torch.uint8, device=dev)
+        cnt = torch.empty(nb, dtype=torch.int64, device=dev)
+        ws = torch.empty(e8q.e8q_encode_workspace_size(nb, rows, cols), dtype=torch.uint8, device=dev)
+        e8q.e8q_encode_core_escape(b.w, b.scale, 16, core, esc, cnt, ws, status, signs=b.signs, had_block=128)
+        torch.cuda.synchronize()
+        enc.append({"shape": (nb, rows, cols), "core": core, "esc": esc, "cnt": cnt, "scale": b.scale,
+                    "signs": b.signs, "escapes": int(cnt.sum().item()),
+                    "out": torch.empty((nb, rows, cols), dtype=torch.bfloat16, device=dev),
+                    "ws": torch.empty(e8q.e8q_decode_workspace_size(nb), dtype=torch.uint8, device=dev)})
+        b.w = None
+        del ws
+    torch.cuda.empty_cache()
+
+    def part(e):
+        def fn(k):
+            if kind == "decode":
+                e8q.e8q_decode_core_escape(e["core"], e["esc"], e["cnt"], e["shape"], 16, e["ws"], status,
+                                           row_scale=e["scale"], signs=e["signs"], had_block=128,
+                                           w_hat_out=e["out"])
+            else:
+                e8q.e8q_decode_core_escape(e["core"], e["esc"], e["cnt"], e["shape"], 16, e["ws"], status,
+                                           row_scale=e["scale"], q_out=e["out"])
+        return fn
+
+    parts = []
+    for e in enc:
+        nb, rows, cols = e["shape"]
+        n = nb * rows * cols
+        # index 0.25 B/w, records, counts, scales, signs (restore) in; 2 B/w out
+        bpw = (2 * (n // 8) + 20 * e["escapes"] + 8 * nb + 4 * nb * rows
+               + (cols if kind == "decode" else 0) + 2 * n) / n
+        parts.append((f"{nb}x{rows}x{cols}", part(e), bpw, n))
+    n = sum(e["out"].numel() for e in enc)
+    alg = sum(bpw * pw for (_, _, bpw, pw) in parts)
+    what = ("restored bf16 weights in the original basis (inverse 128-wide Walsh-Hadamard, sign flip)"
+            if kind == "decode" else "bf16 q = s z in the rotated basis")
+    r = _time_launches(args, torch, parts, n, alg, status,
+                       "dense decoder 32 blocks x (q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008): "
+                       f"core ||2z||^2<=16 indices + escape records decoded to {what}")
+    r["escapes"] = sum(e["escapes"] for e in enc)
+    return r
+
+
 def run_linear(args, torch, e8q, workloads):
     """4096x4096 bf16 rotated projection (q in bf16), cycling over 8 copies of
     the matrix (537 MB) so that the 256 MB last-level cache cannot hold the input."""
@@ -272,23 +328,24 @@ def _time_launches(args, torch, parts, weights, bytes_per_step, status, workload
     each step; events around each part give per-part kernel time."""
     if callable(parts):
         parts = [("step", parts, None if bytes_per_step is None else bytes_per_step / weights)]
+    parts = [p if len(p) == 4 else (p[0], p[1], p[2], weights) for p in parts]
     for k in range(args.warmup):
-        for _, fn, _ in parts:
+        for _, fn, _, _ in parts:
             fn(k)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
         evs[k][0].record()
-        for i, (_, fn, _) in enumerate(parts):
+        for i, (_, fn, _, _) in enumerate(parts):
             fn(k + args.warmup if steps_offset else k)
             evs[k][i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     part_ms = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(len(parts))]
-    detail = {name: {"ms": round(m, 4), "alg_bytes_per_weight": bpw,
-                     "hbm_gbs": None if bpw is None else round(bpw * weights / (m * 1e-3) / 1e9, 1)}
-              for (name, _, bpw), m in zip(parts, part_ms)}
+    detail = {name: {"ms": round(m, 4), "alg_bytes_per_weight": None if bpw is None else round(bpw, 4),
+                     "hbm_gbs": None if bpw is None else round(bpw * pw / (m * 1e-3) / 1e9, 1)}
+              for (name, _, bpw, pw), m in zip(parts, part_ms)}
     return {"weights": weights, "wall": wall, "kernel_ms": sum(part_ms), "alg_bytes": bytes_per_step,
             "status": int(status.item()), "workload": workload, "parts": detail}
 
@@ -303,7 +360,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder",
-                    choices=["decoder", "linear", "moe", "qat", "qat_restore", "qat_rotated_grad"])
+                    choices=["decoder", "linear", "moe", "qat", "qat_restore", "qat_rotated_grad",
+                             "decode", "decode_q"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -332,6 +390,8 @@ def main():
     if args.config != "decoder":
         if args.config.startswith("qat"):
             r = run_qat(args, torch, e8q, workloads, args.config)
+        elif args.config.startswith("decode"):
+            r = run_decode(args, torch, e8q, workloads, args.config)
         else:
             r = {"linear": run_linear, "moe": run_moe}[args.config](args, torch, e8q, workloads)
         gbs = r["alg_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9

@@ -2,6 +2,7 @@
 #include <atomic>
 #include <map>
 #include <mutex>
+#include <tuple>
 
 #include "e8q_core_table.hpp"
 #include "e8q_host.hpp"
@@ -66,6 +67,30 @@ int device_cu_count() {
         cache[dev] = cu;
     }
     return cache[dev];
+}
+
+unsigned resident_grid(const void* func, unsigned block, size_t lds, uint64_t tiles) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void*, unsigned, size_t>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int per_cu = 0;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        const auto key = std::make_tuple(dev, func, block, lds);
+        auto it = cache.find(key);
+        if (it != cache.end()) {
+            per_cu = it->second;
+        } else {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, int(block), lds) != hipSuccess ||
+                per_cu < 1)
+                per_cu = 1;
+            cache.emplace(key, per_cu);
+        }
+    }
+    const uint64_t cap = uint64_t(device_cu_count()) * uint64_t(per_cu);
+    if (tiles < 1) tiles = 1;
+    return unsigned(tiles < cap ? tiles : cap);
 }
 
 }  // namespace e8q

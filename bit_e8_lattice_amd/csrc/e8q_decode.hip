@@ -117,22 +117,38 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     const uint32_t lpos = wv * kWave + (lane & ~15u) + lf.logical;
     const uint32_t glast = a.groups - 1u;
 
-    for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
-        const uint32_t tbase = tile * kTileGroups + lpos;
-        uint32_t g1 = tbase, g2 = tbase + kBlock;
-        uint32_t i1 = a.core_idx[min(g1, glast)], i2 = a.core_idx[min(g2, glast)];
+    // The indices and row scales of the next tile are loaded while this tile is
+    // decoded (the per-group work is short, so a prefetch within the tile
+    // cannot cover the memory latency).
+    const bool need_s = a.q != nullptr || RESTORE;
+    uint32_t nidx[kItems];
+    float ns[kItems];
+    auto load_tile = [&](uint32_t tile) {
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
-            const uint32_t g = g1;
+            const uint32_t gn = min(tile * kTileGroups + uint32_t(j) * kBlock + lpos, glast);
+            nidx[j] = a.core_idx[gn];
+            ns[j] = need_s ? a.scale[fdiv(gn, a.gpr_div)] : 0.0f;
+        }
+    };
+    if (blockIdx.x < a.num_tiles) load_tile(blockIdx.x);
+    for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
+        uint32_t cidx[kItems];
+        float cs[kItems];
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            cidx[j] = nidx[j];
+            cs[j] = ns[j];
+        }
+        if (tile + gridDim.x < a.num_tiles) load_tile(tile + gridDim.x);
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const uint32_t g = tile * kTileGroups + uint32_t(j) * kBlock + lpos;
             const bool live = g < a.groups;
             const uint32_t gl = min(g, glast);
-            const uint32_t idx = i1;
-            g1 = g2; i1 = i2;
-            if (j + 2 < kItems) {
-                g2 = g + 2u * kBlock;
-                i2 = a.core_idx[min(g2, glast)];
-            }
+            const uint32_t idx = cidx[j];
             const uint32_t row = fdiv(gl, a.gpr_div);
+            const float s_row = cs[j];
             uint32_t flags = 0;
             uint32_t t0 = 0x40404040u, t1 = 0x40404040u;   // 2z + 64 bytes (z = 0)
             bool big = false;
@@ -150,12 +166,8 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
             } else if (live) {
                 flags |= E8Q_STATUS_BAD_INDEX;
             }
-            float s = 0.0f;
-            bool bad = true;
-            if (a.q || RESTORE) {
-                s = a.scale[row];
-                bad = !(s > 0.0f) || __builtin_isinf(s);
-            }
+            const float s = s_row;
+            const bool bad = !(s > 0.0f) || __builtin_isinf(s);
             if (live && a.two_z) {
                 uint2 o;
                 if (big) {
@@ -184,11 +196,11 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
                     }
                 }
                 if (a.q_bf16) {
-                    uint4 p;
-                    p.x = pack_bf16x2(q[0], q[1]);
-                    p.y = pack_bf16x2(q[2], q[3]);
-                    p.z = pack_bf16x2(q[4], q[5]);
-                    p.w = pack_bf16x2(q[6], q[7]);
+                    uint4 p;   // q is never NaN: the hardware conversion rounds to nearest even
+                    p.x = bf16x2_rne_dec(q[0], q[1]);
+                    p.y = bf16x2_rne_dec(q[2], q[3]);
+                    p.z = bf16x2_rne_dec(q[4], q[5]);
+                    p.w = bf16x2_rne_dec(q[6], q[7]);
                     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.q) + uint64_t(g) * 8) = p;
                 } else {
                     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.q) + uint64_t(g) * 8);
@@ -244,23 +256,23 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
 }
 
 template <bool RESTORE, bool LDS_PTS>
-static void launch_decode(int hb, const DecodeArgs& a, unsigned grid, size_t lds, hipStream_t st) {
+static void launch_decode(int hb, const DecodeArgs& a, size_t lds, hipStream_t st) {
     if constexpr (!RESTORE) {
         // without the restore the block size plays no part
-        hipLaunchKernelGGL((decode_kernel<8, false, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a);
+        launch_tiles(decode_kernel<8, false, LDS_PTS>, a, a.num_tiles, kBlock, lds, st);
         return;
     }
     switch (hb) {
-        case 8: hipLaunchKernelGGL((decode_kernel<8, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((decode_kernel<16, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((decode_kernel<32, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 64: hipLaunchKernelGGL((decode_kernel<64, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 128: hipLaunchKernelGGL((decode_kernel<128, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 256: hipLaunchKernelGGL((decode_kernel<256, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 512: hipLaunchKernelGGL((decode_kernel<512, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 1024: hipLaunchKernelGGL((decode_kernel<1024, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 2048: hipLaunchKernelGGL((decode_kernel<2048, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 4096: hipLaunchKernelGGL((decode_kernel<4096, RESTORE, LDS_PTS>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 8: launch_tiles(decode_kernel<8, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 16: launch_tiles(decode_kernel<16, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 32: launch_tiles(decode_kernel<32, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 64: launch_tiles(decode_kernel<64, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 128: launch_tiles(decode_kernel<128, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 256: launch_tiles(decode_kernel<256, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 512: launch_tiles(decode_kernel<512, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 1024: launch_tiles(decode_kernel<1024, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 2048: launch_tiles(decode_kernel<2048, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 4096: launch_tiles(decode_kernel<4096, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
         default: break;
     }
 }
@@ -338,13 +350,12 @@ extern "C" e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx, const e
     const size_t pts_lds = size_t(a.npts) * 8;
     const bool lds_pts = base_lds + pts_lds <= 60 * 1024;
     const size_t lds = base_lds + (lds_pts ? pts_lds : 0);
-    const unsigned grid = grid_for(a.num_tiles, 1, lds <= 40 * 1024 ? 3 : 2);
     if (restore) {
-        if (lds_pts) launch_decode<true, true>(had_block, a, grid, lds, s);
-        else launch_decode<true, false>(had_block, a, grid, lds, s);
+        if (lds_pts) launch_decode<true, true>(had_block, a, lds, s);
+        else launch_decode<true, false>(had_block, a, lds, s);
     } else {
-        if (lds_pts) launch_decode<false, true>(0, a, grid, lds, s);
-        else launch_decode<false, false>(0, a, grid, lds, s);
+        if (lds_pts) launch_decode<false, true>(0, a, lds, s);
+        else launch_decode<false, false>(0, a, lds, s);
     }
     return launch_status();
 }

@@ -357,19 +357,19 @@ uint32_t tiles_for(int64_t batch, int64_t rows, int64_t cols) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 template <typename WT, bool LDS, bool FAST>
-void launch_encode(int hb, const EncodeArgs& a, unsigned grid, size_t lds, hipStream_t st) {
+void launch_encode(int hb, const EncodeArgs& a, size_t lds, hipStream_t st) {
     switch (hb) {
-        case 0: hipLaunchKernelGGL((encode_kernel<WT, 0, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 8: hipLaunchKernelGGL((encode_kernel<WT, 8, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((encode_kernel<WT, 16, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((encode_kernel<WT, 32, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 64: hipLaunchKernelGGL((encode_kernel<WT, 64, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 128: hipLaunchKernelGGL((encode_kernel<WT, 128, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 256: hipLaunchKernelGGL((encode_kernel<WT, 256, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 512: hipLaunchKernelGGL((encode_kernel<WT, 512, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 1024: hipLaunchKernelGGL((encode_kernel<WT, 1024, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 2048: hipLaunchKernelGGL((encode_kernel<WT, 2048, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 4096: hipLaunchKernelGGL((encode_kernel<WT, 4096, LDS, FAST>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 0: launch_tiles(encode_kernel<WT, 0, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 8: launch_tiles(encode_kernel<WT, 8, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 16: launch_tiles(encode_kernel<WT, 16, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 32: launch_tiles(encode_kernel<WT, 32, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 64: launch_tiles(encode_kernel<WT, 64, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 128: launch_tiles(encode_kernel<WT, 128, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 256: launch_tiles(encode_kernel<WT, 256, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 512: launch_tiles(encode_kernel<WT, 512, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 1024: launch_tiles(encode_kernel<WT, 1024, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 2048: launch_tiles(encode_kernel<WT, 2048, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
+        case 4096: launch_tiles(encode_kernel<WT, 4096, LDS, FAST>, a, a.num_tiles, kBlock, lds, st); break;
         default: break;
     }
 }
@@ -469,14 +469,13 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
     const bool lds_tab = smask_bytes + tab_bytes <= kLdsLimit;
     const size_t lds = smask_bytes + (lds_tab ? tab_bytes : 0);
     const bool fast = lds_tab && w_dtype == E8Q_BF16 && !two_z_out && ub <= 6;
-    const unsigned grid = grid_for(a.num_tiles, 1, lds <= 50 * 1024 ? 3 : 2);
     if (w_dtype == E8Q_BF16) {
-        if (fast) launch_encode<uint16_t, true, true>(hb, a, grid, lds, s);
-        else if (lds_tab) launch_encode<uint16_t, true, false>(hb, a, grid, lds, s);
-        else launch_encode<uint16_t, false, false>(hb, a, grid, lds, s);
+        if (fast) launch_encode<uint16_t, true, true>(hb, a, lds, s);
+        else if (lds_tab) launch_encode<uint16_t, true, false>(hb, a, lds, s);
+        else launch_encode<uint16_t, false, false>(hb, a, lds, s);
     } else {
-        if (lds_tab) launch_encode<float, true, false>(hb, a, grid, lds, s);
-        else launch_encode<float, false, false>(hb, a, grid, lds, s);
+        if (lds_tab) launch_encode<float, true, false>(hb, a, lds, s);
+        else launch_encode<float, false, false>(hb, a, lds, s);
     }
     return launch_status();
 }

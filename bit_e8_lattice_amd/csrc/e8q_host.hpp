@@ -35,6 +35,20 @@ inline unsigned grid_for(uint64_t items, unsigned per_block, unsigned blocks_per
     return unsigned(need < cap ? need : cap);
 }
 
+// Blocks of `block` threads and `lds` dynamic LDS bytes that the device keeps
+// resident at once for `func` (all CUs), capped at `tiles` (at least 1).
+// Kernels that loop over tiles with a grid stride are launched with exactly
+// this many blocks: more would only start when resident blocks finish, i.e.
+// at the end, and stretch the tail.
+unsigned resident_grid(const void* func, unsigned block, size_t lds, uint64_t tiles);
+
+template <typename A>
+inline void launch_tiles(void (*kernel)(A), const A& args, uint64_t tiles, unsigned block, size_t lds,
+                         hipStream_t st) {
+    const unsigned grid = resident_grid(reinterpret_cast<const void*>(kernel), block, lds, tiles);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), lds, st, args);
+}
+
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Shape checks common to the projection and encode calls.  Returns E8Q_OK or

@@ -253,22 +253,22 @@ __global__ void zero_u64_kernel(unsigned long long* p, uint32_t n) {
 }
 
 template <typename WT, bool FAST, bool RESTORE>
-static void launch_project(int hb, const ProjectArgs& a, unsigned grid, size_t lds, hipStream_t st) {
+static void launch_project(int hb, const ProjectArgs& a, size_t lds, hipStream_t st) {
     switch (hb) {
         case 0:
             if constexpr (!RESTORE)
-                hipLaunchKernelGGL((project_kernel<WT, 0, FAST, false>), dim3(grid), dim3(kBlock), lds, st, a);
+                launch_tiles(project_kernel<WT, 0, FAST, false>, a, a.num_tiles, kBlock, lds, st);
             break;
-        case 8: hipLaunchKernelGGL((project_kernel<WT, 8, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((project_kernel<WT, 16, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((project_kernel<WT, 32, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 64: hipLaunchKernelGGL((project_kernel<WT, 64, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 128: hipLaunchKernelGGL((project_kernel<WT, 128, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 256: hipLaunchKernelGGL((project_kernel<WT, 256, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 512: hipLaunchKernelGGL((project_kernel<WT, 512, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 1024: hipLaunchKernelGGL((project_kernel<WT, 1024, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 2048: hipLaunchKernelGGL((project_kernel<WT, 2048, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 4096: hipLaunchKernelGGL((project_kernel<WT, 4096, FAST, RESTORE>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 8: launch_tiles(project_kernel<WT, 8, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 16: launch_tiles(project_kernel<WT, 16, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 32: launch_tiles(project_kernel<WT, 32, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 64: launch_tiles(project_kernel<WT, 64, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 128: launch_tiles(project_kernel<WT, 128, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 256: launch_tiles(project_kernel<WT, 256, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 512: launch_tiles(project_kernel<WT, 512, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 1024: launch_tiles(project_kernel<WT, 1024, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 2048: launch_tiles(project_kernel<WT, 2048, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 4096: launch_tiles(project_kernel<WT, 4096, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
         default: break;
     }
 }
@@ -317,16 +317,15 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
         hipLaunchKernelGGL(zero_u64_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, s,
                            a.esc, uint32_t(batch));
     }
-    const unsigned grid = grid_for(a.num_tiles, 1, lds <= 40 * 1024 ? 3 : 2);
     if (w_hat_out) {
         if (w_dtype == E8Q_BF16)
-            launch_project<uint16_t, true, true>(had_block, a, grid, lds, s);
+            launch_project<uint16_t, true, true>(had_block, a, lds, s);
         else
-            launch_project<float, false, true>(had_block, a, grid, lds, s);
+            launch_project<float, false, true>(had_block, a, lds, s);
     } else if (w_dtype == E8Q_BF16) {
-        launch_project<uint16_t, true, false>(had_block, a, grid, lds, s);
+        launch_project<uint16_t, true, false>(had_block, a, lds, s);
     } else {
-        launch_project<float, false, false>(had_block, a, grid, lds, s);
+        launch_project<float, false, false>(had_block, a, lds, s);
     }
     return launch_status();
 }

@@ -190,18 +190,18 @@ __global__ __launch_bounds__(kBlock) void ste_hadamard_kernel(SteHadArgs a) {
 }
 
 template <typename WT>
-static void launch_ste_hadamard(int hb, const SteHadArgs& a, unsigned grid, size_t lds, hipStream_t st) {
+static void launch_ste_hadamard(int hb, const SteHadArgs& a, size_t lds, hipStream_t st) {
     switch (hb) {
-        case 8: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 8>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 16: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 16>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 32: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 32>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 64: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 64>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 128: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 128>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 256: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 256>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 512: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 512>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 1024: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 1024>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 2048: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 2048>), dim3(grid), dim3(kBlock), lds, st, a); break;
-        case 4096: hipLaunchKernelGGL((ste_hadamard_kernel<WT, 4096>), dim3(grid), dim3(kBlock), lds, st, a); break;
+        case 8: launch_tiles(ste_hadamard_kernel<WT, 8>, a, a.num_tiles, kBlock, lds, st); break;
+        case 16: launch_tiles(ste_hadamard_kernel<WT, 16>, a, a.num_tiles, kBlock, lds, st); break;
+        case 32: launch_tiles(ste_hadamard_kernel<WT, 32>, a, a.num_tiles, kBlock, lds, st); break;
+        case 64: launch_tiles(ste_hadamard_kernel<WT, 64>, a, a.num_tiles, kBlock, lds, st); break;
+        case 128: launch_tiles(ste_hadamard_kernel<WT, 128>, a, a.num_tiles, kBlock, lds, st); break;
+        case 256: launch_tiles(ste_hadamard_kernel<WT, 256>, a, a.num_tiles, kBlock, lds, st); break;
+        case 512: launch_tiles(ste_hadamard_kernel<WT, 512>, a, a.num_tiles, kBlock, lds, st); break;
+        case 1024: launch_tiles(ste_hadamard_kernel<WT, 1024>, a, a.num_tiles, kBlock, lds, st); break;
+        case 2048: launch_tiles(ste_hadamard_kernel<WT, 2048>, a, a.num_tiles, kBlock, lds, st); break;
+        case 4096: launch_tiles(ste_hadamard_kernel<WT, 4096>, a, a.num_tiles, kBlock, lds, st); break;
         default: break;
     }
 }
@@ -234,11 +234,10 @@ extern "C" e8q_status_t e8q_ste_backward_hadamard(const void* grad_q, e8q_dtype_
     a.gpr_div = make_fastdiv(a.gpr);
     a.num_tiles = uint32_t((uint64_t(a.groups) + kTileGroups - 1) / kTileGroups);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const unsigned grid = grid_for(a.num_tiles, 1, lds <= 40 * 1024 ? 3 : 2);
     if (dtype == E8Q_BF16)
-        launch_ste_hadamard<uint16_t>(had_block, a, grid, lds, s);
+        launch_ste_hadamard<uint16_t>(had_block, a, lds, s);
     else
-        launch_ste_hadamard<float>(had_block, a, grid, lds, s);
+        launch_ste_hadamard<float>(had_block, a, lds, s);
     return launch_status();
 }
 
