@@ -17,7 +17,7 @@ __all__ = [
     "e8q_project", "e8q_project_hadamard", "e8q_project_hadamard_restore",
     "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_ste_backward",
     "e8q_ste_backward_hadamard", "e8q_decode_core_escape", "e8q_decode_workspace_size",
-    "e8q_core_size",
+    "e8q_gemv_core_escape", "e8q_gemv_workspace_size", "e8q_core_size",
     "e8q_status_string", "e8q_version",
     "ESCAPE_RECORD_BYTES", "STATUS_BITS", "F32", "BF16",
 ]
@@ -64,6 +64,11 @@ def lib():
     L.e8q_decode_core_escape.restype = e
     L.e8q_decode_workspace_size.argtypes = [i64]
     L.e8q_decode_workspace_size.restype = sz
+    L.e8q_gemv_core_escape.argtypes = [vp, vp, i64, vp, i64, i64, i64, i32, vp, vp, i32, vp, e, i64, vp,
+                                       vp, sz, vp, vp]
+    L.e8q_gemv_core_escape.restype = e
+    L.e8q_gemv_workspace_size.argtypes = [i64, i64, i64]
+    L.e8q_gemv_workspace_size.restype = sz
     L.e8q_encode_core_escape.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
                                          vp, sz, vp, vp]
     L.e8q_encode_core_escape.restype = e
@@ -243,6 +248,32 @@ def e8q_decode_core_escape(core_idx, esc, esc_count, shape, core_bound, workspac
         _dtype_code(w_hat_out) if w_hat_out is not None else F32, _ptr(workspace), workspace.numel(),
         _ptr(status), _stream(core_idx, stream))
     _check("e8q_decode_core_escape", code)
+
+
+def e8q_gemv_workspace_size(batch, m, cols):
+    return int(lib().e8q_gemv_workspace_size(batch, m, cols))
+
+
+def e8q_gemv_core_escape(core_idx, esc, esc_count, shape, core_bound, row_scale, x, y_out, workspace, status,
+                         signs=None, had_block=0, esc_records=None, stream=None):
+    """``e8q_gemv_core_escape``: ``y_out[b, t, r] = sum_c W_hat[b, r, c] x[b, t, c]``
+    from the exported form, for ``shape = (batch, rows, cols)`` and ``x``
+    [batch, m, cols]."""
+    _dev(core_idx, "core_idx", (torch.int16,)); _dev(esc, "esc", (torch.uint8,))
+    _dev(esc_count, "esc_count", (torch.int64,)); _dev(row_scale, "row_scale", (torch.float32,))
+    _dev(x, "x", _WDT); _dev(y_out, "y_out", (torch.float32,)); _dev(workspace, "workspace", (torch.uint8,))
+    _dev(status, "status", (torch.int32,)); _dev(signs, "signs", (torch.int8,))
+    b, r, c = shape
+    if x.dim() != 3 or x.shape[0] != b or x.shape[2] != c:
+        raise ValueError("x must be [batch, m, cols]")
+    cap = 0 if esc is None else esc.numel() // ESCAPE_RECORD_BYTES
+    if esc_records is not None:
+        cap = min(cap, int(esc_records))
+    code = lib().e8q_gemv_core_escape(
+        _ptr(core_idx), _ptr(esc), cap, _ptr(esc_count), b, r, c, int(core_bound), _ptr(row_scale), _ptr(signs),
+        int(had_block), _ptr(x), _dtype_code(x), x.shape[1], _ptr(y_out), _ptr(workspace), workspace.numel(),
+        _ptr(status), _stream(core_idx, stream))
+    _check("e8q_gemv_core_escape", code)
 
 
 def e8q_core_size(core_bound):

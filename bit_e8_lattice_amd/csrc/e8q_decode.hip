@@ -68,14 +68,15 @@ __global__ __launch_bounds__(1024) void decode_offsets_kernel(const int64_t* cou
 }
 
 // 2z of an escaped slot from its record; false when there is none.
-__device__ __forceinline__ bool find_record(const DecodeArgs& a, uint32_t b, uint32_t gib, int (&t)[8]) {
-    uint64_t lo = a.offsets[b], hi = a.offsets[b + 1];
+__device__ __forceinline__ bool find_record(const uint32_t* esc, const uint64_t* offsets, uint32_t b, uint32_t gib,
+                                            int (&t)[8]) {
+    uint64_t lo = offsets[b], hi = offsets[b + 1];
     // at most 64 halvings: the range never exceeds 2^64 records
     for (int it = 0; it < 64 && lo < hi; ++it) {
         const uint64_t mid = lo + ((hi - lo) >> 1);
-        const uint32_t key = a.esc[mid * 5];
+        const uint32_t key = esc[mid * 5];
         if (key == gib) {
-            const uint32_t* r = a.esc + mid * 5 + 1;
+            const uint32_t* r = esc + mid * 5 + 1;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t wv = r[k];
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
                 t1 = pts[2u * idx + 1u];
             } else if (idx == 0xFFFFu) {
                 const uint32_t b = fdiv(gl, a.gpb_div);
-                if (find_record(a, b, gl - b * a.gpb, tb)) {
+                if (find_record(a.esc, a.offsets, b, gl - b * a.gpb, tb)) {
                     big = true;
                 } else if (live) {
                     flags |= E8Q_STATUS_ESC_MISSING;
@@ -357,5 +358,293 @@ extern "C" e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx, const e
         if (lds_pts) launch_decode<false, true>(0, a, lds, s);
         else launch_decode<false, false>(0, a, lds, s);
     }
+    return launch_status();
+}
+
+// ---------------------------------------------------------------- GEMV
+//
+// e8q_gemv_core_escape: y = W_hat x straight from the exported form.  With
+// W_hat = R^T (s z) and R orthogonal, y_r = s_r sum_g z_g . x~_g where
+// x~ = R x = kappa_b H_b (sigma * x) is computed once per activation vector
+// (rotate_act_kernel, the forward rotation on the projection's lanes), so the
+// product never materializes W_hat: each row reads its 16-bit indices (2 bits
+// per weight) and one table entry per group.  gemv_kernel keeps x~ of one
+// batch item in LDS; a wave owns a row at a time, its lanes stride over the
+// row's groups, and a cross-lane sum finishes the row.
+
+namespace e8q {
+
+struct RotArgs {
+    const void* x;
+    float* xt;
+    const int8_t* signs;
+    float kappa;
+    uint32_t cols;
+    uint32_t groups;
+    uint32_t gpr;
+    FastDiv gpr_div;
+    uint32_t num_tiles;
+};
+
+template <typename WT, int HB>
+__global__ __launch_bounds__(kBlock) void rotate_act_kernel(RotArgs a) {
+    extern __shared__ uint32_t s_dyn[];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wv = tid >> 6;
+    uint32_t* s_smask = s_dyn;
+    float* s_wide = reinterpret_cast<float*>(s_dyn + (HB > 0 ? a.cols / 2u : 0u));
+    if constexpr (HB > 0) {
+        load_sign_masks(s_smask, a.signs, a.cols, tid);
+        __syncthreads();
+    }
+    const LaneFwht lf = lane_fwht<(HB > 128 ? 128 : HB)>(lane);
+    const uint32_t lpos = wv * kWave + (lane & ~15u) + lf.logical;
+    const uint32_t glast = a.groups - 1u;
+    for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
+#pragma unroll 1
+        for (int j = 0; j < kItems; ++j) {
+            const uint32_t g = tile * kTileGroups + uint32_t(j) * kBlock + lpos;
+            const uint32_t gl = min(g, glast);
+            const Raw raw = load_raw<WT>(a.x, gl);
+            float v[8];
+            const uint32_t vs = rotate_group<WT, HB>(s_smask, s_wide, raw, gl - fdiv(gl, a.gpr_div) * a.gpr, lf, lpos,
+                                                     tid, v);
+            const float k = __uint_as_float(__float_as_uint(a.kappa) ^ vs);
+            if (g < a.groups) {
+                float4* dst = reinterpret_cast<float4*>(a.xt + uint64_t(g) * 8);
+                dst[0] = make_float4(v[0] * k, v[1] * k, v[2] * k, v[3] * k);
+                dst[1] = make_float4(v[4] * k, v[5] * k, v[6] * k, v[7] * k);
+            }
+        }
+    }
+}
+
+struct GemvArgs {
+    const uint16_t* core_idx;
+    const uint32_t* esc;
+    const uint64_t* offsets;
+    const float* xt;            // [batch, m, cols] rotated activations
+    const float* scale;
+    const uint32_t* pts;
+    uint32_t npts;
+    uint32_t rows;
+    uint32_t cols;
+    uint32_t gpr;
+    uint32_t rows_per_block;
+    float* y;                   // [batch, m, rows]
+    uint32_t* status;
+};
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvRows = 64;
+
+// 2z bytes (+64 bias) of one word to four floats 2z_i
+__device__ __forceinline__ void unpack4(uint32_t t, float* f) {
+    const uint32_t x = t ^ 0x40404040u;
+    const uint32_t sb = x | ((x & 0x40404040u) << 1);     // signed 2z bytes
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = float(int32_t(sb << (24 - 8 * i)) >> 24);
+}
+
+template <int M, bool LDS_PTS>
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
+    extern __shared__ uint32_t s_dyn[];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wv = tid >> 6;
+    const uint32_t b = blockIdx.y;
+    float* s_xt = reinterpret_cast<float*>(s_dyn);
+    uint32_t* s_pts = s_dyn + M * a.cols;
+    {
+        const float4* src = reinterpret_cast<const float4*>(a.xt + uint64_t(b) * M * a.cols);
+        float4* dst = reinterpret_cast<float4*>(s_xt);
+        for (uint32_t i = tid; i < M * a.cols / 4u; i += kGemvThreads) dst[i] = src[i];
+        if constexpr (LDS_PTS)
+            for (uint32_t i = tid; i < 2u * a.npts; i += kGemvThreads) s_pts[i] = a.pts[i];
+    }
+    __syncthreads();
+    const uint32_t* pts = LDS_PTS ? s_pts : a.pts;
+    const uint32_t r0 = blockIdx.x * a.rows_per_block;
+    const uint32_t r1 = min(r0 + a.rows_per_block, a.rows);
+    uint32_t flags = 0;
+    for (uint32_t r = r0 + wv; r < r1; r += kGemvThreads / kWave) {
+        const uint64_t rowg = (uint64_t(b) * a.rows + r) * a.gpr;
+        float acc[M];
+#pragma unroll
+        for (int t = 0; t < M; ++t) acc[t] = 0.0f;
+        // indices in chunks of 8 per lane, all loads of a chunk issued first
+        for (uint32_t g0 = lane; g0 < a.gpr; g0 += 8u * kWave) {
+          uint32_t ids[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+              const uint32_t g = g0 + uint32_t(c) * kWave;
+              ids[c] = g < a.gpr ? uint32_t(a.core_idx[rowg + g]) : 0u;
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t g = g0 + uint32_t(c) * kWave;
+            if (g >= a.gpr) break;
+            const uint32_t idx = ids[c];
+            float z[8];
+            if (idx < a.npts) {
+                unpack4(pts[2u * idx], z);
+                unpack4(pts[2u * idx + 1u], z + 4);
+            } else {
+                int tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (idx != 0xFFFFu) {
+                    flags |= E8Q_STATUS_BAD_INDEX;
+                } else if (!find_record(a.esc, a.offsets, b, r * a.gpr + g, tb)) {
+                    flags |= E8Q_STATUS_ESC_MISSING;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) z[i] = float(tb[i]);
+            }
+#pragma unroll
+            for (int t = 0; t < M; ++t) {
+                const float4* xp = reinterpret_cast<const float4*>(s_xt + t * a.cols + g * 8u);
+                const float4 x0 = xp[0], x1 = xp[1];
+                float s0 = z[0] * x0.x;
+                s0 = fmaf(z[1], x0.y, s0);
+                s0 = fmaf(z[2], x0.z, s0);
+                s0 = fmaf(z[3], x0.w, s0);
+                s0 = fmaf(z[4], x1.x, s0);
+                s0 = fmaf(z[5], x1.y, s0);
+                s0 = fmaf(z[6], x1.z, s0);
+                s0 = fmaf(z[7], x1.w, s0);
+                acc[t] += s0;
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 64);
+        }
+        if (lane == 0) {
+            const float s = a.scale[uint64_t(b) * a.rows + r];
+            const bool bad = !(s > 0.0f) || __builtin_isinf(s);
+            if (bad) flags |= E8Q_STATUS_BAD_SCALE;
+#pragma unroll
+            for (int t = 0; t < M; ++t) a.y[(uint64_t(b) * M + t) * a.rows + r] = bad ? 0.0f : (0.5f * s) * acc[t];
+        }
+    }
+    flush_status(flags, a.status);
+}
+
+static size_t gemv_ws_bytes(int64_t batch, int64_t m, int64_t cols) {
+    return decode_ws_bytes(batch) + ((size_t(batch) * size_t(m) * size_t(cols) * 4 + 255) & ~size_t(255));
+}
+
+template <typename WT>
+static void launch_rotate(int hb, const RotArgs& a, size_t lds, hipStream_t st) {
+    switch (hb) {
+        case 0: launch_tiles(rotate_act_kernel<WT, 0>, a, a.num_tiles, kBlock, lds, st); break;
+        case 8: launch_tiles(rotate_act_kernel<WT, 8>, a, a.num_tiles, kBlock, lds, st); break;
+        case 16: launch_tiles(rotate_act_kernel<WT, 16>, a, a.num_tiles, kBlock, lds, st); break;
+        case 32: launch_tiles(rotate_act_kernel<WT, 32>, a, a.num_tiles, kBlock, lds, st); break;
+        case 64: launch_tiles(rotate_act_kernel<WT, 64>, a, a.num_tiles, kBlock, lds, st); break;
+        case 128: launch_tiles(rotate_act_kernel<WT, 128>, a, a.num_tiles, kBlock, lds, st); break;
+        case 256: launch_tiles(rotate_act_kernel<WT, 256>, a, a.num_tiles, kBlock, lds, st); break;
+        case 512: launch_tiles(rotate_act_kernel<WT, 512>, a, a.num_tiles, kBlock, lds, st); break;
+        case 1024: launch_tiles(rotate_act_kernel<WT, 1024>, a, a.num_tiles, kBlock, lds, st); break;
+        case 2048: launch_tiles(rotate_act_kernel<WT, 2048>, a, a.num_tiles, kBlock, lds, st); break;
+        case 4096: launch_tiles(rotate_act_kernel<WT, 4096>, a, a.num_tiles, kBlock, lds, st); break;
+        default: break;
+    }
+}
+
+template <int M>
+static void launch_gemv(bool lds_pts, const GemvArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+    if (lds_pts)
+        hipLaunchKernelGGL((gemv_kernel<M, true>), grid, dim3(kGemvThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((gemv_kernel<M, false>), grid, dim3(kGemvThreads), lds, st, a);
+}
+
+}  // namespace e8q
+
+extern "C" size_t e8q_gemv_workspace_size(int64_t batch, int64_t m, int64_t cols) {
+    if (batch <= 0 || batch >= (int64_t(1) << 32) || m <= 0 || cols <= 0) return 0;
+    return e8q::gemv_ws_bytes(batch, m, cols);
+}
+
+extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q_escape_t* esc,
+                                             int64_t esc_capacity, const int64_t* esc_count, int64_t batch,
+                                             int64_t rows, int64_t cols, int32_t core_bound,
+                                             const float* row_scale, const int8_t* signs, int32_t had_block,
+                                             const void* x, e8q_dtype_t x_dtype, int64_t m, float* y_out,
+                                             void* workspace, size_t workspace_bytes, uint32_t* status_dev,
+                                             void* stream) {
+    using namespace e8q;
+    if (!core_idx || !esc_count || !row_scale || !x || !y_out || !status_dev || !workspace) return E8Q_ERR_INVALID;
+    if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 8) return E8Q_ERR_INVALID;
+    if (core_bound < 0 || core_bound > 40) return E8Q_ERR_INVALID;
+    if (esc_capacity < 0 || (esc_capacity > 0 && !esc)) return E8Q_ERR_INVALID;
+    if (reinterpret_cast<uintptr_t>(esc) & 3u) return E8Q_ERR_INVALID;
+    if (x_dtype != E8Q_F32 && x_dtype != E8Q_BF16) return E8Q_ERR_INVALID;
+    if (m != 1 && m != 2 && m != 4) return E8Q_ERR_UNSUPPORTED;
+    if (signs) {
+        const e8q_status_t st = check_block(signs, had_block, cols);
+        if (st != E8Q_OK) return st;
+    }
+    if (batch > 65535) return E8Q_ERR_UNSUPPORTED;   // one grid row per batch item
+    if (workspace_bytes < gemv_ws_bytes(batch, m, cols) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return E8Q_ERR_INVALID;
+    const double groups = double(batch) * double(rows) * double(cols / 8);
+    if (groups >= 4294967295.0 || double(batch) * double(m) * double(cols / 8) >= 4294967295.0 ||
+        double(rows) * double(cols / 8) >= 4294967295.0)
+        return E8Q_ERR_UNSUPPORTED;
+    const size_t xt_lds = size_t(m) * size_t(cols) * 4;
+    if (xt_lds > 96 * 1024) return E8Q_ERR_UNSUPPORTED;
+    const int hb = signs ? had_block : 0;
+    const size_t rot_lds = (hb > 0 ? size_t(cols / 2) * 4 : 0) + (hb > 128 ? size_t(8 * kBlock) * 4 : 0);
+    if (rot_lds > 60 * 1024) return E8Q_ERR_UNSUPPORTED;
+
+    e8q_status_t err = E8Q_OK;
+    const DevTable* tab = get_table(core_bound, err);
+    if (!tab) return err;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint64_t* offsets = static_cast<uint64_t*>(workspace);
+    float* xt = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ws_bytes(batch));
+    hipLaunchKernelGGL(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
+                       uint64_t(esc_capacity), offsets);
+
+    RotArgs ra;
+    ra.x = x;
+    ra.xt = xt;
+    ra.signs = signs;
+    ra.kappa = kappa_for(hb);
+    ra.cols = uint32_t(cols);
+    ra.gpr = uint32_t(cols / 8);
+    ra.groups = uint32_t(uint64_t(batch) * uint64_t(m) * ra.gpr);
+    ra.gpr_div = make_fastdiv(ra.gpr);
+    ra.num_tiles = uint32_t((uint64_t(ra.groups) + kTileGroups - 1) / kTileGroups);
+    if (x_dtype == E8Q_BF16)
+        launch_rotate<uint16_t>(hb, ra, rot_lds, s);
+    else
+        launch_rotate<float>(hb, ra, rot_lds, s);
+
+    GemvArgs ga;
+    ga.core_idx = core_idx;
+    ga.esc = reinterpret_cast<const uint32_t*>(esc);
+    ga.offsets = offsets;
+    ga.xt = xt;
+    ga.scale = row_scale;
+    ga.pts = tab->dpoints;
+    ga.npts = uint32_t(tab->host.size);
+    ga.rows = uint32_t(rows);
+    ga.cols = uint32_t(cols);
+    ga.gpr = uint32_t(cols / 8);
+    ga.rows_per_block = kGemvRows;
+    ga.y = y_out;
+    ga.status = status_dev;
+    const size_t pts_lds = size_t(ga.npts) * 8;
+    const bool lds_pts = xt_lds + pts_lds <= 64 * 1024;
+    const size_t lds = xt_lds + (lds_pts ? pts_lds : 0);
+    const dim3 grid(unsigned((rows + kGemvRows - 1) / kGemvRows), unsigned(batch));
+    if (m == 1) launch_gemv<1>(lds_pts, ga, grid, lds, s);
+    else if (m == 2) launch_gemv<2>(lds_pts, ga, grid, lds, s);
+    else launch_gemv<4>(lds_pts, ga, grid, lds, s);
     return launch_status();
 }

@@ -283,6 +283,40 @@ e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx,
 /* Workspace bytes e8q_decode_core_escape needs (0 on a bad batch count). */
 size_t e8q_decode_workspace_size(int64_t batch);
 
+/* ---------------------------------------------------------------------------
+ * e8q_gemv_core_escape -- y = W_hat x from the exported form, the product a
+ * 2-bit decode step serves (E8-QAT abstract: decode throughput of the 2-bit
+ * representation against BF16; Figure 2(c): the exported form).  W_hat is the
+ * restored weight matrix of each batch item (as e8q_decode_core_escape's
+ * w_hat, before any rounding); it is never formed: with x~ = kappa_b H_b
+ * (sigma * x) computed once per activation vector in float32,
+ * y_r = (s_r / 2) * sum_g 2z_g . x~_g, float32 accumulation.
+ *   core_idx, esc, esc_capacity, esc_count, core_bound, row_scale, signs,
+ *   had_block   as e8q_decode_core_escape (signs NULL: no rotation, W_hat = s z)
+ *   x            [batch, m, cols] activations, x_dtype F32 or BF16; m in {1, 2, 4}
+ *   y_out        [batch, m, rows] float32
+ *   workspace    e8q_gemv_workspace_size(batch, m, cols) bytes, 256-byte aligned
+ * Rounding: |y - W_hat x| <= 2 (L + G + 17) 2^-24 S_r per output, L = log2(b),
+ * G = ceil(cols / 512), S_r = s_r sum_g sum_i |z_gi| xbar_gi, xbar = kappa_b
+ * times the block sums of |x| (|x| itself without rotation).
+ * Limits: m * cols * 4 <= 96 KiB, batch <= 65535.  Malformed exports and bad
+ * scales are flagged as in e8q_decode_core_escape (a bad row gives y = 0).
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx,
+                                  const e8q_escape_t* esc, int64_t esc_capacity,
+                                  const int64_t* esc_count,
+                                  int64_t batch, int64_t rows, int64_t cols,
+                                  int32_t core_bound,
+                                  const float* row_scale,
+                                  const int8_t* signs, int32_t had_block,
+                                  const void* x, e8q_dtype_t x_dtype, int64_t m,
+                                  float* y_out,
+                                  void* workspace, size_t workspace_bytes,
+                                  uint32_t* status_dev, void* stream);
+
+/* Workspace bytes e8q_gemv_core_escape needs (0 on bad sizes). */
+size_t e8q_gemv_workspace_size(int64_t batch, int64_t m, int64_t cols);
+
 /* |C(core_bound)|, the number of core points; -1 if core_bound is outside [0, 40].
  * Host-only. */
 int64_t e8q_core_size(int32_t core_bound);

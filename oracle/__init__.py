@@ -70,4 +70,5 @@ from .restore import (  # noqa: F401
     ste_backward_hadamard,
 )
 from .decode import decode_outputs  # noqa: F401
+from .gemv import exact_restored, gemv_reference, rotated_magnitude  # noqa: F401
 from .brute import brute_nearest_e8  # noqa: F401

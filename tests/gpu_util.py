@@ -154,3 +154,24 @@ def run_decode(core, esc, cnt, shape, bound, s=None, signs=None, hb=0, two_z=Tru
     if wh is not None:
         out["w_hat"] = u16(wh) if w_hat_dtype == torch.bfloat16 else wh.cpu().numpy()
     return out
+
+
+def run_gemv(core, esc, cnt, shape, bound, s, x, signs=None, hb=0, esc_records=None):
+    d = core.device
+    batch, rows, cols = shape
+    m = x.shape[1]
+    st = torch.zeros(1, dtype=torch.int32, device=d)
+    ws = torch.empty(e8q.e8q_gemv_workspace_size(batch, m, cols), dtype=torch.uint8, device=d)
+    y = torch.empty((batch, m, rows), dtype=torch.float32, device=d)
+    e8q.e8q_gemv_core_escape(core, esc, cnt, shape, bound, s, x, y, ws, st, signs=signs, had_block=hb,
+                             esc_records=esc_records)
+    torch.cuda.synchronize()
+    return {"status": int(st.item()) & 0xFFFFFFFF, "y": y.cpu().numpy().astype(np.float64)}
+
+
+def gemv_tolerance(two_z, s, x_vals, signs, hb, cols):
+    """The documented float32 bound 2 (L + G + 17) 2^-24 S_r of the GEMV."""
+    L = int(np.log2(hb)) if hb else 0
+    G = -(-cols // 512)
+    S = oracle.rotated_magnitude(two_z, s, x_vals, signs, hb)
+    return 2.0 * (L + G + 17) * 2.0 ** -24 * S

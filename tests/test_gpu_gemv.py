@@ -1,0 +1,117 @@
+"""GPU GEMV from the exported form against the float64 product of the exact
+restored weights, within the documented float32 bound (the evaluation order is
+the kernel's own, so the bar is a derived tolerance, not bit equality)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_e8_lattice_amd import workloads
+from gpu_util import device, gemv_tolerance, run_encode, run_gemv, upload_export, wbits
+
+pytestmark = pytest.mark.gpu
+
+
+def _x(shape, seed, d, dtype=torch.bfloat16):
+    g = torch.Generator(device=d).manual_seed(seed)
+    return torch.randn(shape, generator=g, device=d).to(dtype)
+
+
+def _xvals(x):
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def _check(out, two_z, s, x, sig, hb, cols):
+    xv = _xvals(x)
+    y, _ = oracle.gemv_reference(two_z, s, xv, sig, hb)
+    tol = gemv_tolerance(two_z, s, xv, sig, hb, cols)
+    err = np.abs(out["y"] - y)
+    assert (err <= tol).all(), f"max err/tol {np.max(err / np.maximum(tol, 1e-300)):.3g}"
+    return y
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+@pytest.mark.parametrize("hb", [0, 8, 128, 1024])
+@pytest.mark.parametrize("alpha", [1.0, 3.0])
+def test_gemv_oracle_export(m, hb, alpha):
+    d = device()
+    shape = (3, 70, 2048)
+    w = workloads.normal(shape, 1600 + hb, d)
+    s = workloads.rms_scale(w, alpha)
+    sg = workloads.signs(2048, 1601, d) if hb else None
+    sn = None if sg is None else sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, hb, 16)
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((3, m, 2048), 1602 + m, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, hb)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, hb, 2048)
+
+
+@pytest.mark.parametrize("bound", [0, 24, 40])
+def test_gemv_bounds_and_f32_activations(bound):
+    """Point table in LDS and in global memory; float32 activations."""
+    d = device()
+    shape = (2, 33, 4096)
+    w = workloads.normal(shape, 1700 + bound, d)
+    s = workloads.rms_scale(w, 2.0)
+    sg = workloads.signs(4096, 1701, d)
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), 4096, bound)
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((2, 1, 4096), 1702, d, torch.float32)
+    out = run_gemv(core, esc, cnt, shape, bound, s, x, sg, 4096)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sg.cpu().numpy(), 4096, 4096)
+
+
+def test_gemv_malformed_and_bad_scale():
+    d = device()
+    shape = (2, 16, 1024)
+    w = workloads.normal(shape, 1800, d)
+    s = workloads.rms_scale(w, 1.0)
+    sg = workloads.signs(1024, 1801, d)
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), 128, 16)
+    core_np = enc["core_idx"].copy()
+    k = int(np.nonzero(core_np != oracle.ESCAPE_SLOT)[0][0])
+    core_np[k] = oracle.core_size(16)
+    s_bad = s.clone()
+    s_bad[5] = 0.0
+    bad = {"core_idx": core_np, "records": enc["records"][:-3], "counts": enc["counts"]}
+    core, esc, cnt = upload_export(bad, d)
+    x = _x((2, 2, 1024), 1802, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s_bad, x, sg, 128)
+    assert out["status"] == (oracle.STATUS_BAD_INDEX | oracle.STATUS_ESC_MISSING | oracle.STATUS_BAD_SCALE)
+    dec = oracle.decode_core_escape(core_np, bad["records"], enc["counts"], 16)
+    sb = s_bad.cpu().numpy().copy()
+    xv = _xvals(x)
+    sref = np.where(sb > 0, sb, 0).astype(np.float32)
+    yref, _ = oracle.gemv_reference(dec.reshape(shape), sref, xv, sg.cpu().numpy(), 128)
+    tol = gemv_tolerance(dec.reshape(shape), sref, xv, sg.cpu().numpy(), 128, 1024)
+    assert (np.abs(out["y"] - yref) <= tol).all()
+    assert (out["y"][0, :, 5] == 0).all()
+
+
+def test_gemv_dense_decoder_shapes():
+    """All 224 dense-decoder matrices in the benchmark's three launches (one
+    activation vector per matrix); the first, middle and last matrix of each
+    launch checked in full against the float64 product of the projection of
+    the original weights."""
+    d = device()
+    for i, b in enumerate(workloads.dense_decoder(d)):
+        nb, rows, cols = b.w.shape
+        shape = (nb, rows, cols)
+        enc = run_encode(b.w, b.scale, 16, b.signs, 128, keep_device=True)
+        core, esc, cnt = enc["dev"]
+        x = _x((nb, 1, cols), 1900 + i, d)
+        out = run_gemv(core, esc, cnt, shape, 16, b.scale, x, b.signs, 128)
+        assert out["status"] == 0
+        sn = b.signs.cpu().numpy()
+        for mi in (0, nb // 2, nb - 1):
+            sm = b.scale[mi * rows:(mi + 1) * rows].cpu().numpy()
+            prj = oracle.project(wbits(b.w[mi]), sm, sn, 128)
+            tz = prj["two_z"].reshape(1, rows, cols)
+            o = {"y": out["y"][mi:mi + 1]}
+            _check(o, tz, sm, x[mi:mi + 1], sn, 128, cols)
+        del enc, core, esc, cnt
+        torch.cuda.empty_cache()

@@ -76,3 +76,32 @@ def test_decode_bad_scale_rows():
     assert out["status"] == oracle.STATUS_BAD_SCALE
     assert (out["q_f32"][0, 1:3] == 0).all() and not np.signbit(out["q_f32"][0, 1:3]).any()
     assert np.array_equal(np.signbit(out["w_hat_f32"][0, 1:3]), np.broadcast_to(sig < 0, (2, 128)))
+
+
+@pytest.mark.parametrize("hb", [0, 8, 128, 512])
+def test_gemv_reference_is_the_restored_product(hb):
+    """The float64 GEMV reference equals the oracle's float32 restored weights
+    times x up to the rounding of those weights, and its exact weights are the
+    restore's values before that rounding."""
+    rng = np.random.default_rng(40 + hb)
+    batch, rows, cols, m = 2, 12, 1024, 3
+    w, s = _weights(rng, batch, rows, cols, 1.5)
+    sig = np.where(rng.integers(0, 2, cols) == 1, 1, -1).astype(np.int8) if hb else None
+    prj = oracle.project_restore(w, s, sig, hb, w_is_bf16=False) if hb else oracle.project(w, s, w_is_bf16=False)
+    two_z = prj["two_z"].reshape(batch, rows, cols)
+    W = oracle.exact_restored(two_z, s, sig, hb)
+    w32 = prj["w_hat_f32"] if hb else prj["q_f32"]
+    assert np.all(np.abs(W - w32) <= 2.0 ** -21 * np.abs(W))
+    x = rng.normal(size=(batch, m, cols))
+    y, mag = oracle.gemv_reference(two_z, s, x, sig, hb)
+    want = np.einsum("brc,btc->btr", w32.astype(np.float64), x)
+    assert np.all(np.abs(y - want) <= 2.0 ** -20 * mag)
+    # the rotated-basis form s * sum z . x_tilde (x_tilde = H_b (sigma x) / sqrt(b))
+    # gives the same product
+    if hb:
+        H = oracle.sylvester_matrix(hb)
+        xt = ((x * sig).reshape(batch, m, cols // hb, hb) @ H.T).reshape(batch, m, cols) / np.sqrt(hb)
+        y2 = np.einsum("brc,btc->btr", two_z * 0.5 * s.reshape(batch, rows, 1).astype(np.float64), xt)
+        assert np.allclose(y2, y, rtol=0, atol=1e-12 * mag.max())
+        rmag = oracle.rotated_magnitude(two_z, s, x, sig, hb)
+        assert (rmag >= np.abs(y2) - 1e-12).all()
