@@ -227,6 +227,71 @@ def run_decode(args, torch, e8q, workloads, kind):
     return r
 
 
+def run_gemv(args, torch, e8q, workloads):
+    """Decode-step products of all 224 dense-decoder matrices with one bf16
+    activation vector each (m = --gemv-m), straight from the exported form
+    (encoded once, untimed); the same products in BF16 (torch.bmm of the
+    decoded bf16 weights, hipBLASLt) are timed alongside as the reference
+    representation."""
+    dev = torch.device("cuda:0")
+    batches = workloads.dense_decoder(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    m = args.gemv_m
+    enc = []
+    for i, b in enumerate(batches):
+        nb, rows, cols = b.w.shape
+        groups = nb * rows * cols // 8
+        core = torch.empty(groups, dtype=torch.int16, device=dev)
+        esc = torch.empty((groups // 16) * e8q.ESCAPE_RECORD_BYTES, dtype=torch.uint8, device=dev)
+        cnt = torch.empty(nb, dtype=torch.int64, device=dev)
+        ws = torch.empty(e8q.e8q_encode_workspace_size(nb, rows, cols), dtype=torch.uint8, device=dev)
+        e8q.e8q_encode_core_escape(b.w, b.scale, 16, core, esc, cnt, ws, status, signs=b.signs, had_block=128)
+        wh = torch.empty_like(b.w)
+        dws = torch.empty(e8q.e8q_decode_workspace_size(nb), dtype=torch.uint8, device=dev)
+        e8q.e8q_decode_core_escape(core, esc, cnt, (nb, rows, cols), 16, dws, status, row_scale=b.scale,
+                                   signs=b.signs, had_block=128, w_hat_out=wh)
+        g = torch.Generator(device=dev).manual_seed(6000 + i)
+        x = torch.randn((nb, m, cols), generator=g, device=dev).to(torch.bfloat16)
+        enc.append({"shape": (nb, rows, cols), "core": core, "esc": esc, "cnt": cnt, "scale": b.scale,
+                    "signs": b.signs, "x": x, "xt": x.transpose(1, 2).contiguous(), "w_hat": wh,
+                    "y": torch.empty((nb, m, rows), dtype=torch.float32, device=dev),
+                    "yb": torch.empty((nb, rows, m), dtype=torch.bfloat16, device=dev),
+                    "ws": torch.empty(e8q.e8q_gemv_workspace_size(nb, m, cols), dtype=torch.uint8, device=dev)})
+        b.w = None
+        del ws, dws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    def part(e):
+        def fn(k):
+            e8q.e8q_gemv_core_escape(e["core"], e["esc"], e["cnt"], e["shape"], 16, e["scale"], e["x"], e["y"],
+                                     e["ws"], status, signs=e["signs"], had_block=128)
+        return fn
+
+    def part_bf16(e):
+        def fn(k):
+            torch.bmm(e["w_hat"], e["xt"], out=e["yb"])
+        return fn
+
+    parts, parts_bf16 = [], []
+    for e in enc:
+        nb, rows, cols = e["shape"]
+        n = nb * rows * cols
+        parts.append((f"{nb}x{rows}x{cols}", part(e), (2 * (n // 8) + 4 * nb * rows + 2 * nb * m * cols) / n, n))
+        parts_bf16.append((f"bf16 {nb}x{rows}x{cols}", part_bf16(e), 2.0, n))
+    n = sum(p[3] for p in parts)
+    alg = sum(p[2] * p[3] for p in parts)
+    r = _time_launches(args, torch, parts, n, alg, status,
+                       f"2-bit GEMV, dense decoder 224 matrices (q,k,v,o 4096x4096; gate,up 11008x4096; "
+                       f"down 4096x11008) x {m} bf16 activation vector(s) each, from core ||2z||^2<=16 indices "
+                       "+ escape records, 128-wide rotation")
+    rb = _time_launches(args, torch, parts_bf16, n, 2 * n, status, "bf16 torch.bmm of the decoded weights")
+    r["parts"].update(rb["parts"])
+    r["parts"]["bf16_ms_per_step"] = round(rb["kernel_ms"], 4)
+    r["parts"]["speedup_vs_bf16"] = round(rb["kernel_ms"] / r["kernel_ms"], 3)
+    return r
+
+
 def run_linear(args, torch, e8q, workloads):
     """4096x4096 bf16 rotated projection (q in bf16), cycling over 8 copies of
     the matrix (537 MB) so that the 256 MB last-level cache cannot hold the input."""
@@ -361,7 +426,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder",
                     choices=["decoder", "linear", "moe", "qat", "qat_restore", "qat_rotated_grad",
-                             "decode", "decode_q"])
+                             "decode", "decode_q", "gemv"])
+    ap.add_argument("--gemv-m", type=int, default=1, choices=[1, 2])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -390,6 +456,8 @@ def main():
     if args.config != "decoder":
         if args.config.startswith("qat"):
             r = run_qat(args, torch, e8q, workloads, args.config)
+        elif args.config == "gemv":
+            r = run_gemv(args, torch, e8q, workloads)
         elif args.config.startswith("decode"):
             r = run_decode(args, torch, e8q, workloads, args.config)
         else:

@@ -436,15 +436,27 @@ struct GemvArgs {
     uint32_t* status;
 };
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvRows = 64;
+constexpr int kGemvThreads = 512;
+constexpr int kGemvRows = 128;
 
-// 2z bytes (+64 bias) of one word to four floats 2z_i
-__device__ __forceinline__ void unpack4(uint32_t t, float* f) {
-    const uint32_t x = t ^ 0x40404040u;
-    const uint32_t sb = x | ((x & 0x40404040u) << 1);     // signed 2z bytes
+constexpr int kGemvR = 4;   // rows a wave works on at once (x~ is read once for all of them)
+
+// Four signed 2z bytes of one word to floats.
+__device__ __forceinline__ void unpack4s(uint32_t sb, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = float(int32_t(sb << (24 - 8 * i)) >> 24);
+}
+
+// 2z of a slot that is not a core index (escape record, or malformed).
+__device__ __forceinline__ void special_point(const GemvArgs& a, uint32_t b, uint32_t gib, uint32_t idx, float* z,
+                                           uint32_t& flags) {
+    int tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (idx != 0xFFFFu)
+        flags |= E8Q_STATUS_BAD_INDEX;
+    else if (!find_record(a.esc, a.offsets, b, gib, tb))
+        flags |= E8Q_STATUS_ESC_MISSING;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = float(tb[i]);
 }
 
 template <int M, bool LDS_PTS>
@@ -460,73 +472,96 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
         const float4* src = reinterpret_cast<const float4*>(a.xt + uint64_t(b) * M * a.cols);
         float4* dst = reinterpret_cast<float4*>(s_xt);
         for (uint32_t i = tid; i < M * a.cols / 4u; i += kGemvThreads) dst[i] = src[i];
-        if constexpr (LDS_PTS)
-            for (uint32_t i = tid; i < 2u * a.npts; i += kGemvThreads) s_pts[i] = a.pts[i];
+        if constexpr (LDS_PTS) {
+            // table words as signed 2z bytes
+            for (uint32_t i = tid; i < 2u * a.npts; i += kGemvThreads) {
+                const uint32_t x = a.pts[i] ^ 0x40404040u;
+                s_pts[i] = x | ((x & 0x40404040u) << 1);
+            }
+        }
     }
     __syncthreads();
-    const uint32_t* pts = LDS_PTS ? s_pts : a.pts;
-    const uint32_t r0 = blockIdx.x * a.rows_per_block;
-    const uint32_t r1 = min(r0 + a.rows_per_block, a.rows);
+    const uint32_t nlast = a.npts - 1u;
+    const uint32_t r_begin = blockIdx.x * a.rows_per_block;
+    const uint32_t r_end = min(r_begin + a.rows_per_block, a.rows);
     uint32_t flags = 0;
-    for (uint32_t r = r0 + wv; r < r1; r += kGemvThreads / kWave) {
-        const uint64_t rowg = (uint64_t(b) * a.rows + r) * a.gpr;
-        float acc[M];
+    for (uint32_t rw = r_begin + wv * kGemvR; rw < r_end; rw += (kGemvThreads / kWave) * kGemvR) {
+        const uint32_t nr = min(uint32_t(kGemvR), r_end - rw);        // wave-uniform
+        float acc[kGemvR][M];
 #pragma unroll
-        for (int t = 0; t < M; ++t) acc[t] = 0.0f;
-        // indices in chunks of 8 per lane, all loads of a chunk issued first
-        for (uint32_t g0 = lane; g0 < a.gpr; g0 += 8u * kWave) {
-          uint32_t ids[8];
+        for (int r = 0; r < kGemvR; ++r)
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-              const uint32_t g = g0 + uint32_t(c) * kWave;
-              ids[c] = g < a.gpr ? uint32_t(a.core_idx[rowg + g]) : 0u;
-          }
+            for (int t = 0; t < M; ++t) acc[r][t] = 0.0f;
+        // rows past the end repeat the last row (computed, never written)
+        const uint16_t* rowp[kGemvR];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const uint32_t g = g0 + uint32_t(c) * kWave;
-            if (g >= a.gpr) break;
-            const uint32_t idx = ids[c];
-            float z[8];
-            if (idx < a.npts) {
-                unpack4(pts[2u * idx], z);
-                unpack4(pts[2u * idx + 1u], z + 4);
-            } else {
-                int tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (idx != 0xFFFFu) {
-                    flags |= E8Q_STATUS_BAD_INDEX;
-                } else if (!find_record(a.esc, a.offsets, b, r * a.gpr + g, tb)) {
-                    flags |= E8Q_STATUS_ESC_MISSING;
-                }
+        for (int r = 0; r < kGemvR; ++r)
+            rowp[r] = a.core_idx + (uint64_t(b) * a.rows + rw + min(uint32_t(r), nr - 1u)) * a.gpr;
+        uint32_t nxt[kGemvR];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) z[i] = float(tb[i]);
+        for (int r = 0; r < kGemvR; ++r) nxt[r] = lane < a.gpr ? uint32_t(rowp[r][lane]) : 0u;
+        for (uint32_t g = lane; g < a.gpr; g += kWave) {
+            uint32_t idx[kGemvR];
+#pragma unroll
+            for (int r = 0; r < kGemvR; ++r) {
+                idx[r] = nxt[r];
+                const uint32_t gn = g + kWave;
+                nxt[r] = gn < a.gpr ? uint32_t(rowp[r][gn]) : 0u;
             }
+            float xv[M][8];
 #pragma unroll
             for (int t = 0; t < M; ++t) {
                 const float4* xp = reinterpret_cast<const float4*>(s_xt + t * a.cols + g * 8u);
                 const float4 x0 = xp[0], x1 = xp[1];
-                float s0 = z[0] * x0.x;
-                s0 = fmaf(z[1], x0.y, s0);
-                s0 = fmaf(z[2], x0.z, s0);
-                s0 = fmaf(z[3], x0.w, s0);
-                s0 = fmaf(z[4], x1.x, s0);
-                s0 = fmaf(z[5], x1.y, s0);
-                s0 = fmaf(z[6], x1.z, s0);
-                s0 = fmaf(z[7], x1.w, s0);
-                acc[t] += s0;
+                xv[t][0] = x0.x; xv[t][1] = x0.y; xv[t][2] = x0.z; xv[t][3] = x0.w;
+                xv[t][4] = x1.x; xv[t][5] = x1.y; xv[t][6] = x1.z; xv[t][7] = x1.w;
             }
-          }
+#pragma unroll
+            for (int r = 0; r < kGemvR; ++r) {
+                const uint32_t ii = min(idx[r], nlast);
+                float z[8];
+                if constexpr (LDS_PTS) {
+                    unpack4s(s_pts[2u * ii], z);
+                    unpack4s(s_pts[2u * ii + 1u], z + 4);
+                } else {
+                    const uint32_t x0 = a.pts[2u * ii] ^ 0x40404040u, x1 = a.pts[2u * ii + 1u] ^ 0x40404040u;
+                    unpack4s(x0 | ((x0 & 0x40404040u) << 1), z);
+                    unpack4s(x1 | ((x1 & 0x40404040u) << 1), z + 4);
+                }
+                const bool special = idx[r] > nlast;
+                if (__ballot(special)) {
+                    if (special && uint32_t(r) < nr)
+                        special_point(a, b, (rw + uint32_t(r)) * a.gpr + g, idx[r], z, flags);
+                }
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    float s0 = z[0] * xv[t][0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) s0 = fmaf(z[i], xv[t][i], s0);
+                    acc[r][t] += s0;
+                }
+            }
         }
 #pragma unroll
-        for (int t = 0; t < M; ++t) {
+        for (int r = 0; r < kGemvR; ++r)
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off, 64);
-        }
-        if (lane == 0) {
+            for (int t = 0; t < M; ++t)
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) acc[r][t] += __shfl_xor(acc[r][t], off, 64);
+        if (lane < nr) {
+            float sel[M];
+#pragma unroll
+            for (int t = 0; t < M; ++t) {
+                sel[t] = acc[0][t];
+#pragma unroll
+                for (int r = 1; r < kGemvR; ++r) sel[t] = lane == uint32_t(r) ? acc[r][t] : sel[t];
+            }
+            const uint32_t r = rw + lane;
             const float s = a.scale[uint64_t(b) * a.rows + r];
             const bool bad = !(s > 0.0f) || __builtin_isinf(s);
             if (bad) flags |= E8Q_STATUS_BAD_SCALE;
 #pragma unroll
-            for (int t = 0; t < M; ++t) a.y[(uint64_t(b) * M + t) * a.rows + r] = bad ? 0.0f : (0.5f * s) * acc[t];
+            for (int t = 0; t < M; ++t) a.y[(uint64_t(b) * M + t) * a.rows + r] = bad ? 0.0f : (0.5f * s) * sel[t];
         }
     }
     flush_status(flags, a.status);
