@@ -71,4 +71,11 @@ from .restore import (  # noqa: F401
 )
 from .decode import decode_outputs  # noqa: F401
 from .gemv import exact_restored, gemv_reference, rotated_magnitude  # noqa: F401
+from .roots import (  # noqa: F401
+    e8_roots,
+    pack_escapes,
+    unpack_escapes,
+    PACKED_RECORD_DTYPE,
+    ROOT_NONE,
+)
 from .brute import brute_nearest_e8  # noqa: F401
