@@ -17,13 +17,15 @@ __all__ = [
     "e8q_project", "e8q_project_hadamard", "e8q_project_hadamard_restore",
     "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_ste_backward",
     "e8q_ste_backward_hadamard", "e8q_decode_core_escape", "e8q_decode_workspace_size",
-    "e8q_gemv_core_escape", "e8q_gemv_workspace_size", "e8q_core_size",
+    "e8q_gemv_core_escape", "e8q_gemv_workspace_size", "e8q_pack_escapes", "e8q_unpack_escapes",
+    "e8q_pack_workspace_size", "PACKED_RECORD_BYTES", "e8q_core_size",
     "e8q_status_string", "e8q_version",
     "ESCAPE_RECORD_BYTES", "STATUS_BITS", "F32", "BF16",
 ]
 
 F32, BF16 = 0, 1
 ESCAPE_RECORD_BYTES = 20
+PACKED_RECORD_BYTES = 8
 STATUS_BITS = {
     "NONFINITE": 1, "BAD_SCALE": 2, "INT8_RANGE": 4, "ESC_OVERFLOW": 8,
     "X_RANGE": 16, "LOOKBACK_TIMEOUT": 32, "BAD_INDEX": 64, "ESC_MISSING": 128,
@@ -69,6 +71,12 @@ def lib():
     L.e8q_gemv_core_escape.restype = e
     L.e8q_gemv_workspace_size.argtypes = [i64, i64, i64]
     L.e8q_gemv_workspace_size.restype = sz
+    L.e8q_pack_escapes.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, sz, vp, vp]
+    L.e8q_pack_escapes.restype = e
+    L.e8q_unpack_escapes.argtypes = [vp, i64, vp, i64, i32, vp, vp, sz, vp, vp]
+    L.e8q_unpack_escapes.restype = e
+    L.e8q_pack_workspace_size.argtypes = [i64]
+    L.e8q_pack_workspace_size.restype = sz
     L.e8q_encode_core_escape.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
                                          vp, sz, vp, vp]
     L.e8q_encode_core_escape.restype = e
@@ -274,6 +282,35 @@ def e8q_gemv_core_escape(core_idx, esc, esc_count, shape, core_bound, row_scale,
         int(had_block), _ptr(x), _dtype_code(x), x.shape[1], _ptr(y_out), _ptr(workspace), workspace.numel(),
         _ptr(status), _stream(core_idx, stream))
     _check("e8q_gemv_core_escape", code)
+
+
+def e8q_pack_workspace_size(n):
+    return int(lib().e8q_pack_workspace_size(n))
+
+
+def e8q_pack_escapes(esc, n, core_bound, packed_out, wide_out, wide_count_out, workspace, status, stream=None):
+    """``e8q_pack_escapes``: ``n`` 20-byte records in ``esc`` (uint8 tensor) to
+    8-byte packed records in ``packed_out`` (uint8) plus the wide list."""
+    for t, nm in ((esc, "esc"), (packed_out, "packed_out"), (wide_out, "wide_out"), (workspace, "workspace")):
+        _dev(t, nm, (torch.uint8,))
+    _dev(wide_count_out, "wide_count_out", (torch.int64,)); _dev(status, "status", (torch.int32,))
+    cap = 0 if wide_out is None else wide_out.numel() // ESCAPE_RECORD_BYTES
+    code = lib().e8q_pack_escapes(_ptr(esc), int(n), int(core_bound), _ptr(packed_out), _ptr(wide_out), cap,
+                                  _ptr(wide_count_out), _ptr(workspace), workspace.numel(), _ptr(status),
+                                  _stream(workspace, stream))
+    _check("e8q_pack_escapes", code)
+
+
+def e8q_unpack_escapes(packed, n, wide, wide_count, core_bound, esc_out, workspace, status, stream=None):
+    """``e8q_unpack_escapes``: packed records (+ ``wide_count`` wide records) back to
+    20-byte records in ``esc_out`` (uint8)."""
+    for t, nm in ((packed, "packed"), (wide, "wide"), (esc_out, "esc_out"), (workspace, "workspace")):
+        _dev(t, nm, (torch.uint8,))
+    _dev(status, "status", (torch.int32,))
+    code = lib().e8q_unpack_escapes(_ptr(packed), int(n), _ptr(wide), int(wide_count), int(core_bound),
+                                    _ptr(esc_out), _ptr(workspace), workspace.numel(), _ptr(status),
+                                    _stream(workspace, stream))
+    _check("e8q_unpack_escapes", code)
 
 
 def e8q_core_size(core_bound):

@@ -44,8 +44,15 @@ const DevTable* get_table(int32_t bound, e8q_status_t& err) {
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }
-    if (!upload(t.host.points, t.dpoints)) {
+    const std::vector<uint32_t> roots = build_roots();
+    if (roots.size() != 480 || !upload(t.host.points, t.dpoints)) {
         (void)hipFree(t.dptr);
+        err = E8Q_ERR_DEVICE;
+        return nullptr;
+    }
+    if (!upload(roots, t.droots)) {
+        (void)hipFree(t.dptr);
+        (void)hipFree(t.dpoints);
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }

@@ -121,4 +121,21 @@ bool build_core_table(int32_t bound, CoreTable& out) {
     return true;
 }
 
+std::vector<uint32_t> build_roots() {
+    // every E8 point with ||2z||^2 = 8, enumerated in lexicographic order
+    std::vector<Pt> pts;
+    enumerate(8, 2, pts);
+    std::vector<uint32_t> out;
+    for (const Pt& t : pts) {
+        int n = 0;
+        for (int k = 0; k < 8; ++k) n += t[k] * t[k];
+        if (n != 8) continue;
+        uint32_t w[2] = {0u, 0u};
+        for (int k = 0; k < 8; ++k) w[k / 4] |= uint32_t(t[k] + 64) << (8 * (k % 4));
+        out.push_back(w[0]);
+        out.push_back(w[1]);
+    }
+    return out;   // 480 words when correct
+}
+
 }  // namespace e8q

@@ -48,4 +48,9 @@ struct CoreTable {
 // self-check fails.
 bool build_core_table(int32_t bound, CoreTable& out);
 
+// The 240 roots of E8 (||r||^2 = 2) as 2r, in lexicographic order (signed,
+// coordinate 0 most significant), two words each with bytes 2r_i + 64 as in
+// CoreTable::points.
+std::vector<uint32_t> build_roots();
+
 }  // namespace e8q

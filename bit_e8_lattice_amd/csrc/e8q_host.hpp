@@ -16,6 +16,7 @@ namespace e8q {
 struct DevTable {
     uint16_t* dptr = nullptr;
     uint32_t* dpoints = nullptr;
+    uint32_t* droots = nullptr;   // the 240 roots (same word layout as the points)
     CoreTable host;
 };
 

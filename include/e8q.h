@@ -97,6 +97,19 @@ typedef struct {
     int16_t two_z[8];
 } e8q_escape_t;
 
+/* A root-packed escape record, 8 bytes: the escaped point is the core point
+ * core_idx plus the root number `root` (E8-QAT Table 3: every escaped group of
+ * the artifact is a core point plus one root of E8).  Roots are numbered 0..239
+ * in lexicographic order of 2r (signed, coordinate 0 first); the root used is
+ * the first that brings the point into the core (a reading).  root == 0xFF
+ * (core_idx == 0xFFFF): no root does; the full record is in the wide list. */
+typedef struct {
+    uint32_t group;
+    uint16_t core_idx;
+    uint8_t root;
+    uint8_t pad;         /* 0 */
+} e8q_escape_packed_t;
+
 /* ---------------------------------------------------------------------------
  * e8q_project -- forward projection without rotation: q = s * nearest_E8(w/s).
  * E8-QAT abstract and Figure 1(c)/2(b) captions: every forward pass maps each
@@ -316,6 +329,42 @@ e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx,
 
 /* Workspace bytes e8q_gemv_core_escape needs (0 on bad sizes). */
 size_t e8q_gemv_workspace_size(int64_t batch, int64_t m, int64_t cols);
+
+/* ---------------------------------------------------------------------------
+ * e8q_pack_escapes -- escape records to root-packed records (E8-QAT Table 3).
+ *   esc, n       the 20-byte records (4-byte aligned)
+ *   core_bound   the encoder's B
+ *   packed_out   [n] packed records, same order (8-byte aligned)
+ *   wide_out, wide_capacity   the full records of points no root brings into
+ *                the core, in record order; past the capacity they are
+ *                dropped and E8Q_STATUS_ESC_OVERFLOW is set
+ *   wide_count_out  device int64: how many records needed the wide list
+ *   workspace    e8q_pack_workspace_size(n) bytes, 8-byte aligned
+ * Payload with packed records: 2 + 8 rho bits per weight (wide records add
+ * 20 bytes each).
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_pack_escapes(const e8q_escape_t* esc, int64_t n, int32_t core_bound,
+                              e8q_escape_packed_t* packed_out,
+                              e8q_escape_t* wide_out, int64_t wide_capacity,
+                              int64_t* wide_count_out,
+                              void* workspace, size_t workspace_bytes,
+                              uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * e8q_unpack_escapes -- the inverse: packed records (and the wide list of
+ * wide_count records) back to 20-byte records esc_out[n] in order.  A packed
+ * record with root >= 240 (other than 0xFF) or core_idx >= |C(B)| decodes to
+ * 2z = 0 (E8Q_STATUS_BAD_INDEX); one that refers past the wide list decodes to
+ * 2z = 0 (E8Q_STATUS_ESC_MISSING).  Workspace as e8q_pack_escapes.
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_unpack_escapes(const e8q_escape_packed_t* packed, int64_t n,
+                                const e8q_escape_t* wide, int64_t wide_count,
+                                int32_t core_bound, e8q_escape_t* esc_out,
+                                void* workspace, size_t workspace_bytes,
+                                uint32_t* status_dev, void* stream);
+
+/* Workspace bytes e8q_pack_escapes / e8q_unpack_escapes need for n records. */
+size_t e8q_pack_workspace_size(int64_t n);
 
 /* |C(core_bound)|, the number of core points; -1 if core_bound is outside [0, 40].
  * Host-only. */

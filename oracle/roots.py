@@ -56,16 +56,19 @@ def pack_escapes(records, core_bound):
     packed["core_idx"] = 0xFFFF
     if n == 0:
         return packed, np.zeros(0, dtype=ESCAPE_RECORD_DTYPE)
-    tz = records["two_z"].astype(np.int64)                          # [n, 8]
-    diff = tz[:, None, :] - roots[None, :, :]                      # [n, 240, 8]
-    ok = (diff * diff).sum(-1) <= core_bound
-    has = ok.any(1)
-    first = np.argmax(ok, axis=1)
-    if has.any():
-        rows = np.nonzero(has)[0]
-        c = diff[rows, first[rows]]
-        packed["root"][rows] = first[rows].astype(np.uint8)
-        packed["core_idx"][rows] = core_rank(c, core_bound).astype(np.uint16)
+    has = np.zeros(n, dtype=bool)
+    for lo in range(0, n, 16384):                                  # bounded memory
+        tz = records["two_z"][lo:lo + 16384].astype(np.int64)       # [k, 8]
+        diff = tz[:, None, :] - roots[None, :, :]                  # [k, 240, 8]
+        ok = (diff * diff).sum(-1) <= core_bound
+        h = ok.any(1)
+        first = np.argmax(ok, axis=1)
+        if h.any():
+            rows = np.nonzero(h)[0]
+            c = diff[rows, first[rows]]
+            packed["root"][lo + rows] = first[rows].astype(np.uint8)
+            packed["core_idx"][lo + rows] = core_rank(c, core_bound).astype(np.uint16)
+        has[lo:lo + len(tz)] = h
     wide = records[~has].copy()
     return packed, wide
 
