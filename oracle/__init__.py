@@ -78,4 +78,5 @@ from .roots import (  # noqa: F401
     PACKED_RECORD_DTYPE,
     ROOT_NONE,
 )
+from .ptq import core_search_two_z, core_project_two_z, row_error, ptq_init  # noqa: F401
 from .brute import brute_nearest_e8  # noqa: F401
