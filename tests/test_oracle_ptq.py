@@ -109,7 +109,7 @@ def test_nan_error_counts_as_infinite():
     rng = np.random.default_rng(5)
     w = (rng.normal(size=(1, 2, 64)) * 0.02).astype(np.float32)
     s0 = oracle.rms_scale(w[0], 1.0)
-    w[0, 1, 3] = np.inf
+    w[0, 1, 3] = np.nan
     out = oracle.ptq_init(w, s0, np.array([0.0, 1.0], np.float32), None, 0, 16, w_is_bf16=False)
     assert np.isinf(out["err"][1, 0]) and np.isnan(out["err"][1, 1])
     assert out["k"][1] == 0 and out["k"][0] == 1
