@@ -18,7 +18,8 @@ __all__ = [
     "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_ste_backward",
     "e8q_ste_backward_hadamard", "e8q_decode_core_escape", "e8q_decode_workspace_size",
     "e8q_gemv_core_escape", "e8q_gemv_workspace_size", "e8q_pack_escapes", "e8q_unpack_escapes",
-    "e8q_pack_workspace_size", "PACKED_RECORD_BYTES", "e8q_core_size",
+    "e8q_pack_workspace_size", "PACKED_RECORD_BYTES", "e8q_ptq_init", "e8q_ptq_workspace_size",
+    "e8q_core_size",
     "e8q_status_string", "e8q_version",
     "ESCAPE_RECORD_BYTES", "STATUS_BITS", "F32", "BF16",
 ]
@@ -77,6 +78,10 @@ def lib():
     L.e8q_unpack_escapes.restype = e
     L.e8q_pack_workspace_size.argtypes = [i64]
     L.e8q_pack_workspace_size.restype = sz
+    L.e8q_ptq_init.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.e8q_ptq_init.restype = e
+    L.e8q_ptq_workspace_size.argtypes = [i64, i64, i64]
+    L.e8q_ptq_workspace_size.restype = sz
     L.e8q_encode_core_escape.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
                                          vp, sz, vp, vp]
     L.e8q_encode_core_escape.restype = e
@@ -311,6 +316,27 @@ def e8q_unpack_escapes(packed, n, wide, wide_count, core_bound, esc_out, workspa
                                     _ptr(esc_out), _ptr(workspace), workspace.numel(), _ptr(status),
                                     _stream(workspace, stream))
     _check("e8q_unpack_escapes", code)
+
+
+def e8q_ptq_workspace_size(batch, rows, cols):
+    return int(lib().e8q_ptq_workspace_size(batch, rows, cols))
+
+
+def e8q_ptq_init(w, base_scale, alphas, core_bound, scale_out, core_idx_out, two_z_out, workspace, status,
+                 signs=None, had_block=0, choice_out=None, err_out=None, stream=None):
+    """``e8q_ptq_init``: per-row scale search over ``alphas * base_scale`` and the
+    finite-core projection at the chosen scale."""
+    _dev(w, "w", _WDT); _dev(base_scale, "base_scale", (torch.float32,)); _dev(alphas, "alphas", (torch.float32,))
+    _dev(scale_out, "scale_out", (torch.float32,)); _dev(core_idx_out, "core_idx_out", (torch.int16,))
+    _dev(two_z_out, "two_z_out", (torch.int8,)); _dev(workspace, "workspace", (torch.uint8,))
+    _dev(status, "status", (torch.int32,)); _dev(signs, "signs", (torch.int8,))
+    _dev(choice_out, "choice_out", (torch.int32,)); _dev(err_out, "err_out", (torch.float64,))
+    b, r, c = _shape3(w)
+    code = lib().e8q_ptq_init(_ptr(w), _dtype_code(w), b, r, c, _ptr(base_scale), _ptr(alphas), alphas.numel(),
+                              _ptr(signs), int(had_block), int(core_bound), _ptr(scale_out), _ptr(choice_out),
+                              _ptr(err_out), _ptr(core_idx_out), _ptr(two_z_out), _ptr(workspace),
+                              workspace.numel(), _ptr(status), _stream(w, stream))
+    _check("e8q_ptq_init", code)
 
 
 def e8q_core_size(core_bound):

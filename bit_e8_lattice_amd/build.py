@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libe8q.so")
 
 SOURCES = ["e8q_common.hip", "e8q_project.hip", "e8q_encode.hip", "e8q_ste.hip", "e8q_decode.hip",
-           "e8q_roots.hip", "e8q_core_table.cpp"]
+           "e8q_roots.hip", "e8q_ptq.hip", "e8q_core_table.cpp"]
 
 # -ffp-contract=off: every float32 step is one IEEE operation (no fused
 # multiply-add), which the bit-exact contract in include/e8q.h relies on.

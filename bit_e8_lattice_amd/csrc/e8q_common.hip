@@ -50,9 +50,20 @@ const DevTable* get_table(int32_t bound, e8q_status_t& err) {
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }
-    if (!upload(roots, t.droots)) {
+    std::vector<double> p64(size_t(t.host.size) * 9, 0.0);
+    for (int64_t i = 0; i < t.host.size; ++i) {
+        double n = 0.0;
+        for (int k = 0; k < 8; ++k) {
+            const int v = int((t.host.points[2 * i + k / 4] >> (8 * (k % 4))) & 0xFFu) - 64;
+            p64[size_t(i) * 9 + k] = double(v);
+            n += double(v * v);
+        }
+        p64[size_t(i) * 9 + 8] = n / 4.0;
+    }
+    if (!upload(roots, t.droots) || !upload(p64, t.dpts64)) {
         (void)hipFree(t.dptr);
         (void)hipFree(t.dpoints);
+        if (t.droots) (void)hipFree(t.droots);
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }

@@ -17,6 +17,7 @@ struct DevTable {
     uint16_t* dptr = nullptr;
     uint32_t* dpoints = nullptr;
     uint32_t* droots = nullptr;   // the 240 roots (same word layout as the points)
+    double* dpts64 = nullptr;     // points in rank order as 9 doubles: t_0..t_7 (= 2z), ||t||^2 / 4
     CoreTable host;
 };
 

@@ -366,6 +366,43 @@ e8q_status_t e8q_unpack_escapes(const e8q_escape_packed_t* packed, int64_t n,
 /* Workspace bytes e8q_pack_escapes / e8q_unpack_escapes need for n records. */
 size_t e8q_pack_workspace_size(int64_t n);
 
+/* ---------------------------------------------------------------------------
+ * e8q_ptq_init -- PTQ initialization onto the fixed core (E8-QAT Figure 2(a)
+ * caption: PTQ initializes the latent weights from a fixed E8 core; Table 9:
+ * QAT then starts with no escapes).  Per row: a scale search over
+ * s_k = fl32(alphas[k] * base_scale[r]) by the row's squared error, then the
+ * finite-core projection at the chosen scale (the nearest E8 point when it is
+ * in C(B), else the nearest point of C(B) by exhaustive search).  Comparisons
+ * are exact-order float64 evaluations (see the source header); ties go to
+ * the lower core index and to the smaller k; NaN errors count as +inf.
+ *   w, w_dtype, batch, rows, cols   as e8q_project
+ *   base_scale   [batch*rows] float32 s0 (e.g. the row RMS)
+ *   alphas       device float32 [n_alpha] candidate multipliers
+ *   signs, had_block   rotation (signs NULL: none)
+ *   core_bound   B in [0, 40]
+ *   scale_out    [batch*rows] float32 chosen scales (required)
+ *   choice_out   [batch*rows] int32 chosen k, or NULL
+ *   err_out      [batch*rows, n_alpha] float64 row errors (+inf for an invalid
+ *                scale), or NULL
+ *   core_idx_out [batch*rows*cols/8] uint16 (required): the exported form with
+ *                no escapes; decode it with e8q_decode_core_escape and zero counts
+ *   two_z_out    [batch, rows, cols] int8 2z (required)
+ *   workspace    e8q_ptq_workspace_size(batch, rows, cols) bytes, 256-aligned
+ * Limits: cols <= 26208 (LDS per row); rotation blocks as e8q_project_hadamard.
+ * Status bits as the projection at the chosen scale.
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype,
+                          int64_t batch, int64_t rows, int64_t cols,
+                          const float* base_scale, const float* alphas, int32_t n_alpha,
+                          const int8_t* signs, int32_t had_block, int32_t core_bound,
+                          float* scale_out, int32_t* choice_out, double* err_out,
+                          uint16_t* core_idx_out, int8_t* two_z_out,
+                          void* workspace, size_t workspace_bytes,
+                          uint32_t* status_dev, void* stream);
+
+/* Workspace bytes e8q_ptq_init needs (0 on bad sizes). */
+size_t e8q_ptq_workspace_size(int64_t batch, int64_t rows, int64_t cols);
+
 /* |C(core_bound)|, the number of core points; -1 if core_bound is outside [0, 40].
  * Host-only. */
 int64_t e8q_core_size(int32_t core_bound);

@@ -175,3 +175,22 @@ def gemv_tolerance(two_z, s, x_vals, signs, hb, cols):
     G = -(-cols // 512)
     S = oracle.rotated_magnitude(two_z, s, x_vals, signs, hb)
     return 2.0 * (L + G + 17) * 2.0 ** -24 * S
+
+
+def run_ptq(w, s0, alphas, bound, signs=None, hb=0):
+    d = w.device
+    batch, rows, cols = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    groups = batch * rows * cols // 8
+    st = torch.zeros(1, dtype=torch.int32, device=d)
+    al = torch.as_tensor(np.asarray(alphas, np.float32)).to(d)
+    scale = torch.empty(batch * rows, dtype=torch.float32, device=d)
+    choice = torch.empty(batch * rows, dtype=torch.int32, device=d)
+    err = torch.empty((batch * rows, len(alphas)), dtype=torch.float64, device=d)
+    core = torch.empty(groups, dtype=torch.int16, device=d)
+    tz = torch.empty(w.shape, dtype=torch.int8, device=d)
+    ws = torch.empty(e8q.e8q_ptq_workspace_size(batch, rows, cols), dtype=torch.uint8, device=d)
+    e8q.e8q_ptq_init(w, s0, al, bound, scale, core, tz, ws, st, signs=signs, had_block=hb, choice_out=choice,
+                     err_out=err)
+    torch.cuda.synchronize()
+    return {"status": int(st.item()) & 0xFFFFFFFF, "scale": scale.cpu().numpy(), "k": choice.cpu().numpy(),
+            "err": err.cpu().numpy(), "core_idx": u16(core), "two_z_i8": tz.cpu().numpy(), "dev": (core, scale)}

@@ -1,0 +1,83 @@
+"""GPU parity of e8q_ptq_init against the oracle: chosen scales and
+candidates, every row error (float64, bit for bit: the evaluation order is
+fixed), the finite-core points, core indices and status."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_e8_lattice_amd import workloads
+from gpu_util import device, first_mismatch, run_decode, run_ptq, wbits
+
+pytestmark = pytest.mark.gpu
+
+ALPHAS = [0.75, 1.0, 1.5, 2.0, 2.5, 3.0]
+
+
+def _cmp(out, ref):
+    assert first_mismatch(out["scale"].view(np.uint32), ref["scale"].view(np.uint32)) is None
+    assert np.array_equal(out["k"], ref["k"])
+    m = first_mismatch(out["err"].view(np.uint64), ref["err"].view(np.uint64))
+    assert m is None, f"err: {m}"
+    assert first_mismatch(out["two_z_i8"].reshape(-1, 8), ref["two_z"]) is None
+    assert first_mismatch(out["core_idx"], ref["core_idx"]) is None
+    assert out["status"] == ref["status"], (out["status"], ref["status"])
+
+
+@pytest.mark.parametrize("hb", [0, 128, 1024])
+@pytest.mark.parametrize("bound", [8, 16, 24])
+def test_ptq_init(hb, bound):
+    d = device()
+    w = workloads.student_t4((2, 23, 1024), 2100 + hb + bound, d)
+    s0 = workloads.rms_scale(w, 1.0)
+    sg = workloads.signs(1024, 2101, d) if hb else None
+    out = run_ptq(w, s0, ALPHAS, bound, sg, hb)
+    ref = oracle.ptq_init(wbits(w), s0.cpu().numpy(), ALPHAS, None if sg is None else sg.cpu().numpy(), hb, bound)
+    _cmp(out, ref)
+
+
+def test_ptq_invalid_rows_and_f32():
+    d = device()
+    w = workloads.normal((1, 9, 256), 2200, d, dtype=torch.float32)
+    s0 = workloads.rms_scale(w, 1.0)
+    w[0, 2, 17] = float("nan")
+    w[0, 4, :8] = 1e6
+    s0[6] = -1.0
+    al = [0.0, 1.0, 2.0]
+    out = run_ptq(w, s0, al, 16)
+    ref = oracle.ptq_init(wbits(w), s0.cpu().numpy(), al, None, 0, 16, w_is_bf16=False)
+    _cmp(out, ref)
+
+
+def test_ptq_decoder_block_sampled_rows_and_decode():
+    """One dense-decoder block (q, k, v, o, gate, up, down) in three launches;
+    sampled rows exact against the oracle; the result decodes (zero escapes)
+    to weights whose error is the reported row error."""
+    d = device()
+    rng = np.random.default_rng(7)
+    for b in workloads.dense_decoder(d, blocks=1, alpha=1.0):
+        nb, rows, cols = b.w.shape
+        out = run_ptq(b.w, b.scale, ALPHAS, 16, b.signs, 128)
+        assert out["status"] == 0
+        for m in (0, nb - 1):
+            rsel = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 2)]))
+            s0 = b.scale[m * rows:(m + 1) * rows].cpu().numpy()[rsel]
+            ref = oracle.ptq_init(wbits(b.w[m])[rsel], s0, ALPHAS, b.signs.cpu().numpy(), 128, 16)
+            r0 = m * rows + rsel
+            sub = {"scale": out["scale"][r0], "k": out["k"][r0], "err": out["err"][r0],
+                   "two_z_i8": out["two_z_i8"].reshape(nb, rows, cols)[m][rsel],
+                   "core_idx": out["core_idx"].reshape(nb, rows, cols // 8)[m][rsel].reshape(-1),
+                   "status": out["status"]}
+            _cmp(sub, ref)
+        core, scale = out["dev"]
+        cnt = torch.zeros(nb, dtype=torch.int64, device=d)
+        dec = run_decode(core, None, cnt, (nb, rows, cols), 16, scale, b.signs, 128, two_z=True,
+                         w_hat_dtype=torch.float32)
+        assert dec["status"] == 0
+        assert np.array_equal(dec["two_z_i8"], out["two_z_i8"])
+        # the decoded weights' squared error is the chosen row error (float32 rounding aside)
+        wf = b.w.float().cpu().numpy().reshape(nb * rows, cols).astype(np.float64)
+        e = ((wf - dec["w_hat"].reshape(nb * rows, cols).astype(np.float64)) ** 2).sum(1)
+        chosen = out["err"][np.arange(nb * rows), out["k"]]
+        assert np.allclose(e, chosen, rtol=1e-4, atol=0)
