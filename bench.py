@@ -347,6 +347,48 @@ def run_pack(args, torch, e8q, workloads):
     return r
 
 
+PTQ_ALPHAS = [0.75, 1.0, 1.5, 2.0, 2.5, 3.0]
+
+
+def run_ptq(args, torch, e8q, workloads):
+    """PTQ initialization of one dense-decoder block (q, k, v, o 4096x4096;
+    gate, up 11008x4096; down 4096x11008; 202 M weights) onto C(16): scale
+    search over 6 multipliers of the row RMS, then the finite-core projection;
+    three launches per step."""
+    dev = torch.device("cuda:0")
+    batches = workloads.dense_decoder(dev, blocks=1, alpha=1.0)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    al = torch.tensor(PTQ_ALPHAS, dtype=torch.float32, device=dev)
+    sets = []
+    for b in batches:
+        nb, rows, cols = b.w.shape
+        sets.append({"b": b, "scale": torch.empty(nb * rows, dtype=torch.float32, device=dev),
+                     "choice": torch.empty(nb * rows, dtype=torch.int32, device=dev),
+                     "core": torch.empty(nb * rows * cols // 8, dtype=torch.int16, device=dev),
+                     "tz": torch.empty((nb, rows, cols), dtype=torch.int8, device=dev),
+                     "ws": torch.empty(e8q.e8q_ptq_workspace_size(nb, rows, cols), dtype=torch.uint8, device=dev)})
+
+    def part(e):
+        b = e["b"]
+        return lambda k: e8q.e8q_ptq_init(b.w, b.scale, al, 16, e["scale"], e["core"], e["tz"], e["ws"], status,
+                                          signs=b.signs, had_block=128, choice_out=e["choice"])
+
+    parts = []
+    for e in sets:
+        nb, rows, cols = e["b"].w.shape
+        n = nb * rows * cols
+        # weights in, transform written and read back per candidate, points out
+        parts.append((f"{nb}x{rows}x{cols}", part(e), 2 + 4 + 4 * (len(PTQ_ALPHAS) + 1) + 1.25, n))
+    n = sum(p[3] for p in parts)
+    r = _time_launches(args, torch, parts, n, sum(p[2] * p[3] for p in parts), status,
+                       "PTQ init of one dense-decoder block (q,k,v,o 4096x4096; gate,up 11008x4096; down "
+                       "4096x11008) bf16 N(0,0.02^2) onto core ||2z||^2<=16: per-row scale search over "
+                       f"{PTQ_ALPHAS} x row RMS, finite-core projection")
+    ch = torch.cat([e["choice"] for e in sets]).cpu()
+    r["parts"]["choice_histogram"] = [int((ch == k).sum()) for k in range(len(PTQ_ALPHAS))]
+    return r
+
+
 def run_linear(args, torch, e8q, workloads):
     """4096x4096 bf16 rotated projection (q in bf16), cycling over 8 copies of
     the matrix (537 MB) so that the 256 MB last-level cache cannot hold the input."""
@@ -481,7 +523,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder",
                     choices=["decoder", "linear", "moe", "qat", "qat_restore", "qat_rotated_grad",
-                             "decode", "decode_q", "gemv", "pack"])
+                             "decode", "decode_q", "gemv", "pack", "ptq"])
     ap.add_argument("--gemv-m", type=int, default=1, choices=[1, 2])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=1)
@@ -515,6 +557,8 @@ def main():
             r = run_gemv(args, torch, e8q, workloads)
         elif args.config == "pack":
             r = run_pack(args, torch, e8q, workloads)
+        elif args.config == "ptq":
+            r = run_ptq(args, torch, e8q, workloads)
         elif args.config.startswith("decode"):
             r = run_decode(args, torch, e8q, workloads, args.config)
         else:
