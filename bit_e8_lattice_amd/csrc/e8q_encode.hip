@@ -104,7 +104,7 @@ __global__ void encode_init_kernel(uint32_t* counter, unsigned long long* tile_s
 }
 
 template <typename WT, int HB, bool LDS_TAB, bool FAST>
-__global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
     extern __shared__ uint32_t s_dyn[];
     __shared__ uint32_t s_tile;
     __shared__ uint32_t s_cnt[kItems * kWaves];
@@ -153,12 +153,12 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
         const uint32_t tbase = tile * kTileGroups + lpos;
 
         uint32_t flags = 0;
-        // Loads run two items ahead of the arithmetic; lanes past the end read
+        // Loads run one item ahead of the arithmetic; lanes past the end read
         // the last group instead (nothing is stored for them).
-        uint32_t g1 = tbase, g2 = tbase + kBlock;
-        uint32_t r1 = fdiv(min(g1, glast), a.gpr_div), r2 = fdiv(min(g2, glast), a.gpr_div);
-        Raw w1 = load_raw<WT>(a.w, min(g1, glast)), w2 = load_raw<WT>(a.w, min(g2, glast));
-        float c1 = a.coef[r1], c2 = a.coef[r2];
+        uint32_t g1 = tbase;
+        uint32_t r1 = fdiv(min(g1, glast), a.gpr_div);
+        Raw w1 = load_raw<WT>(a.w, min(g1, glast));
+        float c1 = a.coef[r1];
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
             const uint32_t g = g1;
@@ -167,13 +167,12 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
             const uint32_t row = r1;
             const Raw raw = w1;
             const float craw = c1;
-            g1 = g2; r1 = r2; w1 = w2; c1 = c2;
-            if (j + 2 < kItems) {
-                g2 = g + 2u * kBlock;
-                const uint32_t gn = min(g2, glast);
-                r2 = fdiv(gn, a.gpr_div);
-                w2 = load_raw<WT>(a.w, gn);
-                c2 = a.coef[r2];
+            if (j + 1 < kItems) {
+                g1 = g + kBlock;
+                const uint32_t gn = min(g1, glast);
+                r1 = fdiv(gn, a.gpr_div);
+                w1 = load_raw<WT>(a.w, gn);
+                c1 = a.coef[r1];
             }
             float v[8];
             const uint32_t vsign = rotate_group<WT, HB>(s_smask, s_wide, raw, gl - row * a.gpr, lf, lpos, tid, v);
@@ -195,12 +194,15 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
                     const uint32_t st = __builtin_amdgcn_udot4(t1, 0x01010101u, sa4, false);
                     // sum (t + 64)^2 - 128 sum (t + 64) + 8 * 64^2 = ||2z||^2
                     const uint32_t norm = qt - (st << 7) + 32768u;
-                    escaped = live && norm > a.core_bound;
+                    // lanes past the end hold the last group's point, which may be
+                    // outside the core: only points inside it index the rank table
+                    const bool outside = norm > a.core_bound;
+                    escaped = live && outside;
                     const uint32_t na = qa - (sa4 << 7) + 16384u;
                     const uint32_t fi = __builtin_amdgcn_udot4(t0, a.wpk, d8 ? kav[0] : kav[1], false) >> 1;
                     const uint32_t gb = __builtin_amdgcn_udot4(t1, a.wpk, d8 ? kbv[0] : kbv[1], false) >> 1;
                     const uint32_t state = (na >> 1) + ((sa4 >> 1) & 1u);
-                    if (!escaped) cidx = uint32_t(tab[fi]) + uint32_t(tab[__umul24(state, a.rp.nh) + gb]);
+                    if (!outside) cidx = uint32_t(tab[fi]) + uint32_t(tab[__umul24(state, a.rp.nh) + gb]);
                     done = true;
                 }
             }
@@ -208,8 +210,9 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
                 int t[8];
                 const uint32_t inv = exact_point(x, __builtin_isnan(craw), t);
                 if (live) flags |= inv;
-                escaped = live && norm_u32(t) > a.core_bound;
-                if (!escaped) cidx = core_rank(t, tab, a.rp);
+                const bool outside = norm_u32(t) > a.core_bound;
+                escaped = live && outside;
+                if (!outside) cidx = core_rank(t, tab, a.rp);
                 if (a.two_z && live) {
                     uint32_t f8 = 0;
                     *reinterpret_cast<uint2*>(a.two_z + uint64_t(g) * 8) = pack_i8x8(t, f8);

@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t unbias_i8x4(uint32_t t) {
 }
 
 template <typename WT, int HB, bool FAST, bool RESTORE>
-__global__ __launch_bounds__(kBlock) void project_kernel(ProjectArgs a) {
+__global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
     extern __shared__ uint32_t s_dyn[];
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;

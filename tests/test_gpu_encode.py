@@ -167,3 +167,18 @@ def test_decoder_secondary_reading_encode():
         out = run_encode(w, s, 16, sg, hb)
         ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), hb, 16)
         _compare(out, ref)
+
+
+@pytest.mark.parametrize("bound", [16, 32, 40])
+def test_tail_lanes_with_an_escaped_last_group(bound):
+    """Lanes past the end of the input work on a copy of the last group; here
+    that group's point is far outside the core, so they must not index the rank
+    table (bounds 32 and 40 keep it in global memory)."""
+    d = device()
+    w = workloads.normal((1, 3, 136), 777 + bound, d, dtype=torch.float32)
+    s = workloads.rms_scale(w, 1.0)
+    w[0, 2, 128:136] = -25.0 * s[2]
+    out = run_encode(w, s, bound)
+    ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), None, 0, bound, w_is_bf16=False)
+    assert ref["core_idx"][-1] == oracle.ESCAPE_SLOT
+    _compare(out, ref)
