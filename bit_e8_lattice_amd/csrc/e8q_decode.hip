@@ -108,10 +108,37 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     const uint32_t wide_words = (RESTORE && HB > 128) ? uint32_t(8 * kBlock) : 0u;
     uint32_t* s_smask = s_dyn;
     float* s_wide = reinterpret_cast<float*>(s_dyn + smask_words);
+    // LDS tables: the points (2z + 64 bytes) when q or 2z is written, and for
+    // the restore the in-lane part of the inverse transform of every point,
+    // H_8 (2z) as signed bytes (|H_8 (2z)| <= 48 for any core), so that a core
+    // group starts its transform at the cross-lane stages.
+    const bool need_2z = a.q != nullptr || a.two_z != nullptr;
     uint32_t* s_pts = s_dyn + smask_words + wide_words;
+    uint32_t* s_h8 = s_pts + (need_2z ? 2u * a.npts : 0u);
     if constexpr (RESTORE) load_sign_masks(s_smask, a.signs, a.cols, tid);
     if constexpr (LDS_PTS) {
-        for (uint32_t i = tid; i < 2u * a.npts; i += kBlock) s_pts[i] = a.pts[i];
+        if (need_2z)
+            for (uint32_t i = tid; i < 2u * a.npts; i += kBlock) s_pts[i] = a.pts[i];
+        if constexpr (RESTORE) {
+            for (uint32_t i = tid; i < a.npts; i += kBlock) {
+                float h[8];
+                const uint32_t w0 = a.pts[2u * i], w1 = a.pts[2u * i + 1u];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    h[k] = float(int((w0 >> (8 * k)) & 0xFFu) - 64);
+                    h[4 + k] = float(int((w1 >> (8 * k)) & 0xFFu) - 64);
+                }
+                fwht_inlane<8>(h);   // exact: small integers
+                uint32_t o0 = 0, o1 = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    o0 |= (uint32_t(int(h[k])) & 0xFFu) << (8 * k);
+                    o1 |= (uint32_t(int(h[4 + k])) & 0xFFu) << (8 * k);
+                }
+                s_h8[2u * i] = o0;
+                s_h8[2u * i + 1u] = o1;
+            }
+        }
     }
     if constexpr (RESTORE || LDS_PTS) __syncthreads();
     const uint32_t* pts = LDS_PTS ? s_pts : a.pts;
@@ -155,9 +182,16 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
             uint32_t t0 = 0x40404040u, t1 = 0x40404040u;   // 2z + 64 bytes (z = 0)
             bool big = false;
             int tb[8];
+            uint32_t h0 = 0u, h1 = 0u;   // H_8 (2z) signed bytes (table restore)
             if (idx < a.npts) {
-                t0 = pts[2u * idx];
-                t1 = pts[2u * idx + 1u];
+                if (!LDS_PTS || need_2z) {
+                    t0 = pts[2u * idx];
+                    t1 = pts[2u * idx + 1u];
+                }
+                if constexpr (RESTORE && LDS_PTS) {
+                    h0 = s_h8[2u * idx];
+                    h1 = s_h8[2u * idx + 1u];
+                }
             } else if (idx == 0xFFFFu) {
                 const uint32_t b = fdiv(gl, a.gpb_div);
                 if (find_record(a.esc, a.offsets, b, gl - b * a.gpb, tb)) {
@@ -213,21 +247,35 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
             if constexpr (RESTORE) {
                 // inverse rotation across the block; every lane takes part
                 float r[8];
-                float rcorr;
-                if (big) {
+                if constexpr (LDS_PTS) {
+                    if (big) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) r[i] = float(tb[i]);
-                    rcorr = 0.0f;
-                } else {
+                        for (int i = 0; i < 8; ++i) r[i] = float(tb[i]);
+                        fwht_inlane<8>(r);
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        r[i] = float((t0 >> (8 * i)) & 0xFFu);
-                        r[4 + i] = float((t1 >> (8 * i)) & 0xFFu);
+                        for (int i = 0; i < 4; ++i) {
+                            r[i] = float(int32_t(h0 << (24 - 8 * i)) >> 24);
+                            r[4 + i] = float(int32_t(h1 << (24 - 8 * i)) >> 24);
+                        }
                     }
-                    rcorr = 512.0f;
+                } else {
+                    float rcorr;
+                    if (big) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) r[i] = float(tb[i]);
+                        rcorr = 0.0f;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            r[i] = float((t0 >> (8 * i)) & 0xFFu);
+                            r[4 + i] = float((t1 >> (8 * i)) & 0xFFu);
+                        }
+                        rcorr = 512.0f;
+                    }
+                    fwht_inlane<8>(r);
+                    r[0] -= rcorr;
                 }
-                fwht_inlane<8>(r);
-                r[0] -= rcorr;
                 const uint32_t rs = fwht_cross<HB>(r, lf, s_wide, lpos, tid);
                 const float c2 = bad ? 0.0f : (s * a.kappa) * 0.5f;
                 const float c2s = __uint_as_float(__float_as_uint(c2) ^ rs);
@@ -349,7 +397,8 @@ extern "C" e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx, const e
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
                        uint64_t(esc_capacity), static_cast<uint64_t*>(workspace));
-    const size_t pts_lds = size_t(a.npts) * 8;
+    const bool need_2z = q_out != nullptr || two_z_out != nullptr;
+    const size_t pts_lds = size_t(a.npts) * 8 * ((need_2z ? 1 : 0) + (restore ? 1 : 0));
     const bool lds_pts = base_lds + pts_lds <= 60 * 1024;
     const size_t lds = base_lds + (lds_pts ? pts_lds : 0);
     if (restore) {
