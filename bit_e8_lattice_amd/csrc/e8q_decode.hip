@@ -290,7 +290,11 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
                         p.y = bf16x2_rne_dec(y[2], y[3]) ^ m.y;
                         p.z = bf16x2_rne_dec(y[4], y[5]) ^ m.z;
                         p.w = bf16x2_rne_dec(y[6], y[7]) ^ m.w;
-                        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.w_hat) + uint64_t(g) * 8) = p;
+                        // streamed out, never read back here: nontemporal
+                        __builtin_nontemporal_store(p.x, reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.w_hat) + uint64_t(g) * 8));
+                        __builtin_nontemporal_store(p.y, reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.w_hat) + uint64_t(g) * 8) + 1);
+                        __builtin_nontemporal_store(p.z, reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.w_hat) + uint64_t(g) * 8) + 2);
+                        __builtin_nontemporal_store(p.w, reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.w_hat) + uint64_t(g) * 8) + 3);
                     } else {
                         flip_f32(y, m);
                         float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.w_hat) + uint64_t(g) * 8);
