@@ -36,8 +36,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_dense_decoder_traffic.json")
+# the encode kernel, its rank table and its launch configuration
 KERNEL_SOURCES = ["e8q_device.hpp", "e8q_point.hpp", "e8q_encode.hip", "e8q_core_table.cpp", "e8q_core_table.hpp",
-                  "e8q_host.hpp", "e8q_common.hip"]
+                  "e8q_host.hpp"]
 
 
 def kernel_hash():

@@ -1,11 +1,19 @@
 // Host-only entry points and shared host state.
 #include <atomic>
+#include <cstddef>
 #include <map>
 #include <mutex>
-#include <tuple>
 
 #include "e8q_core_table.hpp"
 #include "e8q_host.hpp"
+
+// The record layouts are part of the ABI (kernels read and write them as
+// 32-bit words).
+static_assert(sizeof(e8q_escape_t) == 20 && alignof(e8q_escape_t) == 4, "escape record layout");
+static_assert(offsetof(e8q_escape_t, two_z) == 4, "escape record layout");
+static_assert(sizeof(e8q_escape_packed_t) == 8, "packed record layout");
+static_assert(offsetof(e8q_escape_packed_t, core_idx) == 4 && offsetof(e8q_escape_packed_t, root) == 6,
+              "packed record layout");
 
 namespace e8q {
 
@@ -85,30 +93,6 @@ int device_cu_count() {
         cache[dev] = cu;
     }
     return cache[dev];
-}
-
-unsigned resident_grid(const void* func, unsigned block, size_t lds, uint64_t tiles) {
-    static std::mutex mu;
-    static std::map<std::tuple<int, const void*, unsigned, size_t>, int> cache;
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    int per_cu = 0;
-    {
-        std::lock_guard<std::mutex> lk(mu);
-        const auto key = std::make_tuple(dev, func, block, lds);
-        auto it = cache.find(key);
-        if (it != cache.end()) {
-            per_cu = it->second;
-        } else {
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, int(block), lds) != hipSuccess ||
-                per_cu < 1)
-                per_cu = 1;
-            cache.emplace(key, per_cu);
-        }
-    }
-    const uint64_t cap = uint64_t(device_cu_count()) * uint64_t(per_cu);
-    if (tiles < 1) tiles = 1;
-    return unsigned(tiles < cap ? tiles : cap);
 }
 
 }  // namespace e8q

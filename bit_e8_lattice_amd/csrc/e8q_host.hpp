@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "e8q.h"
 #include "e8q_core_table.hpp"
 
@@ -42,7 +46,30 @@ inline unsigned grid_for(uint64_t items, unsigned per_block, unsigned blocks_per
 // Kernels that loop over tiles with a grid stride are launched with exactly
 // this many blocks: more would only start when resident blocks finish, i.e.
 // at the end, and stretch the tail.
-unsigned resident_grid(const void* func, unsigned block, size_t lds, uint64_t tiles);
+inline unsigned resident_grid(const void* func, unsigned block, size_t lds, uint64_t tiles) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, const void*, unsigned, size_t>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int per_cu = 0;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        const auto key = std::make_tuple(dev, func, block, lds);
+        auto it = cache.find(key);
+        if (it != cache.end()) {
+            per_cu = it->second;
+        } else {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, int(block), lds) != hipSuccess ||
+                per_cu < 1)
+                per_cu = 1;
+            cache.emplace(key, per_cu);
+        }
+    }
+    const uint64_t cap = uint64_t(device_cu_count()) * uint64_t(per_cu);
+    if (tiles < 1) tiles = 1;
+    return unsigned(tiles < cap ? tiles : cap);
+}
+
 
 template <typename A>
 inline void launch_tiles(void (*kernel)(A), const A& args, uint64_t tiles, unsigned block, size_t lds,
