@@ -31,6 +31,10 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source additions.  The PTQ search keeps its MFMA accumulators in
+# ordinary VGPRs (no copies out of the accumulation registers per tile).
+SOURCE_FLAGS = {"e8q_ptq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def hipcc():
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -50,7 +54,7 @@ def build(verbose=False, jobs=None):
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmpdir, src + ".o")
-            cmd = [hipcc()] + FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             objs.append(obj)

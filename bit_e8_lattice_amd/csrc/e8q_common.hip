@@ -1,6 +1,7 @@
 // Host-only entry points and shared host state.
 #include <atomic>
 #include <cstddef>
+#include <cstring>
 #include <map>
 #include <mutex>
 
@@ -33,6 +34,49 @@ bool upload(const std::vector<T>& v, T*& dptr) {
         return false;
     }
     return true;
+}
+// The tile tables of DevTable: shells ||t||^2 = 0, 8, 16, ... in increasing
+// norm, each in rank order, cut into tiles of kTileRows rows.
+std::vector<uint8_t> build_tiles(const CoreTable& c, uint32_t& ntiles) {
+    auto coord = [&](int64_t i, int k) { return int((c.points[2 * i + k / 4] >> (8 * (k % 4))) & 0xFFu) - 64; };
+    std::vector<std::vector<int64_t>> shells(size_t(c.bound / 8) + 1);
+    int64_t origin = -1;
+    for (int64_t i = 0; i < c.size; ++i) {
+        int n = 0;
+        for (int k = 0; k < 8; ++k) n += coord(i, k) * coord(i, k);
+        shells[size_t(n / 8)].push_back(i);
+        if (n == 0) origin = i;
+    }
+    std::vector<int64_t> rows;    // -1 = pad
+    std::vector<float> n4;
+    for (size_t s = 0; s < shells.size(); ++s) {
+        const auto& sh = shells[s];
+        if (sh.empty()) continue;
+        const size_t nt = (sh.size() + kTileRows - 1) / kTileRows;
+        for (size_t j = 0; j < nt * kTileRows; ++j) rows.push_back(j < sh.size() ? sh[j] : -1);
+        for (size_t j = 0; j < nt; ++j) n4.push_back(float(s * 8) / 4.0f);
+    }
+    ntiles = uint32_t(n4.size());
+    const size_t nt = ntiles;
+    std::vector<uint8_t> out(nt * 836, 0);
+    uint16_t* bf = reinterpret_cast<uint16_t*>(out.data());
+    int8_t* t8 = reinterpret_cast<int8_t*>(out.data() + nt * 512);
+    uint16_t* idx = reinterpret_cast<uint16_t*>(out.data() + nt * 768);
+    float* nf = reinterpret_cast<float*>(out.data() + nt * 832);
+    for (size_t r = 0; r < rows.size(); ++r) {
+        const int64_t i = rows[r];
+        idx[r] = uint16_t(i < 0 ? origin : i);
+        for (int k = 0; k < 8; ++k) {
+            const int v = i < 0 ? 0 : coord(i, k);
+            const float f = float(v);
+            uint32_t u;
+            std::memcpy(&u, &f, 4);
+            bf[r * 8 + k] = uint16_t(u >> 16);   // small integers are exact in bf16
+            t8[r * 8 + k] = int8_t(v);
+        }
+    }
+    std::memcpy(nf, n4.data(), nt * 4);
+    return out;
 }
 }  // namespace
 
@@ -68,10 +112,12 @@ const DevTable* get_table(int32_t bound, e8q_status_t& err) {
         }
         p64[size_t(i) * 9 + 8] = n / 4.0;
     }
-    if (!upload(roots, t.droots) || !upload(p64, t.dpts64)) {
+    std::vector<uint8_t> tiles = build_tiles(t.host, t.ntiles);
+    if (!upload(roots, t.droots) || !upload(p64, t.dpts64) || !upload(tiles, t.dtiles)) {
         (void)hipFree(t.dptr);
         (void)hipFree(t.dpoints);
         if (t.droots) (void)hipFree(t.droots);
+        if (t.dpts64) (void)hipFree(t.dpts64);
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }

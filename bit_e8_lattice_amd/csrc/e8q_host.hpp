@@ -22,8 +22,19 @@ struct DevTable {
     uint32_t* dpoints = nullptr;
     uint32_t* droots = nullptr;   // the 240 roots (same word layout as the points)
     double* dpts64 = nullptr;     // points in rank order as 9 doubles: t_0..t_7 (= 2z), ||t||^2 / 4
+    // The points grouped by norm shell into tiles of 32 rows for the
+    // matrix-core search; a shell's last tile is padded with zero rows.  Per
+    // tile, at these offsets (in tiles of ntiles):
+    //   0            : 32 rows x 8 bf16 (t = 2z)            512 B per tile
+    //   ntiles * 512 : 32 rows x 8 int8 (t)                 256 B per tile
+    //   ntiles * 768 : 32 uint16 core indices (pads: the origin's)  64 B per tile
+    //   ntiles * 832 : the shell's ||t||^2 / 4 as float        4 B per tile
+    uint8_t* dtiles = nullptr;
+    uint32_t ntiles = 0;
     CoreTable host;
 };
+
+constexpr uint32_t kTileRows = 32;
 
 // Tables for (current device, bound); nullptr with err set on failure.
 const DevTable* get_table(int32_t bound, e8q_status_t& err);

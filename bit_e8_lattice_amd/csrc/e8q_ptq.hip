@@ -22,9 +22,14 @@
 // once (e8q_rotate.hpp) into the workspace.  Per candidate, the lanes stride
 // over the row's groups: the nearest E8 point and, for points inside the core,
 // the group error go to LDS; groups outside the core are listed (in group
-// order) and then searched 64 at a time, one per lane, over the core points,
-// whose float64 coordinates are read as wave-uniform values.  The row error is
-// then summed from LDS in the fixed order.
+// order) and searched 32 at a time.  The search is a dense contraction (every
+// group against every core point), so it runs on the matrix cores: the core
+// points, sorted into norm shells and tiles of 32, meet a bfloat16 hi + mid
+// split of the groups in one 32x32x16 MFMA per tile, which screens the
+// float64 keys to within a bound; only the best tile's 32 points are then
+// evaluated exactly.  Groups whose best two tiles come within the bound go to
+// an exhaustive float64 search.  The row error is then summed from LDS in the
+// fixed order.
 #include "e8q_device.hpp"
 #include "e8q_host.hpp"
 #include "e8q_point.hpp"
@@ -46,6 +51,10 @@ struct PtqArgs {
     int core_bound;
     const double* pts64;       // [npts][9]
     uint32_t npts;
+    const uint8_t* tiles;      // shell tiles (matrix-core search)
+    uint32_t ntiles;
+    float tmax;                // largest |t_i| of a core point (bound)
+    float nmax4;               // B / 4
     const uint16_t* tab;
     RankParams rp;
     float* scale_out;
@@ -79,6 +88,188 @@ __device__ __forceinline__ void load_v(const float* row, uint32_t g, float (&v)[
     const float4 a = p[0], b = p[1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef const __attribute__((address_space(4))) double* const_dptr;
+typedef const __attribute__((address_space(4))) float* const_fptr;
+
+// Round-to-nearest-even to bfloat16 (finite inputs), returned as float.
+__device__ __forceinline__ float bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
+}
+
+// The search key x.t - ||t||^2/4 in float64 in the fixed order: exact
+// products, pairwise sums, then the exact ||t||^2/4.
+__device__ __forceinline__ double exact_key(const double (&x64)[8], const int (&t)[8]) {
+    double q[8];
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        q[i] = x64[i] * double(t[i]);
+        n += t[i] * t[i];
+    }
+    return (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]))) - 0.25 * double(n);
+}
+
+// Nearest core point of the group v*c by the float64 key over every core
+// point in rank order (first maximum wins).
+__device__ uint32_t exhaustive_search(const PtqArgs& a, const float (&v)[8], float c) {
+    double x64[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x64[i] = double(v[i] * c);
+    double best = -__builtin_inf();
+    uint32_t bi = 0;
+    // the candidate is the same on every lane: read it through the constant
+    // address space so that it comes in with scalar loads
+    const const_dptr pts = (const_dptr)(uintptr_t)a.pts64;
+#pragma unroll 2
+    for (uint32_t p = 0; p < a.npts; ++p) {
+        const const_dptr tp = pts + uint64_t(p) * 9;
+        double q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = x64[i] * tp[i];
+        const double key = (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]))) - tp[8];
+        if (key > best) {
+            best = key;
+            bi = p;
+        }
+    }
+    return bi;
+}
+
+__device__ __forceinline__ float tile_max(const f32x16_t& d) {
+    float m = fmaxf(fmaxf(d[0], d[1]), d[2]);
+    m = fmaxf(fmaxf(m, d[3]), d[4]);
+    m = fmaxf(fmaxf(m, d[5]), d[6]);
+    m = fmaxf(fmaxf(m, d[7]), d[8]);
+    m = fmaxf(fmaxf(m, d[9]), d[10]);
+    m = fmaxf(fmaxf(m, d[11]), d[12]);
+    m = fmaxf(fmaxf(m, d[13]), d[14]);
+    return fmaxf(m, d[15]);
+}
+
+// Matrix-core screening of one group per lane pair (lanes l and l + 32 hold
+// the group of column l % 32).  x = v*c is split as x = hi + mid + r with hi,
+// mid bfloat16; one 32x32x16 MFMA per tile of 32 core points computes
+// t.hi + t.mid for every (point, group) pair, lanes < 32 feeding hi and lanes
+// >= 32 mid against the same points.  Each lane keeps, over the tiles, the
+// largest approximate key of its 16 rows (M1, in tile T1) and the largest of
+// the other tiles (M2).  The approximate keys are within eps of the float64
+// keys:
+//   eps = tmax * sum|r_i| + 2^-18 * (tmax * sum|x_i| + B/4)
+// (|t_i| <= tmax; the products are exact in float32 and the sum of 16
+// products plus the norm takes fewer than 2^5 roundings of at most 2^-23
+// relative each).  If no tile other than the best one comes within 3 eps of
+// the best key, the winner is in the best tile: the two lanes evaluate its 32
+// rows exactly and keep the largest float64 key, ties to the lower core index.
+// Otherwise `amb` is set and the group goes to the exhaustive search.
+__device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (&v)[8], float c, uint32_t lane,
+                                                 bool& amb) {
+    const bool lo_half = lane < 32u;
+    float x[8];
+    bf16x8_t b;
+    float rsum = 0.0f, xsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        x[i] = v[i] * c;
+        const float hi = bf16_rne(x[i]);
+        const float d = x[i] - hi;          // exact
+        const float mid = bf16_rne(d);
+        rsum += fabsf(d - mid);             // d - mid exact
+        xsum += fabsf(x[i]);
+        const uint16_t bits = uint16_t(__float_as_uint(lo_half ? hi : mid) >> 16);
+        b[i] = __builtin_bit_cast(__bf16, bits);
+    }
+    const float eps = 1.01f * (a.tmax * rsum + 0x1p-18f * (a.tmax * xsum + a.nmax4)) + 1e-30f;
+
+    const bf16x8_t* at = reinterpret_cast<const bf16x8_t*>(a.tiles) + (lane & 31u);
+    const const_fptr n4t = (const_fptr)(uintptr_t)(a.tiles + size_t(a.ntiles) * 832);
+    const f32x16_t zero = {};
+    const uint32_t last = a.ntiles - 1u;
+    float m1 = -__builtin_inff(), m2 = -__builtin_inff();
+    uint32_t t1 = 0;
+    // two tiles per step, the next two tiles' points loaded ahead (the loads
+    // clamp to the last tile; a step past the end repeats it, which changes
+    // neither maximum)
+    bf16x8_t p0 = at[0], p1 = at[size_t(min(1u, last)) * kTileRows];
+    for (uint32_t tile = 0; tile < a.ntiles; tile += 2) {
+        const uint32_t tb = min(tile + 1u, last);
+        const f32x16_t d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, b, zero, 0, 0, 0);
+        const f32x16_t d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, b, zero, 0, 0, 0);
+        p0 = at[size_t(min(tile + 2u, last)) * kTileRows];
+        p1 = at[size_t(min(tile + 3u, last)) * kTileRows];
+        const float k0 = tile_max(d0) - n4t[tile];
+        const float k1 = tile_max(d1) - n4t[tb];
+        m2 = __builtin_amdgcn_fmed3f(m1, m2, k0);
+        t1 = k0 > m1 ? tile : t1;
+        m1 = fmaxf(m1, k0);
+        // a repeated last tile must not count as a second tile
+        if (tb != tile) {
+            m2 = __builtin_amdgcn_fmed3f(m1, m2, k1);
+            t1 = k1 > m1 ? tb : t1;
+            m1 = fmaxf(m1, k1);
+        }
+    }
+    // combine the two halves of the tile rows (values of half 0 first)
+    const float om1 = __shfl_xor(m1, 32, 64), om2 = __shfl_xor(m2, 32, 64);
+    const uint32_t ot1 = uint32_t(__shfl_xor(int(t1), 32, 64));
+    const float a1 = lo_half ? m1 : om1, a2 = lo_half ? m2 : om2;
+    const float b1 = lo_half ? om1 : m1, b2 = lo_half ? om2 : m2;
+    const uint32_t ta = lo_half ? t1 : ot1, tb = lo_half ? ot1 : t1;
+    const uint32_t ts = a1 >= b1 ? ta : tb;
+    const float top = fmaxf(a1, b1);
+    const float comp = fmaxf(ta == ts ? a2 : a1, tb == ts ? b2 : b1);
+    amb = !(top - comp > 3.0f * eps);
+
+    // exact keys of this lane's 16 rows of tile ts
+    double x64[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x64[i] = double(x[i]);
+    const uint8_t* t8 = a.tiles + size_t(a.ntiles) * 512 + size_t(ts) * kTileRows * 8;
+    const uint16_t* ix = reinterpret_cast<const uint16_t*>(a.tiles + size_t(a.ntiles) * 768) + size_t(ts) * kTileRows;
+    const uint32_t half = lane >> 5;
+    double best = -__builtin_inf();
+    uint32_t bi = 0xFFFFFFFFu;
+#pragma unroll 2
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t row = 8u * uint32_t(r >> 2) + 4u * half + uint32_t(r & 3);
+        const uint2 w = *reinterpret_cast<const uint2*>(t8 + row * 8);
+        int t[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            t[i] = int(int8_t(w.x >> (8 * i)));
+            t[4 + i] = int(int8_t(w.y >> (8 * i)));
+        }
+        const double key = exact_key(x64, t);
+        const uint32_t idx = ix[row];
+        if (key > best || (key == best && idx < bi)) {
+            best = key;
+            bi = idx;
+        }
+    }
+    const double ob = __shfl_xor(best, 32, 64);
+    const uint32_t oi = uint32_t(__shfl_xor(int(bi), 32, 64));
+    if (ob > best || (ob == best && oi < bi)) bi = oi;
+    return bi;
+}
+
+// The group's error (and, with WRITE, its point) for core point bi.
+template <bool WRITE>
+__device__ __forceinline__ void finish_group(const PtqArgs& a, const float (&v)[8], uint32_t bi, uint32_t g,
+                                             uint64_t gbase, double k64, double s64, double* s_e) {
+    const double* tp = a.pts64 + uint64_t(bi) * 9;
+    int t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = int(tp[i]);
+    s_e[g] = group_error(v, t, k64, s64);
+    if constexpr (WRITE) {
+        uint32_t f8 = 0;
+        *reinterpret_cast<uint2*>(a.two_z + (gbase + g) * 8) = pack_i8x8(t, f8);
+        a.core_idx[gbase + g] = uint16_t(bi);
+    }
 }
 
 // One candidate scale over one row.  Returns the row error (valid on every
@@ -123,46 +314,32 @@ __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, dou
         nlist += uint32_t(__popcll(m));
     }
     wave_sync();
-    // groups outside the core: exhaustive search, one group per lane
-    for (uint32_t j0 = 0; j0 < nlist; j0 += kWave) {
+    // groups outside the core, 32 at a time: matrix-core screening, then the
+    // exact keys of the one tile that can hold the winner
+    uint32_t namb = 0;
+    for (uint32_t j0 = 0; j0 < nlist; j0 += kTileRows) {
+        const uint32_t jn = j0 + (lane & 31u);
+        const bool act = jn < nlist;
+        const uint32_t g = uint32_t(s_list[act ? jn : j0]);
+        float v[8];
+        load_v(vrow, g, v);
+        bool amb;
+        const uint32_t bi = screen_group(a, v, c, lane, amb);
+        const uint64_t m = __ballot(act && amb && lane < 32u);
+        if (act && amb && lane < 32u) s_list[namb + __popcll(m & ((1ull << lane) - 1ull))] = uint16_t(g);
+        namb += uint32_t(__popcll(m));
+        if (act && !amb && lane < 32u) finish_group<WRITE>(a, v, bi, g, gbase, k64, s64, s_e);
+    }
+    wave_sync();
+    // near ties between tiles: exhaustive float64 search, one group per lane
+    for (uint32_t j0 = 0; j0 < namb; j0 += kWave) {
         const uint32_t j = j0 + lane;
-        const bool act = j < nlist;
+        const bool act = j < namb;
         const uint32_t g = act ? uint32_t(s_list[j]) : 0u;
         float v[8];
         load_v(vrow, g, v);
-        double x64[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x64[i] = double(v[i] * c);
-        double best = -__builtin_inf();
-        uint32_t bi = 0;
-        // the candidate is the same on every lane: read it through the constant
-        // address space so that it comes in with scalar loads
-        typedef const __attribute__((address_space(4))) double* const_dptr;
-        const const_dptr pts = (const_dptr)(uintptr_t)a.pts64;
-#pragma unroll 2
-        for (uint32_t p = 0; p < a.npts; ++p) {
-            const const_dptr tp = pts + uint64_t(p) * 9;
-            double q[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = x64[i] * tp[i];
-            const double key = (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]))) - tp[8];
-            if (key > best) {
-                best = key;
-                bi = p;
-            }
-        }
-        if (act) {
-            const double* tp = a.pts64 + uint64_t(bi) * 9;
-            int t[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) t[i] = int(tp[i]);
-            s_e[g] = group_error(v, t, k64, s64);
-            if constexpr (WRITE) {
-                uint32_t f8 = 0;
-                *reinterpret_cast<uint2*>(a.two_z + (gbase + g) * 8) = pack_i8x8(t, f8);
-                a.core_idx[gbase + g] = uint16_t(bi);
-            }
-        }
+        const uint32_t bi = exhaustive_search(a, v, c);
+        if (act) finish_group<WRITE>(a, v, bi, g, gbase, k64, s64, s_e);
     }
     wave_sync();
     // the row error in the fixed order
@@ -292,6 +469,10 @@ extern "C" e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype, int64_t
     a.core_bound = core_bound;
     a.pts64 = tab->dpts64;
     a.npts = uint32_t(tab->host.size);
+    a.tiles = tab->dtiles;
+    a.ntiles = tab->ntiles;
+    a.tmax = floorf(sqrtf(float(core_bound)));
+    a.nmax4 = float(core_bound) / 4.0f;
     a.tab = tab->dptr;
     a.rp = tab->host.p;
     a.scale_out = scale_out;

@@ -81,3 +81,48 @@ def test_ptq_decoder_block_sampled_rows_and_decode():
         e = ((wf - dec["w_hat"].reshape(nb * rows, cols).astype(np.float64)) ** 2).sum(1)
         chosen = out["err"][np.arange(nb * rows), out["k"]]
         assert np.allclose(e, chosen, rtol=1e-4, atol=0)
+
+
+def _search_groups(bound, n, seed):
+    """Normalized groups (exact float32 values) that stress the core search:
+    points on the bisector mu (t1 + t2) / 4 of two points of one shell (their
+    keys are exactly equal), groups far outside the core, and ordinary ones."""
+    rng = np.random.default_rng(seed)
+    pts = oracle.core_points(bound).astype(np.int64)
+    nrm = (pts * pts).sum(1)
+    shells = [pts[nrm == s] for s in range(8, bound + 1, 8) if (nrm == s).any()]
+    out = []
+    while len(out) < n:
+        kind = int(rng.integers(0, 3))
+        if kind == 0 and shells:
+            sh = shells[int(rng.integers(0, len(shells)))]
+            t1, t2 = sh[rng.integers(0, len(sh), 2)]
+            x = float(rng.choice([1.25, 1.5, 2.0, 3.0, 5.0])) * (t1 + t2) / 4.0
+        elif kind == 1:
+            x = np.round(rng.standard_normal(8) * float(rng.choice([4.0, 16.0, 64.0])) * 64) / 64
+        else:
+            x = np.round(rng.standard_normal(8) * 2 * 256) / 256
+        out.append(x)
+    return np.asarray(out, np.float32), pts, nrm
+
+
+@pytest.mark.parametrize("bound", [0, 7, 16, 32, 40])
+def test_ptq_search_ties_and_far_groups(bound):
+    """The search against the oracle on groups chosen so that the best core
+    point is often tied (equal float64 keys in different tiles and in one
+    tile), including the one-point core and the largest core."""
+    d = device()
+    n = 128 if bound == 40 else 1024
+    x, pts, nrm = _search_groups(bound, n, 2300 + bound)
+    keys = x.astype(np.float64) @ pts.T.astype(np.float64) - nrm / 4.0
+    outside = (oracle.nearest_e8_two_z(x) ** 2).sum(1) > bound
+    ties = (keys == keys.max(1, keepdims=True)).sum(1) >= 2
+    if bound >= 8:
+        assert (outside & ties).sum() >= 10     # the tie cases are really searched
+    assert outside.sum() >= n // 2
+    w = torch.from_numpy(x.reshape(1, n // 32, 256)).to(d)
+    s0 = torch.ones(n // 32, dtype=torch.float32, device=d)
+    out = run_ptq(w, s0, [1.0], bound)
+    ref = oracle.ptq_init(x.reshape(1, n // 32, 256), np.ones(n // 32, np.float32), [1.0], None, 0, bound,
+                          w_is_bf16=False)
+    _cmp(out, ref)
