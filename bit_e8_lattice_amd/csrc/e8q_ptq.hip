@@ -26,10 +26,9 @@
 // group against every core point), so it runs on the matrix cores: the core
 // points, sorted into norm shells and tiles of 32, meet a bfloat16 hi + mid
 // split of the groups in one 32x32x16 MFMA per tile, which screens the
-// float64 keys to within a bound; only the best tile's 32 points are then
-// evaluated exactly.  Groups whose best two tiles come within the bound go to
-// an exhaustive float64 search.  The row error is then summed from LDS in the
-// fixed order.
+// float64 keys to within a bound; only the best tile's 32 points (and, on a
+// near tie, the other tiles within the bound) are then evaluated exactly.  The
+// row error is then summed from LDS in the fixed order.
 #include "e8q_device.hpp"
 #include "e8q_host.hpp"
 #include "e8q_point.hpp"
@@ -114,32 +113,6 @@ __device__ __forceinline__ double exact_key(const double (&x64)[8], const int (&
     return (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]))) - 0.25 * double(n);
 }
 
-// Nearest core point of the group v*c by the float64 key over every core
-// point in rank order (first maximum wins).
-__device__ uint32_t exhaustive_search(const PtqArgs& a, const float (&v)[8], float c) {
-    double x64[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x64[i] = double(v[i] * c);
-    double best = -__builtin_inf();
-    uint32_t bi = 0;
-    // the candidate is the same on every lane: read it through the constant
-    // address space so that it comes in with scalar loads
-    const const_dptr pts = (const_dptr)(uintptr_t)a.pts64;
-#pragma unroll 2
-    for (uint32_t p = 0; p < a.npts; ++p) {
-        const const_dptr tp = pts + uint64_t(p) * 9;
-        double q[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = x64[i] * tp[i];
-        const double key = (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]))) - tp[8];
-        if (key > best) {
-            best = key;
-            bi = p;
-        }
-    }
-    return bi;
-}
-
 __device__ __forceinline__ float tile_max(const f32x16_t& d) {
     float m = fmaxf(fmaxf(d[0], d[1]), d[2]);
     m = fmaxf(fmaxf(m, d[3]), d[4]);
@@ -149,6 +122,32 @@ __device__ __forceinline__ float tile_max(const f32x16_t& d) {
     m = fmaxf(fmaxf(m, d[11]), d[12]);
     m = fmaxf(fmaxf(m, d[13]), d[14]);
     return fmaxf(m, d[15]);
+}
+
+// Exact float64 keys of this lane's 16 rows of a tile (rows 8(r/4) + 4 half
+// + r%4, the rows an MFMA result holds for lane half `half`); the largest key
+// wins, ties to the lower core index.
+__device__ __forceinline__ void eval_rows(const PtqArgs& a, const double (&x64)[8], uint32_t tile, uint32_t half,
+                                          double& best, uint32_t& bi) {
+    const uint8_t* t8 = a.tiles + size_t(a.ntiles) * 512 + size_t(tile) * kTileRows * 8;
+    const uint16_t* ix = reinterpret_cast<const uint16_t*>(a.tiles + size_t(a.ntiles) * 768) + size_t(tile) * kTileRows;
+#pragma unroll 1
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t row = 8u * uint32_t(r >> 2) + 4u * half + uint32_t(r & 3);
+        const uint2 w = *reinterpret_cast<const uint2*>(t8 + row * 8);
+        int t[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            t[i] = int(int8_t(w.x >> (8 * i)));
+            t[4 + i] = int(int8_t(w.y >> (8 * i)));
+        }
+        const double key = exact_key(x64, t);
+        const uint32_t idx = ix[row];
+        if (key > best || (key == best && idx < bi)) {
+            best = key;
+            bi = idx;
+        }
+    }
 }
 
 // Matrix-core screening of one group per lane pair (lanes l and l + 32 hold
@@ -162,12 +161,13 @@ __device__ __forceinline__ float tile_max(const f32x16_t& d) {
 //   eps = tmax * sum|r_i| + 2^-18 * (tmax * sum|x_i| + B/4)
 // (|t_i| <= tmax; the products are exact in float32 and the sum of 16
 // products plus the norm takes fewer than 2^5 roundings of at most 2^-23
-// relative each).  If no tile other than the best one comes within 3 eps of
-// the best key, the winner is in the best tile: the two lanes evaluate its 32
-// rows exactly and keep the largest float64 key, ties to the lower core index.
-// Otherwise `amb` is set and the group goes to the exhaustive search.
-__device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (&v)[8], float c, uint32_t lane,
-                                                 bool& amb) {
+// relative each).  A point whose approximate key is below best - 3 eps has a
+// float64 key below that of the best tile's best point, so only tiles within
+// 3 eps of the best can hold the winner.  The two lanes evaluate the best
+// tile's 32 rows exactly; if another tile comes within 3 eps (a near tie), a
+// second sweep evaluates every such tile too.  The largest float64 key wins,
+// ties to the lower core index.
+__device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (&v)[8], float c, uint32_t lane) {
     const bool lo_half = lane < 32u;
     float x[8];
     bf16x8_t b;
@@ -201,6 +201,8 @@ __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (
         const f32x16_t d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, b, zero, 0, 0, 0);
         p0 = at[size_t(min(tile + 2u, last)) * kTileRows];
         p1 = at[size_t(min(tile + 3u, last)) * kTileRows];
+        // keep the loads of the next step ahead of this step's reductions
+        __builtin_amdgcn_sched_barrier(0);
         const float k0 = tile_max(d0) - n4t[tile];
         const float k1 = tile_max(d1) - n4t[tb];
         m2 = __builtin_amdgcn_fmed3f(m1, m2, k0);
@@ -222,32 +224,23 @@ __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (
     const uint32_t ts = a1 >= b1 ? ta : tb;
     const float top = fmaxf(a1, b1);
     const float comp = fmaxf(ta == ts ? a2 : a1, tb == ts ? b2 : b1);
-    amb = !(top - comp > 3.0f * eps);
+    const bool amb = !(top - comp > 3.0f * eps);
 
-    // exact keys of this lane's 16 rows of tile ts
     double x64[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x64[i] = double(x[i]);
-    const uint8_t* t8 = a.tiles + size_t(a.ntiles) * 512 + size_t(ts) * kTileRows * 8;
-    const uint16_t* ix = reinterpret_cast<const uint16_t*>(a.tiles + size_t(a.ntiles) * 768) + size_t(ts) * kTileRows;
     const uint32_t half = lane >> 5;
     double best = -__builtin_inf();
     uint32_t bi = 0xFFFFFFFFu;
-#pragma unroll 2
-    for (int r = 0; r < 16; ++r) {
-        const uint32_t row = 8u * uint32_t(r >> 2) + 4u * half + uint32_t(r & 3);
-        const uint2 w = *reinterpret_cast<const uint2*>(t8 + row * 8);
-        int t[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            t[i] = int(int8_t(w.x >> (8 * i)));
-            t[4 + i] = int(int8_t(w.y >> (8 * i)));
-        }
-        const double key = exact_key(x64, t);
-        const uint32_t idx = ix[row];
-        if (key > best || (key == best && idx < bi)) {
-            best = key;
-            bi = idx;
+    eval_rows(a, x64, ts, half, best, bi);
+    // near ties between tiles: a second sweep evaluates exactly every other
+    // tile whose approximate key comes within 3 eps of the best
+    if (__ballot(amb)) {
+        const float thr = top - 3.0f * eps;
+        for (uint32_t tile = 0; tile < a.ntiles; ++tile) {
+            const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at[size_t(tile) * kTileRows], b, zero, 0, 0, 0);
+            const float k = tile_max(d) - n4t[tile];
+            if (amb && tile != ts && k >= thr) eval_rows(a, x64, tile, half, best, bi);
         }
     }
     const double ob = __shfl_xor(best, 32, 64);
@@ -314,32 +307,15 @@ __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, dou
         nlist += uint32_t(__popcll(m));
     }
     wave_sync();
-    // groups outside the core, 32 at a time: matrix-core screening, then the
-    // exact keys of the one tile that can hold the winner
-    uint32_t namb = 0;
+    // groups outside the core, 32 at a time (lanes l and l + 32 share one)
     for (uint32_t j0 = 0; j0 < nlist; j0 += kTileRows) {
         const uint32_t jn = j0 + (lane & 31u);
         const bool act = jn < nlist;
         const uint32_t g = uint32_t(s_list[act ? jn : j0]);
         float v[8];
         load_v(vrow, g, v);
-        bool amb;
-        const uint32_t bi = screen_group(a, v, c, lane, amb);
-        const uint64_t m = __ballot(act && amb && lane < 32u);
-        if (act && amb && lane < 32u) s_list[namb + __popcll(m & ((1ull << lane) - 1ull))] = uint16_t(g);
-        namb += uint32_t(__popcll(m));
-        if (act && !amb && lane < 32u) finish_group<WRITE>(a, v, bi, g, gbase, k64, s64, s_e);
-    }
-    wave_sync();
-    // near ties between tiles: exhaustive float64 search, one group per lane
-    for (uint32_t j0 = 0; j0 < namb; j0 += kWave) {
-        const uint32_t j = j0 + lane;
-        const bool act = j < namb;
-        const uint32_t g = act ? uint32_t(s_list[j]) : 0u;
-        float v[8];
-        load_v(vrow, g, v);
-        const uint32_t bi = exhaustive_search(a, v, c);
-        if (act) finish_group<WRITE>(a, v, bi, g, gbase, k64, s64, s_e);
+        const uint32_t bi = screen_group(a, v, c, lane);
+        if (act && lane < 32u) finish_group<WRITE>(a, v, bi, g, gbase, k64, s64, s_e);
     }
     wave_sync();
     // the row error in the fixed order
@@ -351,7 +327,7 @@ __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, dou
     return acc;
 }
 
-__global__ __launch_bounds__(kPtqWaves * kWave) void ptq_kernel(PtqArgs a) {
+__global__ __launch_bounds__(kPtqWaves * kWave, 4) void ptq_kernel(PtqArgs a) {
     extern __shared__ uint32_t s_dyn[];
     const uint32_t wv = threadIdx.x >> 6;
     const uint32_t lane = threadIdx.x & 63u;
