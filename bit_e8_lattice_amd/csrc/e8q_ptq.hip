@@ -18,11 +18,11 @@
 //     counts as +inf, ties go to the smaller k, a candidate with an invalid
 //     scale (the projection's bad-row rule) has error +inf.
 //
-// One wave per row.  The un-normalized transform v of the weights is computed
-// once (e8q_rotate.hpp) into the workspace.  Per candidate, the lanes stride
-// over the row's groups: the nearest E8 point and, for points inside the core,
-// the group error go to LDS; groups outside the core are listed (in group
-// order) and searched 32 at a time.  The search is a dense contraction (every
+// One block of four waves per row.  The un-normalized transform v of the
+// weights is computed once (e8q_rotate.hpp) into the workspace.  Per
+// candidate, the threads stride over the row's groups: the nearest E8 point
+// and, for points inside the core, the group error go to LDS; groups outside
+// the core are queued and searched 32 per wave at a time.  The search is a dense contraction (every
 // group against every core point), so it runs on the matrix cores: the core
 // points, sorted into norm shells and tiles of 32, meet a bfloat16 hi + mid
 // split of the groups in one 32x32x16 MFMA per tile, which screens the
@@ -36,7 +36,8 @@
 
 namespace e8q {
 
-constexpr int kPtqWaves = 2;   // waves (rows) per block
+constexpr int kPtqWaves = 4;   // waves per block; one block per row
+constexpr uint32_t kPtqThreads = kPtqWaves * kWave;
 
 struct PtqArgs {
     const float* v;            // [rows_total, cols] un-normalized rotated weights
@@ -63,14 +64,6 @@ struct PtqArgs {
     int8_t* two_z;
     uint32_t* status;
 };
-
-// Orders this wave's LDS accesses across lanes (a lane reads what another
-// lane of the same wave wrote).
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __device__ __forceinline__ double group_error(const float (&v)[8], const int (&t)[8], double k64, double s64) {
     double q[8];
@@ -269,14 +262,13 @@ __device__ __forceinline__ void finish_group(const PtqArgs& a, const float (&v)[
 // lane); with WRITE the points of the row are stored.
 template <bool WRITE>
 __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, double* s_e, uint16_t* s_list,
-                           uint32_t& flags) {
-    const uint32_t lane = threadIdx.x & 63u;
+                           uint32_t* s_cnt, uint32_t& flags) {
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
     const float* vrow = a.v + uint64_t(row) * a.cols;
     const double k64 = double(a.kappa), s64 = double(s);
     const uint64_t gbase = uint64_t(row) * a.gpr;
-    uint32_t nlist = 0;
-    for (uint32_t g0 = 0; g0 < a.gpr; g0 += kWave) {
-        const uint32_t g = g0 + lane;
+    for (uint32_t g0 = 0; g0 < a.gpr; g0 += kPtqThreads) {
+        const uint32_t g = g0 + tid;
         bool outside = false;
         if (g < a.gpr) {
             float v[8], x[8];
@@ -302,13 +294,17 @@ __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, dou
                 }
             }
         }
+        // the list is a work queue: its order does not affect any result
         const uint64_t m = __ballot(outside);
-        if (outside) s_list[nlist + __popcll(m & ((1ull << lane) - 1ull))] = uint16_t(g);
-        nlist += uint32_t(__popcll(m));
+        uint32_t base = 0;
+        if (lane == 0 && m) base = atomicAdd(s_cnt, uint32_t(__popcll(m)));
+        base = __shfl(base, 0, 64);
+        if (outside) s_list[base + __popcll(m & ((1ull << lane) - 1ull))] = uint16_t(g);
     }
-    wave_sync();
-    // groups outside the core, 32 at a time (lanes l and l + 32 share one)
-    for (uint32_t j0 = 0; j0 < nlist; j0 += kTileRows) {
+    __syncthreads();
+    const uint32_t nlist = *s_cnt;
+    // groups outside the core, 32 per wave at a time (lanes l and l + 32 share one)
+    for (uint32_t j0 = wv * kTileRows; j0 < nlist; j0 += kPtqWaves * kTileRows) {
         const uint32_t jn = j0 + (lane & 31u);
         const bool act = jn < nlist;
         const uint32_t g = uint32_t(s_list[act ? jn : j0]);
@@ -317,25 +313,26 @@ __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, dou
         const uint32_t bi = screen_group(a, v, c, lane);
         if (act && lane < 32u) finish_group<WRITE>(a, v, bi, g, gbase, k64, s64, s_e);
     }
-    wave_sync();
-    // the row error in the fixed order
+    __syncthreads();
+    if (tid == 0) *s_cnt = 0;
+    // the row error in the fixed order (every wave computes the same value)
     double acc = 0.0;
     for (uint32_t g = lane; g < a.gpr; g += kWave) acc = acc + s_e[g];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_xor(acc, off, 64);
-    wave_sync();   // the buffers are reused by the next candidate
+    __syncthreads();   // the buffers are reused by the next candidate
     return acc;
 }
 
-__global__ __launch_bounds__(kPtqWaves * kWave, 4) void ptq_kernel(PtqArgs a) {
+__global__ __launch_bounds__(kPtqThreads, 4) void ptq_kernel(PtqArgs a) {
     extern __shared__ uint32_t s_dyn[];
-    const uint32_t wv = threadIdx.x >> 6;
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t row = blockIdx.x * kPtqWaves + wv;
-    if (row >= a.rows_total) return;   // whole wave leaves; no block barrier below
-    double* s_e = reinterpret_cast<double*>(s_dyn) + size_t(wv) * a.gpr;
-    uint16_t* s_list = reinterpret_cast<uint16_t*>(reinterpret_cast<double*>(s_dyn) + size_t(kPtqWaves) * a.gpr) +
-                       size_t(wv) * a.gpr;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t row = blockIdx.x;
+    double* s_e = reinterpret_cast<double*>(s_dyn);
+    uint32_t* s_cnt = reinterpret_cast<uint32_t*>(s_e + a.gpr);
+    uint16_t* s_list = reinterpret_cast<uint16_t*>(s_cnt + 1);
+    if (tid == 0) *s_cnt = 0;
+    __syncthreads();
     const float s0 = a.s0[row];
     uint32_t flags = 0;
     double best = __builtin_inf();
@@ -345,8 +342,8 @@ __global__ __launch_bounds__(kPtqWaves * kWave, 4) void ptq_kernel(PtqArgs a) {
         bool bad;
         const float c = row_coef(s, a.kappa, bad);
         double e = __builtin_inf();
-        if (!bad) e = row_pass<false>(a, row, s, c, s_e, s_list, flags);
-        if (a.err_out && lane == 0) a.err_out[uint64_t(row) * uint32_t(a.n_alpha) + uint32_t(k)] = e;
+        if (!bad) e = row_pass<false>(a, row, s, c, s_e, s_list, s_cnt, flags);
+        if (a.err_out && tid == 0) a.err_out[uint64_t(row) * uint32_t(a.n_alpha) + uint32_t(k)] = e;
         const double key = e != e ? __builtin_inf() : e;
         if (key < best) {
             best = key;
@@ -360,15 +357,15 @@ __global__ __launch_bounds__(kPtqWaves * kWave, 4) void ptq_kernel(PtqArgs a) {
         // the projection's bad-row rule: every point is 0
         const int t0[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         const uint16_t zero_idx = uint16_t(core_rank(t0, a.tab, a.rp));
-        for (uint32_t g = lane; g < a.gpr; g += kWave) {
+        for (uint32_t g = tid; g < a.gpr; g += kPtqThreads) {
             *reinterpret_cast<uint2*>(a.two_z + (uint64_t(row) * a.gpr + g) * 8) = make_uint2(0u, 0u);
             a.core_idx[uint64_t(row) * a.gpr + g] = zero_idx;
         }
         flags |= E8Q_STATUS_BAD_SCALE;
     } else {
-        (void)row_pass<true>(a, row, s, c, s_e, s_list, flags);
+        (void)row_pass<true>(a, row, s, c, s_e, s_list, s_cnt, flags);
     }
-    if (lane == 0) {
+    if (tid == 0) {
         a.scale_out[row] = s;
         if (a.choice_out) a.choice_out[row] = kbest;
     }
@@ -406,7 +403,7 @@ extern "C" e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype, int64_t
         return E8Q_ERR_INVALID;
     const uint64_t rows_total = uint64_t(batch) * uint64_t(rows);
     const uint32_t gpr = uint32_t(cols / 8);
-    const size_t lds = size_t(kPtqWaves) * gpr * (8 + 2);
+    const size_t lds = size_t(gpr) * (8 + 2) + 4;
     if (lds > 64 * 1024 || rows_total >= (uint64_t(1) << 31)) return E8Q_ERR_UNSUPPORTED;
     const int hb = signs ? had_block : 0;
     const size_t rot_lds = (hb > 0 ? size_t(cols / 2) * 4 : 0) + (hb > 128 ? size_t(8 * kBlock) * 4 : 0);
@@ -457,7 +454,6 @@ extern "C" e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype, int64_t
     a.core_idx = core_idx_out;
     a.two_z = two_z_out;
     a.status = status_dev;
-    const unsigned grid = unsigned((rows_total + kPtqWaves - 1) / kPtqWaves);
-    hipLaunchKernelGGL(ptq_kernel, dim3(grid), dim3(kPtqWaves * kWave), lds, s, a);
+    hipLaunchKernelGGL(ptq_kernel, dim3(unsigned(rows_total)), dim3(kPtqThreads), lds, s, a);
     return launch_status();
 }
