@@ -36,7 +36,8 @@ bool upload(const std::vector<T>& v, T*& dptr) {
     return true;
 }
 // The tile tables of DevTable: shells ||t||^2 = 0, 8, 16, ... in increasing
-// norm, each in rank order, cut into tiles of kTileRows rows.
+// norm, each in rank order, cut into tiles of kTileRows rows (pads after the
+// shell's last point).
 std::vector<uint8_t> build_tiles(const CoreTable& c, uint32_t& ntiles) {
     auto coord = [&](int64_t i, int k) { return int((c.points[2 * i + k / 4] >> (8 * (k % 4))) & 0xFFu) - 64; };
     std::vector<std::vector<int64_t>> shells(size_t(c.bound / 8) + 1);
@@ -55,6 +56,12 @@ std::vector<uint8_t> build_tiles(const CoreTable& c, uint32_t& ntiles) {
         const size_t nt = (sh.size() + kTileRows - 1) / kTileRows;
         for (size_t j = 0; j < nt * kTileRows; ++j) rows.push_back(j < sh.size() ? sh[j] : -1);
         for (size_t j = 0; j < nt; ++j) n4.push_back(float(s * 8) / 4.0f);
+    }
+    // an even tile count (the search takes two tiles per step): a dummy tile
+    // of pads whose key can never be the best
+    if (n4.size() % 2) {
+        for (size_t j = 0; j < kTileRows; ++j) rows.push_back(-1);
+        n4.push_back(1e30f);
     }
     ntiles = uint32_t(n4.size());
     const size_t nt = ntiles;

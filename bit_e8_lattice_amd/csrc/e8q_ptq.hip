@@ -93,19 +93,6 @@ __device__ __forceinline__ float bf16_rne(float x) {
     return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
 }
 
-// The search key x.t - ||t||^2/4 in float64 in the fixed order: exact
-// products, pairwise sums, then the exact ||t||^2/4.
-__device__ __forceinline__ double exact_key(const double (&x64)[8], const int (&t)[8]) {
-    double q[8];
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        q[i] = x64[i] * double(t[i]);
-        n += t[i] * t[i];
-    }
-    return (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]))) - 0.25 * double(n);
-}
-
 __device__ __forceinline__ float tile_max(const f32x16_t& d) {
     float m = fmaxf(fmaxf(d[0], d[1]), d[2]);
     m = fmaxf(fmaxf(m, d[3]), d[4]);
@@ -117,28 +104,37 @@ __device__ __forceinline__ float tile_max(const f32x16_t& d) {
     return fmaxf(m, d[15]);
 }
 
-// Exact float64 keys of this lane's 16 rows of a tile (rows 8(r/4) + 4 half
-// + r%4, the rows an MFMA result holds for lane half `half`); the largest key
-// wins, ties to the lower core index.
+// Exact float64 keys of this lane's 16 rows of a tile (rows 8j + 4 half + q,
+// j, q < 4: the rows an MFMA result holds for lane half `half`); the largest
+// key wins, ties to the lower core index.  Every real row of a tile has the
+// tile's norm; a pad row (t = 0, the origin's index) gets key -||t||^2/4 of
+// its tile, which never reaches the best key unless the tile is the origin's
+// own (where it is the origin's exact key).
 __device__ __forceinline__ void eval_rows(const PtqArgs& a, const double (&x64)[8], uint32_t tile, uint32_t half,
                                           double& best, uint32_t& bi) {
-    const uint8_t* t8 = a.tiles + size_t(a.ntiles) * 512 + size_t(tile) * kTileRows * 8;
-    const uint16_t* ix = reinterpret_cast<const uint16_t*>(a.tiles + size_t(a.ntiles) * 768) + size_t(tile) * kTileRows;
+    const uint4* t8 = reinterpret_cast<const uint4*>(a.tiles + size_t(a.ntiles) * 512) + size_t(tile) * 16 + 2 * half;
+    const uint2* ix = reinterpret_cast<const uint2*>(a.tiles + size_t(a.ntiles) * 768) + size_t(tile) * 8 + half;
+    const double n4 = double(reinterpret_cast<const float*>(a.tiles + size_t(a.ntiles) * 832)[tile]);
 #pragma unroll 1
-    for (int r = 0; r < 16; ++r) {
-        const uint32_t row = 8u * uint32_t(r >> 2) + 4u * half + uint32_t(r & 3);
-        const uint2 w = *reinterpret_cast<const uint2*>(t8 + row * 8);
-        int t[8];
+    for (int j = 0; j < 4; ++j) {
+        // a run of four consecutive rows, loaded before any is used
+        const uint4 w0 = t8[4 * j], w1 = t8[4 * j + 1];
+        const uint2 id = ix[2 * j];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            t[i] = int(int8_t(w.x >> (8 * i)));
-            t[4 + i] = int(int8_t(w.y >> (8 * i)));
-        }
-        const double key = exact_key(x64, t);
-        const uint32_t idx = ix[row];
-        if (key > best || (key == best && idx < bi)) {
-            best = key;
-            bi = idx;
+        for (int q = 0; q < 4; ++q) {
+            const uint4 ww = (q >> 1) ? w1 : w0;
+            const uint32_t lo = (q & 1) ? ww.z : ww.x, hi = (q & 1) ? ww.w : ww.y;
+            double p[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = x64[i] * double(int(int8_t(lo >> (8 * i))));
+                p[4 + i] = x64[4 + i] * double(int(int8_t(hi >> (8 * i))));
+            }
+            const double key = (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) - n4;
+            const uint32_t idx = (((q >> 1) ? id.y : id.x) >> (16 * (q & 1))) & 0xFFFFu;
+            const bool better = key > best || (key == best && idx < bi);
+            best = better ? key : best;
+            bi = better ? idx : bi;
         }
     }
 }
@@ -184,29 +180,24 @@ __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (
     const uint32_t last = a.ntiles - 1u;
     float m1 = -__builtin_inff(), m2 = -__builtin_inff();
     uint32_t t1 = 0;
-    // two tiles per step, the next two tiles' points loaded ahead (the loads
-    // clamp to the last tile; a step past the end repeats it, which changes
-    // neither maximum)
-    bf16x8_t p0 = at[0], p1 = at[size_t(min(1u, last)) * kTileRows];
+    // two tiles per step (the tile count is even), the next two tiles'
+    // points loaded ahead (clamped to the last tile at the end)
+    bf16x8_t p0 = at[0], p1 = at[kTileRows];
     for (uint32_t tile = 0; tile < a.ntiles; tile += 2) {
-        const uint32_t tb = min(tile + 1u, last);
         const f32x16_t d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p0, b, zero, 0, 0, 0);
         const f32x16_t d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p1, b, zero, 0, 0, 0);
-        p0 = at[size_t(min(tile + 2u, last)) * kTileRows];
+        p0 = at[size_t(min(tile + 2u, last - 1u)) * kTileRows];
         p1 = at[size_t(min(tile + 3u, last)) * kTileRows];
         // keep the loads of the next step ahead of this step's reductions
         __builtin_amdgcn_sched_barrier(0);
         const float k0 = tile_max(d0) - n4t[tile];
-        const float k1 = tile_max(d1) - n4t[tb];
+        const float k1 = tile_max(d1) - n4t[tile + 1u];
         m2 = __builtin_amdgcn_fmed3f(m1, m2, k0);
         t1 = k0 > m1 ? tile : t1;
         m1 = fmaxf(m1, k0);
-        // a repeated last tile must not count as a second tile
-        if (tb != tile) {
-            m2 = __builtin_amdgcn_fmed3f(m1, m2, k1);
-            t1 = k1 > m1 ? tb : t1;
-            m1 = fmaxf(m1, k1);
-        }
+        m2 = __builtin_amdgcn_fmed3f(m1, m2, k1);
+        t1 = k1 > m1 ? tile + 1u : t1;
+        m1 = fmaxf(m1, k1);
     }
     // combine the two halves of the tile rows (values of half 0 first)
     const float om1 = __shfl_xor(m1, 32, 64), om2 = __shfl_xor(m2, 32, 64);
