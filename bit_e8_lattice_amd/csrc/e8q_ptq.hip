@@ -55,6 +55,7 @@ struct PtqArgs {
     uint32_t ntiles;
     float tmax;                // largest |t_i| of a core point (bound)
     float nmax4;               // B / 4
+    float big;                 // above every approximate key (3e38)
     const uint16_t* tab;
     RankParams rp;
     float* scale_out;
@@ -93,15 +94,18 @@ __device__ __forceinline__ float bf16_rne(float x) {
     return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ float tile_max(const f32x16_t& d) {
-    float m = fmaxf(fmaxf(d[0], d[1]), d[2]);
-    m = fmaxf(fmaxf(m, d[3]), d[4]);
-    m = fmaxf(fmaxf(m, d[5]), d[6]);
-    m = fmaxf(fmaxf(m, d[7]), d[8]);
-    m = fmaxf(fmaxf(m, d[9]), d[10]);
-    m = fmaxf(fmaxf(m, d[11]), d[12]);
-    m = fmaxf(fmaxf(m, d[13]), d[14]);
-    return fmaxf(m, d[15]);
+// Largest of the 16 values.  max(a, b) is taken as med3(a, b, big) with
+// big > every value (a kernel argument, so that it is not folded back into a
+// plain max, which would quiet NaNs of the raw MFMA results first).
+__device__ __forceinline__ float tile_max(const f32x16_t& d, float big) {
+    float m = __builtin_amdgcn_fmed3f(d[0], d[1], big);
+    m = fmaxf(fmaxf(m, d[2]), d[3]);
+    m = fmaxf(fmaxf(m, d[4]), d[5]);
+    m = fmaxf(fmaxf(m, d[6]), d[7]);
+    m = fmaxf(fmaxf(m, d[8]), d[9]);
+    m = fmaxf(fmaxf(m, d[10]), d[11]);
+    m = fmaxf(fmaxf(m, d[12]), d[13]);
+    return fmaxf(fmaxf(m, d[14]), d[15]);
 }
 
 // Exact float64 keys of this lane's 16 rows of a tile (rows 8j + 4 half + q,
@@ -190,14 +194,14 @@ __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (
         p1 = at[size_t(min(tile + 3u, last)) * kTileRows];
         // keep the loads of the next step ahead of this step's reductions
         __builtin_amdgcn_sched_barrier(0);
-        const float k0 = tile_max(d0) - n4t[tile];
-        const float k1 = tile_max(d1) - n4t[tile + 1u];
+        const float k0 = tile_max(d0, a.big) - n4t[tile];
+        const float k1 = tile_max(d1, a.big) - n4t[tile + 1u];
         m2 = __builtin_amdgcn_fmed3f(m1, m2, k0);
         t1 = k0 > m1 ? tile : t1;
-        m1 = fmaxf(m1, k0);
+        m1 = __builtin_amdgcn_fmed3f(m1, k0, a.big);
         m2 = __builtin_amdgcn_fmed3f(m1, m2, k1);
         t1 = k1 > m1 ? tile + 1u : t1;
-        m1 = fmaxf(m1, k1);
+        m1 = __builtin_amdgcn_fmed3f(m1, k1, a.big);
     }
     // combine the two halves of the tile rows (values of half 0 first)
     const float om1 = __shfl_xor(m1, 32, 64), om2 = __shfl_xor(m2, 32, 64);
@@ -223,7 +227,7 @@ __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (
         const float thr = top - 3.0f * eps;
         for (uint32_t tile = 0; tile < a.ntiles; ++tile) {
             const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at[size_t(tile) * kTileRows], b, zero, 0, 0, 0);
-            const float k = tile_max(d) - n4t[tile];
+            const float k = tile_max(d, a.big) - n4t[tile];
             if (amb && tile != ts && k >= thr) eval_rows(a, x64, tile, half, best, bi);
         }
     }
@@ -437,6 +441,7 @@ extern "C" e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype, int64_t
     a.ntiles = tab->ntiles;
     a.tmax = floorf(sqrtf(float(core_bound)));
     a.nmax4 = float(core_bound) / 4.0f;
+    a.big = 3.0e38f;
     a.tab = tab->dptr;
     a.rp = tab->host.p;
     a.scale_out = scale_out;
