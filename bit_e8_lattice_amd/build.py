@@ -31,9 +31,10 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-# Per-source additions.  The PTQ search keeps its MFMA accumulators in
-# ordinary VGPRs (no copies out of the accumulation registers per tile).
-SOURCE_FLAGS = {"e8q_ptq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions.  The PTQ search and the GEMV keep their MFMA
+# accumulators in ordinary VGPRs (no copies out of the accumulation registers).
+SOURCE_FLAGS = {"e8q_ptq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "e8q_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

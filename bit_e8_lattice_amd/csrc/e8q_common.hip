@@ -120,14 +120,24 @@ const DevTable* get_table(int32_t bound, e8q_status_t& err) {
         p64[size_t(i) * 9 + 8] = n / 4.0;
     }
     std::vector<uint8_t> tiles = build_tiles(t.host, t.ntiles);
-    if (!upload(roots, t.droots) || !upload(p64, t.dpts64) || !upload(tiles, t.dtiles)) {
+    std::vector<uint16_t> pbf((size_t(t.host.size) + 1) * 8, 0);
+    for (size_t i = 0; i < size_t(t.host.size) * 8; ++i) {
+        const float f = float(p64[(i / 8) * 9 + i % 8]);
+        uint32_t u;
+        std::memcpy(&u, &f, 4);
+        pbf[i] = uint16_t(u >> 16);   // small integers are exact in bf16
+    }
+    uint16_t* dpbf = nullptr;
+    if (!upload(roots, t.droots) || !upload(p64, t.dpts64) || !upload(tiles, t.dtiles) || !upload(pbf, dpbf)) {
         (void)hipFree(t.dptr);
         (void)hipFree(t.dpoints);
         if (t.droots) (void)hipFree(t.droots);
         if (t.dpts64) (void)hipFree(t.dpts64);
+        if (t.dtiles) (void)hipFree(t.dtiles);
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }
+    t.dpts_bf16 = reinterpret_cast<uint4*>(dpbf);
     auto res = g_tabs->emplace(key, std::move(t));
     return &res.first->second;
 }

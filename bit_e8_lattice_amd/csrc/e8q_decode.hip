@@ -575,8 +575,268 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
     flush_status(flags, a.status);
 }
 
+// ---------------------------------------------------------------------------
+// The GEMV on the matrix cores (rows of a multiple of 32 groups, 16-byte
+// aligned indices).  One 16x16x32 bf16 MFMA takes 16 rows x 4 groups:
+//   A (16 x 32): the rows' points of the four groups, read from a table that
+//     holds every core point's 2z as 8 bfloat16 (exact: |2z| <= 12); entry
+//     npts is the zero point, taken by escaped and malformed slots;
+//   B (32 x 16): the same groups' activations split as x~ = hi + mid + lo
+//     (bfloat16, round to nearest even; |x~ - hi - mid - lo| <= 2^-24 |x~|),
+//     column 3v + p holding part p of vector v, columns >= 3M zero;
+//   D[i][3v + p] = the row's 32 products with part p, each product exact.
+// Lane l holds row l % 16 of the tile in A and column l % 16 in B and D (D row
+// 4 (l / 16) + r in element r).  A wave walks its 16 rows in chunks of 32
+// groups: lane quarter q = l / 16 loads the 16-byte index word of groups
+// 32c + 8q ... 32c + 8q + 7 (a whole 64-byte row segment per four lanes), and
+// step s of the chunk puts group 32c + 8q + s in K slice q (the order of the
+// groups along K is free).  Index words are loaded three chunks ahead, also
+// across the wave's tiles.  Every step's MFMA starts from 0; the
+// steps are added in float32 in order, 16 steps (512 columns) per partial
+// sum, the partials in order.  Escaped and malformed slots are added per lane
+// in float32 (2z . x~, the same partial scheme).
+constexpr uint32_t kGmRows = 16;
+
+typedef __bf16 gm_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
+
+struct GemvMfmaArgs {
+    const uint16_t* core_idx;
+    const uint32_t* esc;
+    const uint64_t* offsets;
+    const float* xt;           // [batch, m, cols] x~ (float32), for the escaped slots
+    const uint4* xb;           // [batch, m, 3, gpr] x~ parts hi, mid, lo (8 bf16 per group)
+    const float* scale;
+    const uint4* tab;          // [npts + 1] points as 8 bf16 (entry npts: zero)
+    uint32_t npts;
+    uint32_t rows;
+    uint32_t gpr;
+    uint32_t tiles_per_b;      // ceil(rows / 16)
+    uint32_t tiles;            // batch * tiles_per_b
+    float* y;
+    uint32_t* status;
+};
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+}
+
+// x~ parts: per group, hi, mid and lo as 8 bf16 each ([batch, m, 3, gpr]).
+__global__ __launch_bounds__(256) void gemv_split_kernel(const float* xt, uint4* xb, uint32_t gpr, uint32_t groups) {
+    for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < groups; g += gridDim.x * 256u) {
+        const float4* src = reinterpret_cast<const float4*>(xt + uint64_t(g) * 8);
+        const float4 x0 = src[0], x1 = src[1];
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t h[8], m[8], l[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t hb = bf16_rne_bits(x[i]);
+            const float d = x[i] - __uint_as_float(hb);          // exact
+            const uint32_t mb = bf16_rne_bits(d);
+            const float e = d - __uint_as_float(mb);             // exact
+            h[i] = hb >> 16;
+            m[i] = mb >> 16;
+            l[i] = bf16_rne_bits(e) >> 16;
+        }
+        const uint32_t vec = g / gpr, gi = g - vec * gpr;
+        uint4* dst = xb + uint64_t(vec) * 3 * gpr + gi;
+        dst[0] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        dst[gpr] = make_uint4(m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16));
+        dst[2 * gpr] =
+            make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+    }
+}
+
+// The float32 contribution of an escaped or malformed slot, per vector.
+template <int M>
+__device__ __forceinline__ void gm_special(const GemvMfmaArgs& a, uint32_t b, uint32_t row, uint32_t g, uint32_t idx,
+                                           bool row_ok, float* sp, uint32_t& flags) {
+    int tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (idx != 0xFFFFu) {
+        if (row_ok) flags |= E8Q_STATUS_BAD_INDEX;
+    } else if (!find_record(a.esc, a.offsets, b, row * a.gpr + g, tb)) {
+        if (row_ok) flags |= E8Q_STATUS_ESC_MISSING;
+    }
+#pragma unroll
+    for (int v = 0; v < M; ++v) {
+        const float* xv = a.xt + ((uint64_t(b) * M + v) * a.gpr + g) * 8;
+        float s0 = float(tb[0]) * xv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) s0 = fmaf(float(tb[i]), xv[i], s0);
+        sp[v] += s0;
+    }
+}
+
+// LDS accesses of one wave, ordered across its lanes.
+__device__ __forceinline__ void gm_wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Work units: (batch item, kWaves consecutive tiles); each wave takes one
+// tile of a unit, a block a contiguous range of units (so its waves read
+// neighbouring rows and, with X_LDS, share one batch item's activation parts,
+// staged in LDS when the item changes).
+template <int M, bool LDS_TAB, bool X_LDS>
+__global__ __launch_bounds__(X_LDS ? 1024 : 512) void gemv_mfma_kernel(GemvMfmaArgs a) {
+    constexpr uint32_t kWaves = X_LDS ? 16u : 8u;
+    constexpr uint32_t kThreads = kWaves * kWave;
+    extern __shared__ uint4 s_gm[];
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+    const uint32_t tab_n = LDS_TAB ? a.npts + 1u : 0u;
+    const uint32_t xs_n = X_LDS ? uint32_t(M) * 3u * a.gpr : 0u;
+    uint4* s_x = s_gm + tab_n;
+    float* s_red = reinterpret_cast<float*>(s_gm + tab_n + xs_n) + wv * (256u + 64u * M);
+    if constexpr (LDS_TAB) {
+        for (uint32_t i = tid; i <= a.npts; i += kThreads) s_gm[i] = a.tab[i];
+        __syncthreads();
+    }
+    const uint4* tab = LDS_TAB ? s_gm : a.tab;
+    const uint32_t i16 = lane & 15u, q = lane >> 4;
+    const uint32_t nc = a.gpr >> 5;                 // chunks of 32 groups per row
+    const uint32_t vcol = i16 / 3u, pcol = i16 - 3u * vcol;
+    const bool bcol = i16 < 3u * M;
+    const gm_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t flags = 0;
+
+    const uint32_t units_per_b = (a.tiles_per_b + kWaves - 1u) / kWaves;
+    const uint32_t units = (a.tiles / a.tiles_per_b) * units_per_b;
+    const uint32_t per = (units + gridDim.x - 1u) / gridDim.x;
+    const uint32_t u_begin = min(blockIdx.x * per, units), u_end = min(u_begin + per, units);
+    // this wave's tile of unit u (within its batch item), or tiles_per_b
+    const auto wave_tile = [&](uint32_t u) { return (u % units_per_b) * kWaves + wv; };
+    const auto row_words = [&](uint32_t u) {
+        const uint32_t bb = u / units_per_b;
+        const uint32_t rr = min(wave_tile(u) * kGmRows + i16, a.rows - 1u);
+        return reinterpret_cast<const uint4*>(a.core_idx + (uint64_t(bb) * a.rows + rr) * a.gpr) + q;
+    };
+    // the index words run three chunks ahead, on across this wave's tiles
+    // (past its last tile the pipeline re-reads words it already has)
+    uint32_t pf_u = u_begin, pf_c = 0;
+    while (pf_u < u_end && wave_tile(pf_u) >= a.tiles_per_b) ++pf_u;
+    const uint4* pf_ip = pf_u < u_end ? row_words(pf_u) : reinterpret_cast<const uint4*>(a.core_idx) + q;
+    const auto next_word = [&]() {
+        const uint4 w = pf_ip[4u * pf_c];
+        if (++pf_c == nc) {
+            pf_c = 0;
+            if (pf_u < u_end) {
+                do ++pf_u; while (pf_u < u_end && wave_tile(pf_u) >= a.tiles_per_b);
+                if (pf_u < u_end) pf_ip = row_words(pf_u);
+            }
+        }
+        return w;
+    };
+    uint4 w0 = next_word(), w1 = next_word(), w2 = next_word();
+    uint32_t staged = 0xFFFFFFFFu;
+    for (uint32_t u = u_begin; u < u_end; ++u) {
+        const uint32_t b = u / units_per_b;
+        if constexpr (X_LDS) {
+            if (b != staged) {   // block-uniform
+                __syncthreads();
+                const uint4* src = a.xb + uint64_t(b) * xs_n;
+                for (uint32_t i = tid; i < xs_n; i += kThreads) s_x[i] = src[i];
+                __syncthreads();
+                staged = b;
+            }
+        }
+        const uint32_t t = wave_tile(u);
+        if (t >= a.tiles_per_b) continue;
+        const uint32_t r0 = t * kGmRows;
+        const bool row_ok = r0 + i16 < a.rows;
+        const uint32_t row = row_ok ? r0 + i16 : a.rows - 1u;   // rows past the end repeat the last
+        // this lane's activation part
+        const uint32_t xoff = ((bcol ? vcol : 0u) * 3u + (bcol ? pcol : 0u)) * a.gpr + 8u * q;
+        const uint4* xp = X_LDS ? s_x + xoff : a.xb + uint64_t(b) * M * 3u * a.gpr + xoff;
+        gm_f32x4 acc1 = zero, acc2 = zero;
+        float sp1[M], sp2[M];
+#pragma unroll
+        for (int v = 0; v < M; ++v) sp1[v] = sp2[v] = 0.0f;
+        for (uint32_t c = 0; c < nc; ++c) {
+            const uint4 w = w0;
+            w0 = w1;
+            w1 = w2;
+            w2 = next_word();
+            // only the 3M lanes of real columns load (the others hold zeros)
+            uint4 xc[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) xc[s] = make_uint4(0u, 0u, 0u, 0u);
+            if (bcol) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) xc[s] = xp[32u * c + uint32_t(s)];
+            }
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+            uint32_t idx[8];
+            bool any = false;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                idx[s] = (wd[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
+                any = any || idx[s] >= a.npts;
+            }
+            if (__ballot(any)) {
+                // rare: one copy of the slow path, stepping through the word
+#pragma unroll 1
+                for (uint32_t s = 0; s < 8; ++s) {
+                    const uint32_t h = s >> 1;
+                    const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
+                    const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
+                    if (id >= a.npts) gm_special<M>(a, b, row, 32u * c + 8u * q + s, id, row_ok, sp1, flags);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint4 pt = tab[min(idx[s], a.npts)];
+                const gm_f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(gm_bf16x8, pt), __builtin_bit_cast(gm_bf16x8, xc[s]), zero, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc1[r] = acc1[r] + d[r];
+            }
+            if ((c & 1u) == 1u || c + 1u == nc) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc2[r] = acc2[r] + acc1[r];
+                acc1 = zero;
+#pragma unroll
+                for (int v = 0; v < M; ++v) {
+                    sp2[v] = sp2[v] + sp1[v];
+                    sp1[v] = 0.0f;
+                }
+            }
+        }
+        // D (16 rows x 16 columns) and the four lane quarters' escaped-slot sums
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_red[(4u * q + uint32_t(r)) * 16u + i16] = acc2[r];
+#pragma unroll
+        for (int v = 0; v < M; ++v) s_red[256u + (q * M + uint32_t(v)) * 16u + i16] = sp2[v];
+        gm_wave_sync();
+        if (lane < kGmRows && r0 + lane < a.rows) {
+            const uint32_t r = r0 + lane;
+            const float s = a.scale[uint64_t(b) * a.rows + r];
+            const bool bad = !(s > 0.0f) || __builtin_isinf(s);
+            if (bad) flags |= E8Q_STATUS_BAD_SCALE;
+            const float* d = s_red + lane * 16u;
+            const float* e = s_red + 256u + lane;
+#pragma unroll
+            for (int v = 0; v < M; ++v) {
+                const float dv = (d[3 * v] + d[3 * v + 1]) + d[3 * v + 2];
+                const float ev =
+                    (e[(0 * M + v) * 16] + e[(1 * M + v) * 16]) + (e[(2 * M + v) * 16] + e[(3 * M + v) * 16]);
+                a.y[(uint64_t(b) * M + uint32_t(v)) * a.rows + r] = bad ? 0.0f : (0.5f * s) * (dv + ev);
+            }
+        }
+        gm_wave_sync();
+    }
+    flush_status(flags, a.status);
+}
+
+static size_t gemv_xt_bytes(int64_t batch, int64_t m, int64_t cols) {
+    return (size_t(batch) * size_t(m) * size_t(cols) * 4 + 255) & ~size_t(255);
+}
+
+// offsets, x~ (float32), x~ parts (3 x 8 bf16 per group)
 static size_t gemv_ws_bytes(int64_t batch, int64_t m, int64_t cols) {
-    return decode_ws_bytes(batch) + ((size_t(batch) * size_t(m) * size_t(cols) * 4 + 255) & ~size_t(255));
+    return decode_ws_bytes(batch) + gemv_xt_bytes(batch, m, cols) +
+           ((size_t(batch) * size_t(m) * size_t(cols / 8) * 48 + 255) & ~size_t(255));
 }
 
 template <int M>
@@ -585,6 +845,24 @@ static void launch_gemv(bool lds_pts, const GemvArgs& a, dim3 grid, size_t lds, 
         hipLaunchKernelGGL((gemv_kernel<M, true>), grid, dim3(kGemvThreads), lds, st, a);
     else
         hipLaunchKernelGGL((gemv_kernel<M, false>), grid, dim3(kGemvThreads), lds, st, a);
+}
+
+template <int M>
+static void launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t st) {
+    const size_t tab = size_t(a.npts + 1) * 16;
+    const size_t xs = size_t(M) * 3 * a.gpr * 16;
+    const size_t red16 = 16 * (256 + 64 * M) * 4, red8 = 8 * (256 + 64 * M) * 4;
+    const uint64_t tiles_per_b = a.tiles_per_b, batch = a.tiles / a.tiles_per_b;
+    if (tab + xs + red16 <= 160 * 1024) {
+        const uint64_t units = batch * ((tiles_per_b + 15) / 16);
+        launch_tiles(gemv_mfma_kernel<M, true, true>, a, units, 1024, tab + xs + red16, st);
+    } else {
+        const uint64_t units = batch * ((tiles_per_b + 7) / 8);
+        if (tab <= 48 * 1024)
+            launch_tiles(gemv_mfma_kernel<M, true, false>, a, units, 512, tab + red8, st);
+        else
+            launch_tiles(gemv_mfma_kernel<M, false, false>, a, units, 512, red8, st);
+    }
 }
 
 }  // namespace e8q
@@ -649,6 +927,34 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
         launch_rotate<uint16_t>(hb, ra, rot_lds, s);
     else
         launch_rotate<float>(hb, ra, rot_lds, s);
+
+    const uint32_t gpr = uint32_t(cols / 8);
+    const uint64_t tiles = uint64_t(batch) * uint64_t((rows + kGmRows - 1) / kGmRows);
+    if (gpr % 32 == 0 && (reinterpret_cast<uintptr_t>(core_idx) & 15u) == 0 && tiles < (uint64_t(1) << 32)) {
+        // the matrix-core path
+        uint4* xb = reinterpret_cast<uint4*>(reinterpret_cast<char*>(xt) + gemv_xt_bytes(batch, m, cols));
+        const uint32_t xg = uint32_t(uint64_t(batch) * uint64_t(m) * gpr);
+        hipLaunchKernelGGL(gemv_split_kernel, dim3(grid_for(xg, 256, 8)), dim3(256), 0, s, xt, xb, gpr, xg);
+        GemvMfmaArgs gm;
+        gm.core_idx = core_idx;
+        gm.esc = reinterpret_cast<const uint32_t*>(esc);
+        gm.offsets = offsets;
+        gm.xt = xt;
+        gm.xb = xb;
+        gm.scale = row_scale;
+        gm.tab = tab->dpts_bf16;
+        gm.npts = uint32_t(tab->host.size);
+        gm.rows = uint32_t(rows);
+        gm.gpr = gpr;
+        gm.tiles_per_b = uint32_t((rows + kGmRows - 1) / kGmRows);
+        gm.tiles = uint32_t(tiles);
+        gm.y = y_out;
+        gm.status = status_dev;
+        if (m == 1) launch_gemv_mfma<1>(gm, s);
+        else if (m == 2) launch_gemv_mfma<2>(gm, s);
+        else launch_gemv_mfma<4>(gm, s);
+        return launch_status();
+    }
 
     GemvArgs ga;
     ga.core_idx = core_idx;

@@ -32,6 +32,9 @@ struct DevTable {
     //   ntiles * 832 : the shell's ||t||^2 / 4 as float        4 B per tile
     uint8_t* dtiles = nullptr;
     uint32_t ntiles = 0;
+    // The points in rank order as 8 bfloat16 (2z) each, plus a zero entry at
+    // index |C(B)| (the GEMV's matrix-core operand table).
+    uint4* dpts_bf16 = nullptr;
     CoreTable host;
 };
 

@@ -309,9 +309,13 @@ size_t e8q_decode_workspace_size(int64_t batch);
  *   x            [batch, m, cols] activations, x_dtype F32 or BF16; m in {1, 2, 4}
  *   y_out        [batch, m, rows] float32
  *   workspace    e8q_gemv_workspace_size(batch, m, cols) bytes, 256-byte aligned
- * Rounding: |y - W_hat x| <= 2 (L + G + 17) 2^-24 S_r per output, L = log2(b),
- * G = ceil(cols / 512), S_r = s_r sum_g sum_i |z_gi| xbar_gi, xbar = kappa_b
- * times the block sums of |x| (|x| itself without rotation).
+ * Rows whose column count is a multiple of 64, with 16-byte aligned core_idx,
+ * run on the matrix cores (x~ split into three bfloat16 parts, exact products,
+ * float32 sums whose order inside one MFMA is the hardware's); other shapes
+ * use float32 FMA chains.  Rounding, either way: |y - W_hat x| <=
+ * 2 (L + G + 66) 2^-24 S_r + 2^-120 s_r sum_g sum_i |z_gi| per output,
+ * L = log2(b), G = ceil(cols / 512), S_r = s_r sum_g sum_i |z_gi| xbar_gi,
+ * xbar = kappa_b times the block sums of |x| (|x| itself without rotation).
  * Limits: m * cols * 4 <= 96 KiB, batch <= 65535.  Malformed exports and bad
  * scales are flagged as in e8q_decode_core_escape (a bad row gives y = 0).
  * ------------------------------------------------------------------------- */

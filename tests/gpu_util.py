@@ -170,11 +170,14 @@ def run_gemv(core, esc, cnt, shape, bound, s, x, signs=None, hb=0, esc_records=N
 
 
 def gemv_tolerance(two_z, s, x_vals, signs, hb, cols):
-    """The documented float32 bound 2 (L + G + 17) 2^-24 S_r of the GEMV."""
+    """The documented bound 2 (L + G + 66) 2^-24 S_r + 2^-120 s_r sum|z| of
+    the GEMV (both of its evaluation orders)."""
     L = int(np.log2(hb)) if hb else 0
     G = -(-cols // 512)
     S = oracle.rotated_magnitude(two_z, s, x_vals, signs, hb)
-    return 2.0 * (L + G + 17) * 2.0 ** -24 * S
+    tz = np.asarray(two_z, dtype=np.float64)
+    z1 = np.abs(tz).sum(-1) * 0.5 * np.asarray(s, dtype=np.float64).reshape(tz.shape[0], tz.shape[1])
+    return 2.0 * (L + G + 66) * 2.0 ** -24 * S + 2.0 ** -120 * z1[:, None, :]
 
 
 def run_ptq(w, s0, alphas, bound, signs=None, hb=0):

@@ -1,6 +1,8 @@
 """GPU GEMV from the exported form against the float64 product of the exact
-restored weights, within the documented float32 bound (the evaluation order is
-the kernel's own, so the bar is a derived tolerance, not bit equality)."""
+restored weights, within the documented bound (the evaluation order is the
+kernel's own, so the bar is a derived tolerance, not bit equality).  Rows of
+a multiple of 64 columns with 16-byte aligned indices take the matrix-core
+kernel; other shapes and alignments the vector kernel."""
 
 import numpy as np
 import pytest
@@ -115,3 +117,54 @@ def test_gemv_dense_decoder_shapes():
             _check(o, tz, sm, x[mi:mi + 1], sn, 128, cols)
         del enc, core, esc, cnt
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_gemv_vector_path_shapes(m):
+    """Rows whose group count is not a multiple of 8 (1000 columns), and a
+    16-byte misaligned index pointer: the vector kernel."""
+    d = device()
+    shape = (2, 37, 1000)
+    w = workloads.normal(shape, 1750 + m, d)
+    s = workloads.rms_scale(w, 1.0)
+    sg = workloads.signs(1000, 1751, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 8, 16)
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((2, m, 1000), 1752 + m, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 8)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 8, 1000)
+    # the same 2048-column export through a misaligned copy of its indices
+    shape = (1, 9, 2048)
+    w = workloads.normal(shape, 1760 + m, d)
+    s = workloads.rms_scale(w, 1.0)
+    sg = workloads.signs(2048, 1761, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, 16)
+    core, esc, cnt = upload_export(enc, d)
+    buf = torch.empty(core.numel() + 1, dtype=core.dtype, device=d)
+    buf[1:].copy_(core)
+    x = _x((1, m, 2048), 1762 + m, d)
+    out = run_gemv(buf[1:], esc, cnt, shape, 16, s, x, sg, 128)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, 2048)
+
+
+@pytest.mark.parametrize("m,cols", [(4, 4096), (2, 11008)])
+def test_gemv_activation_parts_from_global(m, cols):
+    """Shapes whose activation parts do not fit in LDS next to the point table
+    (four vectors of 4096 columns, two of 11008): the matrix-core kernel reads
+    them from global memory."""
+    d = device()
+    shape = (2, 45, cols)
+    w = workloads.normal(shape, 1770 + m, d)
+    s = workloads.rms_scale(w, 2.0)
+    sg = workloads.signs(cols, 1771, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, 16)
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((2, m, cols), 1772 + m, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, cols)
