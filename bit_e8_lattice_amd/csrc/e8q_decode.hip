@@ -590,12 +590,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
 // groups: lane quarter q = l / 16 loads the 16-byte index word of groups
 // 32c + 8q ... 32c + 8q + 7 (a whole 64-byte row segment per four lanes), and
 // step s of the chunk puts group 32c + 8q + s in K slice q (the order of the
-// groups along K is free).  Index words are loaded three chunks ahead, also
+// groups along K is free).  Index words are loaded five chunks ahead, also
 // across the wave's tiles.  Every step's MFMA starts from 0; the
 // steps are added in float32 in order, 16 steps (512 columns) per partial
 // sum, the partials in order.  Escaped and malformed slots are added per lane
 // in float32 (2z . x~, the same partial scheme).
 constexpr uint32_t kGmRows = 16;
+constexpr int kGmAhead = 5;   // index words (chunks) loaded ahead
 
 typedef __bf16 gm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
@@ -680,7 +681,7 @@ __device__ __forceinline__ void gm_wave_sync() {
 // neighbouring rows and, with X_LDS, share one batch item's activation parts,
 // staged in LDS when the item changes).
 template <int M, bool LDS_TAB, bool X_LDS>
-__global__ __launch_bounds__(X_LDS ? 1024 : 512) void gemv_mfma_kernel(GemvMfmaArgs a) {
+__global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMfmaArgs a) {
     constexpr uint32_t kWaves = X_LDS ? 16u : 8u;
     constexpr uint32_t kThreads = kWaves * kWave;
     extern __shared__ uint4 s_gm[];
@@ -712,7 +713,7 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512) void gemv_mfma_kernel(GemvMfmaA
         const uint32_t rr = min(wave_tile(u) * kGmRows + i16, a.rows - 1u);
         return reinterpret_cast<const uint4*>(a.core_idx + (uint64_t(bb) * a.rows + rr) * a.gpr) + q;
     };
-    // the index words run three chunks ahead, on across this wave's tiles
+    // the index words run kGmAhead chunks ahead, on across this wave's tiles
     // (past its last tile the pipeline re-reads words it already has)
     uint32_t pf_u = u_begin, pf_c = 0;
     while (pf_u < u_end && wave_tile(pf_u) >= a.tiles_per_b) ++pf_u;
@@ -728,15 +729,28 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512) void gemv_mfma_kernel(GemvMfmaA
         }
         return w;
     };
-    uint4 w0 = next_word(), w1 = next_word(), w2 = next_word();
+    uint4 wq[kGmAhead];
+#pragma unroll
+    for (int k = 0; k < kGmAhead; ++k) wq[k] = next_word();
     uint32_t staged = 0xFFFFFFFFu;
+    uint4 xc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) xc[s] = make_uint4(0u, 0u, 0u, 0u);
     for (uint32_t u = u_begin; u < u_end; ++u) {
         const uint32_t b = u / units_per_b;
         if constexpr (X_LDS) {
             if (b != staged) {   // block-uniform
                 __syncthreads();
+                // staged in step order: entry ((8c + s) 4 + q) 3M + n holds column
+                // n's part for group 32c + 8q + s, so that the lanes of one
+                // step read consecutive entries (no bank conflicts)
                 const uint4* src = a.xb + uint64_t(b) * xs_n;
-                for (uint32_t i = tid; i < xs_n; i += kThreads) s_x[i] = src[i];
+                for (uint32_t i = tid; i < xs_n; i += kThreads) {
+                    const uint32_t n = i % (3u * M), rest = i / (3u * M);
+                    const uint32_t qq = rest & 3u, cs = rest >> 2;
+                    const uint32_t g = 32u * (cs >> 3) + 8u * qq + (cs & 7u);
+                    s_x[i] = src[n * a.gpr + g];
+                }
                 __syncthreads();
                 staged = b;
             }
@@ -746,25 +760,25 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512) void gemv_mfma_kernel(GemvMfmaA
         const uint32_t r0 = t * kGmRows;
         const bool row_ok = r0 + i16 < a.rows;
         const uint32_t row = row_ok ? r0 + i16 : a.rows - 1u;   // rows past the end repeat the last
-        // this lane's activation part
-        const uint32_t xoff = ((bcol ? vcol : 0u) * 3u + (bcol ? pcol : 0u)) * a.gpr + 8u * q;
-        const uint4* xp = X_LDS ? s_x + xoff : a.xb + uint64_t(b) * M * 3u * a.gpr + xoff;
+        // this lane's activation part: step s of chunk c at xp[32c + s] (global,
+        // [batch, m, 3, gpr]) or at xp[(32c + 4s) 3M] (LDS, step order)
+        const uint4* xp = X_LDS ? s_x + (q * 3u * M + i16)
+                                : a.xb + uint64_t(b) * M * 3u * a.gpr + (bcol ? i16 : 0u) * a.gpr + 8u * q;
         gm_f32x4 acc1 = zero, acc2 = zero;
         float sp1[M], sp2[M];
 #pragma unroll
         for (int v = 0; v < M; ++v) sp1[v] = sp2[v] = 0.0f;
         for (uint32_t c = 0; c < nc; ++c) {
-            const uint4 w = w0;
-            w0 = w1;
-            w1 = w2;
-            w2 = next_word();
-            // only the 3M lanes of real columns load (the others hold zeros)
-            uint4 xc[8];
+            const uint4 w = wq[0];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) xc[s] = make_uint4(0u, 0u, 0u, 0u);
+            for (int k = 0; k + 1 < kGmAhead; ++k) wq[k] = wq[k + 1];
+            wq[kGmAhead - 1] = next_word();
+            // only the 3M lanes of real columns load (the D columns of the
+            // others are never read)
             if (bcol) {
 #pragma unroll
-                for (int s = 0; s < 8; ++s) xc[s] = xp[32u * c + uint32_t(s)];
+                for (int s = 0; s < 8; ++s)
+                    xc[s] = X_LDS ? xp[(32u * c + 4u * uint32_t(s)) * 3u * M] : xp[32u * c + uint32_t(s)];
             }
             const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
             uint32_t idx[8];
