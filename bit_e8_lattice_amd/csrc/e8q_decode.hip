@@ -764,6 +764,8 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
         // [batch, m, 3, gpr]) or at xp[(32c + 4s) 3M] (LDS, step order)
         const uint4* xp = X_LDS ? s_x + (q * 3u * M + i16)
                                 : a.xb + uint64_t(b) * M * 3u * a.gpr + (bcol ? i16 : 0u) * a.gpr + 8u * q;
+        // the row scale of lane (row) l < 16, loaded now and used at the end
+        const float s_row = a.scale[uint64_t(b) * a.rows + min(r0 + (lane & 15u), a.rows - 1u)];
         gm_f32x4 acc1 = zero, acc2 = zero;
         float sp1[M], sp2[M];
 #pragma unroll
@@ -825,7 +827,7 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
         gm_wave_sync();
         if (lane < kGmRows && r0 + lane < a.rows) {
             const uint32_t r = r0 + lane;
-            const float s = a.scale[uint64_t(b) * a.rows + r];
+            const float s = s_row;
             const bool bad = !(s > 0.0f) || __builtin_isinf(s);
             if (bad) flags |= E8Q_STATUS_BAD_SCALE;
             const float* d = s_red + lane * 16u;

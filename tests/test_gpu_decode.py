@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _cmp(out, ref, q=None, w_hat=None):
-    assert first_mismatch(out["two_z_i8"], ref["two_z_i8"]) is None
+    if "two_z_i8" in out:
+        assert first_mismatch(out["two_z_i8"], ref["two_z_i8"]) is None
     if q is not None:
         key = "q_bf16" if q == torch.bfloat16 else "q_f32"
         want = ref[key] if q == torch.bfloat16 else ref[key].view(np.uint32)
@@ -142,3 +143,53 @@ def test_device_encode_then_decode_matches_projection():
         assert first_mismatch(out["w_hat"], full["w_hat"]) is None
         del enc, core, esc, cnt, out, full
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bound", [0, 16, 40])
+@pytest.mark.parametrize("alpha", [1.0, 3.0])
+def test_decode_restore_only(bound, alpha):
+    """Restored weights as the only output with 128-wide blocks (point table
+    in LDS, and in global memory for C(40)); alpha 1 escapes most groups."""
+    d = device()
+    shape = (3, 37, 512)
+    w = workloads.normal(shape, 1600 + bound, d)
+    s = workloads.rms_scale(w, alpha)
+    sg = workloads.signs(512, 1601, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, bound)
+    ref = oracle.decode_outputs(enc["core_idx"], enc["records"], enc["counts"], bound, shape,
+                                s.cpu().numpy(), sn, 128)
+    core, esc, cnt = upload_export(enc, d)
+    for wd in (torch.bfloat16, torch.float32):
+        out = run_decode(core, esc, cnt, shape, bound, s, sg, 128, two_z=False, w_hat_dtype=wd)
+        _cmp(out, ref, None, wd)
+
+
+def test_decode_restore_only_large_escapes_and_malformed():
+    """Restored weights only, with escaped points far outside bfloat16's exact
+    integers (|2z| > 256), an index past the core, a missing record and
+    invalid row scales."""
+    d = device()
+    shape = (2, 21, 256)
+    w = workloads.normal(shape, 1610, d, dtype=torch.float32)
+    s = workloads.rms_scale(w, 1.0)
+    s = s * 0.004                              # |x| ~ 2000 after the rotation
+    sg = workloads.signs(256, 1611, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, 16, w_is_bf16=False)
+    assert np.abs(enc["two_z"]).max() > 256
+    core_np = enc["core_idx"].copy()
+    k = int(np.nonzero(core_np != oracle.ESCAPE_SLOT)[0][0]) if (core_np != oracle.ESCAPE_SLOT).any() else 0
+    core_np[k] = oracle.core_size(16) + 3
+    s_bad = s.clone()
+    s_bad[4] = float("nan")
+    s_bad[30] = -1.0
+    recs = enc["records"][:-4]
+    bad_enc = {"core_idx": core_np, "records": recs, "counts": enc["counts"]}
+    ref = oracle.decode_outputs(core_np, recs, enc["counts"], 16, shape, s_bad.cpu().numpy(), sn, 128,
+                                want_two_z=False)
+    assert ref["status"] == (oracle.STATUS_ESC_MISSING | oracle.STATUS_BAD_INDEX | oracle.STATUS_BAD_SCALE)
+    core, esc, cnt = upload_export(bad_enc, d)
+    for wd in (torch.bfloat16, torch.float32):
+        out = run_decode(core, esc, cnt, shape, 16, s_bad, sg, 128, two_z=False, w_hat_dtype=wd)
+        _cmp(out, ref, None, wd)
