@@ -168,3 +168,21 @@ def test_gemv_activation_parts_from_global(m, cols):
     out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
     assert out["status"] == 0
     _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, cols)
+
+
+@pytest.mark.parametrize("rows", [1, 3, 17])
+def test_gemv_matrix_core_few_rows(rows):
+    """Fewer rows than one tile (and one past a tile): the lanes of missing
+    rows repeat the last row and write nothing."""
+    d = device()
+    shape = (2, rows, 256)
+    w = workloads.normal(shape, 1780 + rows, d)
+    s = workloads.rms_scale(w, 1.0)
+    sg = workloads.signs(256, 1781, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, 16)
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((2, 2, 256), 1782 + rows, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, 256)
