@@ -3,6 +3,7 @@
 #include <cstddef>
 #include <cstring>
 #include <map>
+#include <unordered_map>
 #include <mutex>
 
 #include "e8q_core_table.hpp"
@@ -36,17 +37,30 @@ bool upload(const std::vector<T>& v, T*& dptr) {
     return true;
 }
 // The tile tables of DevTable: shells ||t||^2 = 0, 8, 16, ... in increasing
-// norm, each in rank order, cut into tiles of kTileRows rows (pads after the
-// shell's last point).
+// norm; of each pair +-t only t with its first nonzero coordinate positive
+// (the origin alone in its shell), in rank order, cut into tiles of kTileRows
+// rows (pads after the shell's last point); each row also names the core
+// index of -t.
 std::vector<uint8_t> build_tiles(const CoreTable& c, uint32_t& ntiles) {
     auto coord = [&](int64_t i, int k) { return int((c.points[2 * i + k / 4] >> (8 * (k % 4))) & 0xFFu) - 64; };
+    auto key = [](const int (&t)[8]) {
+        uint64_t k = 0;
+        for (int i = 0; i < 8; ++i) k = (k << 8) | uint64_t(uint8_t(t[i] + 64));
+        return k;
+    };
+    std::unordered_map<uint64_t, int64_t> where;
     std::vector<std::vector<int64_t>> shells(size_t(c.bound / 8) + 1);
     int64_t origin = -1;
     for (int64_t i = 0; i < c.size; ++i) {
-        int n = 0;
-        for (int k = 0; k < 8; ++k) n += coord(i, k) * coord(i, k);
-        shells[size_t(n / 8)].push_back(i);
+        int t[8], n = 0, first = 0;
+        for (int k = 0; k < 8; ++k) {
+            t[k] = coord(i, k);
+            n += t[k] * t[k];
+            if (first == 0) first = t[k];
+        }
+        where[key(t)] = i;
         if (n == 0) origin = i;
+        if (first >= 0) shells[size_t(n / 8)].push_back(i);   // the origin, or t with first nonzero > 0
     }
     std::vector<int64_t> rows;    // -1 = pad
     std::vector<float> n4;
@@ -65,21 +79,27 @@ std::vector<uint8_t> build_tiles(const CoreTable& c, uint32_t& ntiles) {
     }
     ntiles = uint32_t(n4.size());
     const size_t nt = ntiles;
-    std::vector<uint8_t> out(nt * 836, 0);
+    std::vector<uint8_t> out(nt * 900, 0);
     uint16_t* bf = reinterpret_cast<uint16_t*>(out.data());
     int8_t* t8 = reinterpret_cast<int8_t*>(out.data() + nt * 512);
-    uint16_t* idx = reinterpret_cast<uint16_t*>(out.data() + nt * 768);
-    float* nf = reinterpret_cast<float*>(out.data() + nt * 832);
+    uint16_t* ipos = reinterpret_cast<uint16_t*>(out.data() + nt * 768);
+    uint16_t* ineg = reinterpret_cast<uint16_t*>(out.data() + nt * 832);
+    float* nf = reinterpret_cast<float*>(out.data() + nt * 896);
     for (size_t r = 0; r < rows.size(); ++r) {
         const int64_t i = rows[r];
-        idx[r] = uint16_t(i < 0 ? origin : i);
+        int t[8], m[8];
         for (int k = 0; k < 8; ++k) {
-            const int v = i < 0 ? 0 : coord(i, k);
-            const float f = float(v);
+            t[k] = i < 0 ? 0 : coord(i, k);
+            m[k] = -t[k];
+        }
+        ipos[r] = uint16_t(i < 0 ? origin : i);
+        ineg[r] = uint16_t(i < 0 ? origin : where.at(key(m)));
+        for (int k = 0; k < 8; ++k) {
+            const float f = float(t[k]);
             uint32_t u;
             std::memcpy(&u, &f, 4);
             bf[r * 8 + k] = uint16_t(u >> 16);   // small integers are exact in bf16
-            t8[r * 8 + k] = int8_t(v);
+            t8[r * 8 + k] = int8_t(t[k]);
         }
     }
     std::memcpy(nf, n4.data(), nt * 4);

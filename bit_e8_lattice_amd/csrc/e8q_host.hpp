@@ -23,13 +23,16 @@ struct DevTable {
     uint32_t* droots = nullptr;   // the 240 roots (same word layout as the points)
     double* dpts64 = nullptr;     // points in rank order as 9 doubles: t_0..t_7 (= 2z), ||t||^2 / 4
     // The points grouped by norm shell into tiles of 32 rows for the
-    // matrix-core search; a shell's last tile is padded with zero rows, and
-    // an odd tile count gets one more tile of pads with norm 1e30 (its key is
-    // never the best).  Per tile, at these offsets (in tiles of ntiles):
+    // matrix-core search, one of each pair +-t (first nonzero coordinate
+    // positive; the origin alone); a shell's last tile is padded with zero
+    // rows, and an odd tile count gets one more tile of pads with norm 1e30
+    // (its key is never the best).  Per tile, at these offsets (in tiles of
+    // ntiles):
     //   0            : 32 rows x 8 bf16 (t = 2z)            512 B per tile
     //   ntiles * 512 : 32 rows x 8 int8 (t)                 256 B per tile
-    //   ntiles * 768 : 32 uint16 core indices (pads: the origin's)  64 B per tile
-    //   ntiles * 832 : the shell's ||t||^2 / 4 as float        4 B per tile
+    //   ntiles * 768 : 32 uint16 core indices of t (pads: the origin's)  64 B
+    //   ntiles * 832 : 32 uint16 core indices of -t (pads: the origin's) 64 B
+    //   ntiles * 896 : the shell's ||t||^2 / 4 as float        4 B per tile
     uint8_t* dtiles = nullptr;
     uint32_t ntiles = 0;
     // The points in rank order as 8 bfloat16 (2z) each, plus a zero entry at

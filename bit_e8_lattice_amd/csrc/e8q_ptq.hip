@@ -94,36 +94,41 @@ __device__ __forceinline__ float bf16_rne(float x) {
     return __uint_as_float((u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u);
 }
 
-// Largest of the 16 values.  max(a, b) is taken as med3(a, b, big) with
-// big > every value (a kernel argument, so that it is not folded back into a
-// plain max, which would quiet NaNs of the raw MFMA results first).
+// Largest of the 16 magnitudes |d_i| (a row holds t, and -t has dot product
+// -d: |d| screens the better of the two).  max(a, b) is taken as med3(a, b,
+// big) with big > every value (a kernel argument, so that it is not folded
+// back into a plain max, which would quiet NaNs of the raw MFMA results
+// first).
 __device__ __forceinline__ float tile_max(const f32x16_t& d, float big) {
-    float m = __builtin_amdgcn_fmed3f(d[0], d[1], big);
-    m = fmaxf(fmaxf(m, d[2]), d[3]);
-    m = fmaxf(fmaxf(m, d[4]), d[5]);
-    m = fmaxf(fmaxf(m, d[6]), d[7]);
-    m = fmaxf(fmaxf(m, d[8]), d[9]);
-    m = fmaxf(fmaxf(m, d[10]), d[11]);
-    m = fmaxf(fmaxf(m, d[12]), d[13]);
-    return fmaxf(fmaxf(m, d[14]), d[15]);
+    float m = __builtin_amdgcn_fmed3f(fabsf(d[0]), fabsf(d[1]), big);
+    m = fmaxf(fmaxf(m, fabsf(d[2])), fabsf(d[3]));
+    m = fmaxf(fmaxf(m, fabsf(d[4])), fabsf(d[5]));
+    m = fmaxf(fmaxf(m, fabsf(d[6])), fabsf(d[7]));
+    m = fmaxf(fmaxf(m, fabsf(d[8])), fabsf(d[9]));
+    m = fmaxf(fmaxf(m, fabsf(d[10])), fabsf(d[11]));
+    m = fmaxf(fmaxf(m, fabsf(d[12])), fabsf(d[13]));
+    return fmaxf(fmaxf(m, fabsf(d[14])), fabsf(d[15]));
 }
 
 // Exact float64 keys of this lane's 16 rows of a tile (rows 8j + 4 half + q,
-// j, q < 4: the rows an MFMA result holds for lane half `half`); the largest
-// key wins, ties to the lower core index.  Every real row of a tile has the
+// j, q < 4: the rows an MFMA result holds for lane half `half`), each for t
+// and for -t: with S the oracle's pairwise sum of x_i t_i, the key of -t is
+// exactly -S - ||t||^2/4 (negation commutes with rounding).  The largest key
+// wins, ties to the lower core index.  Every real row of a tile has the
 // tile's norm; a pad row (t = 0, the origin's index) gets key -||t||^2/4 of
 // its tile, which never reaches the best key unless the tile is the origin's
 // own (where it is the origin's exact key).
 __device__ __forceinline__ void eval_rows(const PtqArgs& a, const double (&x64)[8], uint32_t tile, uint32_t half,
                                           double& best, uint32_t& bi) {
     const uint4* t8 = reinterpret_cast<const uint4*>(a.tiles + size_t(a.ntiles) * 512) + size_t(tile) * 16 + 2 * half;
-    const uint2* ix = reinterpret_cast<const uint2*>(a.tiles + size_t(a.ntiles) * 768) + size_t(tile) * 8 + half;
-    const double n4 = double(reinterpret_cast<const float*>(a.tiles + size_t(a.ntiles) * 832)[tile]);
+    const uint2* ip = reinterpret_cast<const uint2*>(a.tiles + size_t(a.ntiles) * 768) + size_t(tile) * 8 + half;
+    const uint2* in = reinterpret_cast<const uint2*>(a.tiles + size_t(a.ntiles) * 832) + size_t(tile) * 8 + half;
+    const double n4 = double(reinterpret_cast<const float*>(a.tiles + size_t(a.ntiles) * 896)[tile]);
 #pragma unroll 1
     for (int j = 0; j < 4; ++j) {
         // a run of four consecutive rows, loaded before any is used
         const uint4 w0 = t8[4 * j], w1 = t8[4 * j + 1];
-        const uint2 id = ix[2 * j];
+        const uint2 idp = ip[2 * j], idn = in[2 * j];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint4 ww = (q >> 1) ? w1 : w0;
@@ -134,11 +139,17 @@ __device__ __forceinline__ void eval_rows(const PtqArgs& a, const double (&x64)[
                 p[i] = x64[i] * double(int(int8_t(lo >> (8 * i))));
                 p[4 + i] = x64[4 + i] * double(int(int8_t(hi >> (8 * i))));
             }
-            const double key = (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) - n4;
-            const uint32_t idx = (((q >> 1) ? id.y : id.x) >> (16 * (q & 1))) & 0xFFFFu;
-            const bool better = key > best || (key == best && idx < bi);
-            best = better ? key : best;
-            bi = better ? idx : bi;
+            const double sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            const double kp = sum - n4, kn = -sum - n4;
+            const uint32_t sh = 16u * uint32_t(q & 1);
+            const uint32_t xp = (((q >> 1) ? idp.y : idp.x) >> sh) & 0xFFFFu;
+            const uint32_t xn = (((q >> 1) ? idn.y : idn.x) >> sh) & 0xFFFFu;
+            bool better = kp > best || (kp == best && xp < bi);
+            best = better ? kp : best;
+            bi = better ? xp : bi;
+            better = kn > best || (kn == best && xn < bi);
+            best = better ? kn : best;
+            bi = better ? xn : bi;
         }
     }
 }
@@ -147,9 +158,10 @@ __device__ __forceinline__ void eval_rows(const PtqArgs& a, const double (&x64)[
 // the group of column l % 32).  x = v*c is split as x = hi + mid + r with hi,
 // mid bfloat16; one 32x32x16 MFMA per tile of 32 core points computes
 // t.hi + t.mid for every (point, group) pair, lanes < 32 feeding hi and lanes
-// >= 32 mid against the same points.  Each lane keeps, over the tiles, the
-// largest approximate key of its 16 rows (M1, in tile T1) and the largest of
-// the other tiles (M2).  The approximate keys are within eps of the float64
+// >= 32 mid against the same points.  The tiles hold one point of each pair
+// +-t, so |t.x| - ||t||^2/4 screens both.  Each lane keeps, over the tiles,
+// the largest approximate key of its 16 rows (M1, in tile T1) and the largest
+// of the other tiles (M2).  The approximate keys are within eps of the float64
 // keys:
 //   eps = tmax * sum|r_i| + 2^-18 * (tmax * sum|x_i| + B/4)
 // (|t_i| <= tmax; the products are exact in float32 and the sum of 16
@@ -157,7 +169,7 @@ __device__ __forceinline__ void eval_rows(const PtqArgs& a, const double (&x64)[
 // relative each).  A point whose approximate key is below best - 3 eps has a
 // float64 key below that of the best tile's best point, so only tiles within
 // 3 eps of the best can hold the winner.  The two lanes evaluate the best
-// tile's 32 rows exactly; if another tile comes within 3 eps (a near tie), a
+// tile's 32 rows (64 points) exactly; if another tile comes within 3 eps (a near tie), a
 // second sweep evaluates every such tile too.  The largest float64 key wins,
 // ties to the lower core index.
 __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (&v)[8], float c, uint32_t lane) {
@@ -179,7 +191,7 @@ __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (
     const float eps = 1.01f * (a.tmax * rsum + 0x1p-18f * (a.tmax * xsum + a.nmax4)) + 1e-30f;
 
     const bf16x8_t* at = reinterpret_cast<const bf16x8_t*>(a.tiles) + (lane & 31u);
-    const const_fptr n4t = (const_fptr)(uintptr_t)(a.tiles + size_t(a.ntiles) * 832);
+    const const_fptr n4t = (const_fptr)(uintptr_t)(a.tiles + size_t(a.ntiles) * 896);
     const f32x16_t zero = {};
     const uint32_t last = a.ntiles - 1u;
     float m1 = -__builtin_inff(), m2 = -__builtin_inff();
