@@ -140,16 +140,16 @@ __device__ __forceinline__ void eval_rows(const PtqArgs& a, const double (&x64)[
                 p[4 + i] = x64[4 + i] * double(int(int8_t(hi >> (8 * i))));
             }
             const double sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            const double kp = sum - n4, kn = -sum - n4;
+            // the better of t (key sum - n4) and -t (key -sum - n4): |sum| - n4,
+            // from t if sum > 0, from -t if sum < 0, the lower index if sum = 0
+            const double key = fabs(sum) - n4;
             const uint32_t sh = 16u * uint32_t(q & 1);
             const uint32_t xp = (((q >> 1) ? idp.y : idp.x) >> sh) & 0xFFFFu;
             const uint32_t xn = (((q >> 1) ? idn.y : idn.x) >> sh) & 0xFFFFu;
-            bool better = kp > best || (kp == best && xp < bi);
-            best = better ? kp : best;
-            bi = better ? xp : bi;
-            better = kn > best || (kn == best && xn < bi);
-            best = better ? kn : best;
-            bi = better ? xn : bi;
+            const uint32_t idx = sum > 0.0 ? xp : sum < 0.0 ? xn : min(xp, xn);
+            const bool better = key > best || (key == best && idx < bi);
+            best = better ? key : best;
+            bi = better ? idx : bi;
         }
     }
 }
