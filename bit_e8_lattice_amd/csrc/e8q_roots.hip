@@ -9,7 +9,9 @@
 // 20-byte record in a second list.
 //
 // Both directions are one pass over the records in blocks of 1024 (the root
-// search is a loop over the 240 roots held in LDS; records are sparse), then
+// search is a loop over the 240 roots held in LDS as int16 pairs, the test
+// ||t - 2r||^2 <= B taken as 2 t.(2r) >= ||t||^2 + 8 - B with four packed
+// int16 dot products per root; records are sparse), then
 // an exclusive scan of the per-block counts of wide records, then a pass that
 // places the wide records in record order.
 #include "e8q_device.hpp"
@@ -67,11 +69,19 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 
 // Pack: root search and core index per record, packed record out, count of
 // records that need a wide record per block.
+typedef short rt_short2 __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(kRootThreads) void pack_kernel(RootArgs a) {
-    __shared__ uint32_t s_roots[480];
+    // the roots as 2r in int16 pairs (four words per root)
+    __shared__ uint32_t s_r16[960];
     __shared__ uint32_t s_scan[kRootThreads];
     const uint32_t tid = threadIdx.x;
-    for (uint32_t i = tid; i < 480u; i += kRootThreads) s_roots[i] = a.roots[i];
+    for (uint32_t i = tid; i < 960u; i += kRootThreads) {
+        const uint32_t w = a.roots[2u * (i >> 2) + ((i >> 1) & 1u)];
+        const uint32_t sh = 16u * (i & 1u);   // bytes 2i', 2i'+1 of the word pair
+        const int lo = int((w >> sh) & 0xFFu) - 64, hi = int((w >> (sh + 8u)) & 0xFFu) - 64;
+        s_r16[i] = (uint32_t(lo) & 0xFFFFu) | (uint32_t(hi) << 16);
+    }
     __syncthreads();
     const uint64_t base = uint64_t(blockIdx.x) * kRootBlock + uint64_t(tid) * kRootPer;
     uint32_t nwide = 0;
@@ -79,30 +89,42 @@ __global__ __launch_bounds__(kRootThreads) void pack_kernel(RootArgs a) {
         const uint64_t i = base + k;
         if (i >= a.n) break;
         const uint32_t* r = a.esc + i * 5;
+        // 2z as int16 pairs, as the record stores it
+        const uint32_t w[4] = {r[1], r[2], r[3], r[4]};
         int t[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t wv = r[1 + q];
-            t[2 * q] = int(int16_t(uint16_t(wv & 0xFFFFu)));
-            t[2 * q + 1] = int(int16_t(uint16_t(wv >> 16)));
+            t[2 * q] = int(int16_t(uint16_t(w[q] & 0xFFFFu)));
+            t[2 * q + 1] = int(int16_t(uint16_t(w[q] >> 16)));
         }
+        uint32_t nt = 0;   // ||t||^2 < 8 * 16386^2 < 2^32
+#pragma unroll
+        for (int q = 0; q < 8; ++q) nt += uint32_t(t[q] * t[q]);
+        // ||t - 2r||^2 = ||t||^2 - 2 t.(2r) + 8 <= B  <=>  2 t.(2r) >= ||t||^2 + 8 - B;
+        // |t.(2r)| <= 8 * 16386 (2r is (+-2, +-2, 0, ...) or (+-1, ...)), so a
+        // larger threshold admits no root
+        const int64_t need = int64_t(nt) + 8 - int64_t(a.core_bound);
         uint32_t root = 0xFFu, core = 0xFFFFu;
-        for (uint32_t j = 0; j < 240u; ++j) {
-            int rr[8];
-            bytes_to_ints(s_roots[2 * j], s_roots[2 * j + 1], rr);
-            int64_t nrm = 0;
+        if (need <= 2 * 131088) {
+            const int th = int(need);
+            for (uint32_t j = 0; j < 240u; ++j) {
+                const uint32_t* rr = s_r16 + 4u * j;
+                int dot = 0;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int64_t d = int64_t(t[q]) - rr[q];
-                nrm += d * d;
-            }
-            if (nrm <= a.core_bound) {
-                int c[8];
+                for (int q = 0; q < 4; ++q)
+                    dot = __builtin_amdgcn_sdot2(__builtin_bit_cast(rt_short2, w[q]), __builtin_bit_cast(rt_short2, rr[q]),
+                                                 dot, false);
+                if (2 * dot >= th) {
+                    int c[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) c[q] = t[q] - rr[q];
-                root = j;
-                core = core_rank(c, a.tab, a.rp);
-                break;
+                    for (int q = 0; q < 4; ++q) {
+                        c[2 * q] = t[2 * q] - int(int16_t(uint16_t(rr[q] & 0xFFFFu)));
+                        c[2 * q + 1] = t[2 * q + 1] - int(int16_t(uint16_t(rr[q] >> 16)));
+                    }
+                    root = j;
+                    core = core_rank(c, a.tab, a.rp);
+                    break;
+                }
             }
         }
         a.packed[2 * i] = r[0];
