@@ -225,16 +225,6 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
                 s_cnt[j * kWaves + wv] = uint32_t(__popcll(mask));
                 s_ball[j][wv] = mask;
             }
-            if (mask) {
-                const uint32_t b = live ? fdiv(g, a.gpb_div) : 0u;
-                const uint32_t b0 = __shfl(b, 0, 64);
-                const bool uniform = __ballot(live && b != b0) == 0;
-                if (uniform) {
-                    if (lane == 0) atomicAdd(a.esc_count + b0, (unsigned long long)__popcll(mask));
-                } else if (escaped) {
-                    atomicAdd(a.esc_count + b, 1ull);
-                }
-            }
         }
         flush_status(flags, a.status);
         __syncthreads();
@@ -251,6 +241,27 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
             }
             s_cnt[lane] = incl - c;
             const unsigned long long total = __shfl(incl, 63, 64);
+            // Escape counts per batch item: one atomic for a tile inside one
+            // item, else one per (slice, item) pair. Slice `lane` holds groups
+            // tile * kTileGroups + 64 * lane + [0, 64) in logical lane order.
+            {
+                const uint32_t t0g = tile * kTileGroups;
+                const uint32_t bfirst = fdiv(t0g, a.gpb_div);
+                if (bfirst == fdiv(min(t0g + (kTileGroups - 1u), glast), a.gpb_div)) {
+                    if (lane == 0 && total != 0ull) atomicAdd(a.esc_count + bfirst, total);
+                } else if (c != 0u) {
+                    uint64_t lm = logical_lane_mask(s_ball[lane / kWaves][lane % kWaves]);
+                    const uint32_t gs = t0g + 64u * lane;
+                    while (lm) {
+                        const uint32_t first = uint32_t(__ffsll((unsigned long long)lm) - 1);
+                        const uint32_t b = fdiv(gs + first, a.gpb_div);
+                        const uint32_t end = (b + 1u) * a.gpb_div.d - gs;
+                        const uint64_t sel = end >= 64u ? lm : (lm & ((1ull << end) - 1ull));
+                        atomicAdd(a.esc_count + b, (unsigned long long)__popcll(sel));
+                        lm &= ~sel;
+                    }
+                }
+            }
             unsigned long long excl = 0;
             bool timeout = false;
             if (tile == 0) {

@@ -182,3 +182,17 @@ def test_tail_lanes_with_an_escaped_last_group(bound):
     ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), None, 0, bound, w_is_bf16=False)
     assert ref["core_idx"][-1] == oracle.ESCAPE_SLOT
     _compare(out, ref)
+
+
+@pytest.mark.parametrize("shape", [(5000, 1, 8), (1500, 3, 8), (900, 1, 72), (250, 37, 8)])
+def test_many_small_batch_items(shape):
+    """Batch items of 1 to 37 groups: tiles and 64-group slices span many
+    items, so the per-item escape counts are split inside one tile."""
+    d = device()
+    w = workloads.normal(shape, 31 * shape[0] + shape[2], d)
+    s = workloads.rms_scale(w, 1.0)
+    for bound in (0, 16):
+        out = run_encode(w, s, bound)
+        ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), None, 0, bound)
+        _compare(out, ref)
+        assert out["counts"].sum() > shape[0] // 4
