@@ -91,6 +91,8 @@ __device__ __forceinline__ bool find_record(const uint32_t* esc, const uint64_t*
     return false;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint32_t bf16x2_rne_dec(float lo, float hi) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     typedef float float2_t __attribute__((ext_vector_type(2)));
@@ -160,7 +162,10 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
             ns[j] = need_s ? a.scale[fdiv(gn, a.gpr_div)] : 0.0f;
         }
     };
-    if (blockIdx.x < a.num_tiles) load_tile(blockIdx.x);
+    // The loads are unconditional (indices past the end read the last group):
+    // a conditional prefetch merges old and new values at the branch and the
+    // merge waits for the loads at once.
+    load_tile(blockIdx.x);
     for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
         uint32_t cidx[kItems];
         float cs[kItems];
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
             cidx[j] = nidx[j];
             cs[j] = ns[j];
         }
-        if (tile + gridDim.x < a.num_tiles) load_tile(tile + gridDim.x);
+        load_tile(tile + gridDim.x);
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
             const uint32_t g = tile * kTileGroups + uint32_t(j) * kBlock + lpos;
@@ -237,7 +242,9 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
                     p.y = bf16x2_rne_dec(q[2], q[3]);
                     p.z = bf16x2_rne_dec(q[4], q[5]);
                     p.w = bf16x2_rne_dec(q[6], q[7]);
-                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.q) + uint64_t(g) * 8) = p;
+                    // streamed out, never read back here: nontemporal
+                    const u32x4 pv = {p.x, p.y, p.z, p.w};
+                    __builtin_nontemporal_store(pv, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.q) + uint64_t(g) * 8));
                 } else {
                     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.q) + uint64_t(g) * 8);
                     dst[0] = make_float4(q[0], q[1], q[2], q[3]);
@@ -312,8 +319,11 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
 template <bool RESTORE, bool LDS_PTS>
 static void launch_decode(int hb, const DecodeArgs& a, size_t lds, hipStream_t st) {
     if constexpr (!RESTORE) {
-        // without the restore the block size plays no part
-        launch_tiles(decode_kernel<8, false, LDS_PTS>, a, a.num_tiles, kBlock, lds, st);
+        // Without the restore the block size plays no part, and a block's set-up
+        // is one copy of the point table: one block per tile (the hardware
+        // dispatcher keeps every CU full) decodes faster than resident blocks
+        // that loop over tiles.
+        hipLaunchKernelGGL((decode_kernel<8, false, LDS_PTS>), dim3(a.num_tiles), dim3(kBlock), lds, st, a);
         return;
     }
     switch (hb) {
