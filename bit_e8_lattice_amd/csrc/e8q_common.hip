@@ -147,13 +147,28 @@ const DevTable* get_table(int32_t bound, e8q_status_t& err) {
         std::memcpy(&u, &f, 4);
         pbf[i] = uint16_t(u >> 16);   // small integers are exact in bf16
     }
+    std::vector<uint32_t> h8(size_t(t.host.size) * 2, 0u);
+    for (int64_t i = 0; i < t.host.size; ++i) {
+        int v[8];
+        for (int k = 0; k < 8; ++k) v[k] = int(p64[size_t(i) * 9 + k]);
+        for (int h = 1; h < 8; h <<= 1)
+            for (int k = 0; k < 8; ++k)
+                if ((k & h) == 0) {
+                    const int a = v[k], b = v[k + h];
+                    v[k] = a + b;
+                    v[k + h] = a - b;
+                }
+        for (int k = 0; k < 8; ++k) h8[size_t(i) * 2 + k / 4] |= (uint32_t(v[k]) & 0xFFu) << (8 * (k % 4));
+    }
     uint16_t* dpbf = nullptr;
-    if (!upload(roots, t.droots) || !upload(p64, t.dpts64) || !upload(tiles, t.dtiles) || !upload(pbf, dpbf)) {
+    if (!upload(roots, t.droots) || !upload(p64, t.dpts64) || !upload(tiles, t.dtiles) || !upload(pbf, dpbf) ||
+        !upload(h8, t.dh8)) {
         (void)hipFree(t.dptr);
         (void)hipFree(t.dpoints);
         if (t.droots) (void)hipFree(t.droots);
         if (t.dpts64) (void)hipFree(t.dpts64);
         if (t.dtiles) (void)hipFree(t.dtiles);
+        if (dpbf) (void)hipFree(dpbf);
         err = E8Q_ERR_DEVICE;
         return nullptr;
     }

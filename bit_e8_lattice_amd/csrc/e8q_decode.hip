@@ -32,6 +32,7 @@ struct DecodeArgs {
     const int8_t* signs;
     uint32_t cols;
     const uint32_t* pts;          // point table (global copy)
+    const uint32_t* h8;           // H_8 (2z) of the points as signed bytes
     uint32_t npts;
     int8_t* two_z;
     void* q;
@@ -121,26 +122,8 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     if constexpr (LDS_PTS) {
         if (need_2z)
             for (uint32_t i = tid; i < 2u * a.npts; i += kBlock) s_pts[i] = a.pts[i];
-        if constexpr (RESTORE) {
-            for (uint32_t i = tid; i < a.npts; i += kBlock) {
-                float h[8];
-                const uint32_t w0 = a.pts[2u * i], w1 = a.pts[2u * i + 1u];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    h[k] = float(int((w0 >> (8 * k)) & 0xFFu) - 64);
-                    h[4 + k] = float(int((w1 >> (8 * k)) & 0xFFu) - 64);
-                }
-                fwht_inlane<8>(h);   // exact: small integers
-                uint32_t o0 = 0, o1 = 0;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    o0 |= (uint32_t(int(h[k])) & 0xFFu) << (8 * k);
-                    o1 |= (uint32_t(int(h[4 + k])) & 0xFFu) << (8 * k);
-                }
-                s_h8[2u * i] = o0;
-                s_h8[2u * i + 1u] = o1;
-            }
-        }
+        if constexpr (RESTORE)
+            for (uint32_t i = tid; i < 2u * a.npts; i += kBlock) s_h8[i] = a.h8[i];
     }
     if constexpr (RESTORE || LDS_PTS) __syncthreads();
     const uint32_t* pts = LDS_PTS ? s_pts : a.pts;
@@ -316,6 +299,16 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     }
 }
 
+// The restore's blocks loop over 16 tiles each (at least one block per resident
+// slot): more blocks than fit at once balance the CUs better than resident
+// blocks, and 16 tiles amortize a block's table set-up.
+template <typename K>
+static void launch_restore(K kernel, const DecodeArgs& a, size_t lds, hipStream_t st) {
+    const uint64_t resident = resident_grid(reinterpret_cast<const void*>(kernel), kBlock, lds, a.num_tiles);
+    const uint64_t grid = std::min<uint64_t>(a.num_tiles, std::max<uint64_t>(resident, (uint64_t(a.num_tiles) + 15) / 16));
+    hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kBlock), lds, st, a);
+}
+
 template <bool RESTORE, bool LDS_PTS>
 static void launch_decode(int hb, const DecodeArgs& a, size_t lds, hipStream_t st) {
     if constexpr (!RESTORE) {
@@ -327,16 +320,16 @@ static void launch_decode(int hb, const DecodeArgs& a, size_t lds, hipStream_t s
         return;
     }
     switch (hb) {
-        case 8: launch_tiles(decode_kernel<8, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 16: launch_tiles(decode_kernel<16, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 32: launch_tiles(decode_kernel<32, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 64: launch_tiles(decode_kernel<64, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 128: launch_tiles(decode_kernel<128, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 256: launch_tiles(decode_kernel<256, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 512: launch_tiles(decode_kernel<512, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 1024: launch_tiles(decode_kernel<1024, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 2048: launch_tiles(decode_kernel<2048, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
-        case 4096: launch_tiles(decode_kernel<4096, RESTORE, LDS_PTS>, a, a.num_tiles, kBlock, lds, st); break;
+        case 8: launch_restore(decode_kernel<8, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 16: launch_restore(decode_kernel<16, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 32: launch_restore(decode_kernel<32, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 64: launch_restore(decode_kernel<64, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 128: launch_restore(decode_kernel<128, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 256: launch_restore(decode_kernel<256, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 512: launch_restore(decode_kernel<512, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 1024: launch_restore(decode_kernel<1024, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 2048: launch_restore(decode_kernel<2048, RESTORE, LDS_PTS>, a, lds, st); break;
+        case 4096: launch_restore(decode_kernel<4096, RESTORE, LDS_PTS>, a, lds, st); break;
         default: break;
     }
 }
@@ -399,6 +392,7 @@ extern "C" e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx, const e
     a.signs = signs;
     a.cols = uint32_t(cols);
     a.pts = tab->dpoints;
+    a.h8 = tab->dh8;
     a.npts = uint32_t(tab->host.size);
     a.two_z = two_z_out;
     a.q = q_out;

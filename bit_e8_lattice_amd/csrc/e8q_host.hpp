@@ -38,6 +38,10 @@ struct DevTable {
     // The points in rank order as 8 bfloat16 (2z) each, plus a zero entry at
     // index |C(B)| (the GEMV's matrix-core operand table).
     uint4* dpts_bf16 = nullptr;
+    // H_8 (2z) of every point (natural-order 8-point Walsh-Hadamard transform,
+    // exact in integers, |entry| <= 48 for any supported core) as signed bytes,
+    // two words per point in the layout of the points.
+    uint32_t* dh8 = nullptr;
     CoreTable host;
 };
 
