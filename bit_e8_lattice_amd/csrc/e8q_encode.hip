@@ -13,7 +13,10 @@
 // word) gives the tile's first record slot; pass 2 recomputes only the
 // (item, wave) slices that contain escapes -- their weights are still in L2 --
 // and writes the records.  Record order is therefore ascending group order
-// whatever the scheduling.
+// whatever the scheduling.  A tile without escapes publishes only its zero
+// aggregate and goes on (no look-back, so no wait for its predecessors),
+// except every kAnchorTiles-th tile, which bounds how far back a tile with
+// records has to look.
 //
 // The lattice point of a group is computed on one of two paths that give the
 // same result:
@@ -41,6 +44,7 @@ constexpr uint64_t kFlagA = 1ull << 62;            // aggregate published
 constexpr uint64_t kFlagP = 2ull << 62;            // inclusive prefix published
 constexpr uint64_t kValMask = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kAnchorTiles = 64;                // tiles that resolve their prefix even without records
 constexpr size_t kWsHeader = 256;
 constexpr size_t kLdsLimit = 60 * 1024;   // dynamic LDS per block (static use is < 1 KB)
 
@@ -267,6 +271,13 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
             if (tile == 0) {
                 if (lane == 0)
                     __hip_atomic_store(a.tile_status, kFlagP | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else if (total == 0ull && tile % kAnchorTiles != 0u) {
+                // No records to place: publish the (zero) aggregate and skip
+                // the look-back and its wait.  Successors look back past it;
+                // every kAnchorTiles-th tile still resolves its prefix, so a
+                // look-back never runs far.
+                if (lane == 0)
+                    __hip_atomic_store(a.tile_status + tile, kFlagA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
                 if (lane == 0)
                     __hip_atomic_store(a.tile_status + tile, kFlagA | total, __ATOMIC_RELAXED,
