@@ -13,10 +13,12 @@
 // word) gives the tile's first record slot; pass 2 recomputes only the
 // (item, wave) slices that contain escapes -- their weights are still in L2 --
 // and writes the records.  Record order is therefore ascending group order
-// whatever the scheduling.  A tile without escapes publishes only its zero
-// aggregate and goes on (no look-back, so no wait for its predecessors),
-// except every kAnchorTiles-th tile, which bounds how far back a tile with
-// records has to look.
+// whatever the scheduling.  Only tiles with more than kStagedRecs escapes,
+// and every kAnchorTiles-th tile, resolve their prefix there; every other
+// tile publishes its aggregate and goes on without waiting for its
+// predecessors, staging its (at most kStagedRecs) records in the workspace.
+// A second kernel then places the staged records: the anchors' inclusive
+// prefixes plus a scan of the per-tile counts give every tile's first slot.
 //
 // The lattice point of a group is computed on one of two paths that give the
 // same result:
@@ -44,7 +46,8 @@ constexpr uint64_t kFlagA = 1ull << 62;            // aggregate published
 constexpr uint64_t kFlagP = 2ull << 62;            // inclusive prefix published
 constexpr uint64_t kValMask = (1ull << 62) - 1;
 constexpr uint32_t kSpinLimit = 1u << 22;
-constexpr uint32_t kAnchorTiles = 64;                // tiles that resolve their prefix even without records
+constexpr uint32_t kAnchorTiles = 64;                // tiles that always resolve their prefix
+constexpr uint32_t kStagedRecs = 16;                 // records a tile may stage for later placement
 constexpr size_t kWsHeader = 256;
 constexpr size_t kLdsLimit = 60 * 1024;   // dynamic LDS per block (static use is < 1 KB)
 
@@ -69,6 +72,8 @@ struct EncodeArgs {
     int8_t* two_z;
     uint32_t* tile_counter;
     unsigned long long* tile_status;
+    uint32_t* tile_total;     // escapes per tile
+    uint32_t* staged;         // kStagedRecs records (5 words each) per tile
     uint32_t num_tiles;
     uint32_t* status;
 };
@@ -114,6 +119,7 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
     __shared__ uint32_t s_cnt[kItems * kWaves];
     __shared__ unsigned long long s_ball[kItems][kWaves];
     __shared__ unsigned long long s_excl;
+    __shared__ uint32_t s_staged;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
@@ -268,16 +274,20 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
             }
             unsigned long long excl = 0;
             bool timeout = false;
+            bool staged = false;
+            if (lane == 0) a.tile_total[tile] = uint32_t(total);
             if (tile == 0) {
                 if (lane == 0)
                     __hip_atomic_store(a.tile_status, kFlagP | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else if (total == 0ull && tile % kAnchorTiles != 0u) {
-                // No records to place: publish the (zero) aggregate and skip
-                // the look-back and its wait.  Successors look back past it;
-                // every kAnchorTiles-th tile still resolves its prefix, so a
-                // look-back never runs far.
+            } else if (total <= kStagedRecs && tile % kAnchorTiles != 0u) {
+                // Few records: publish the aggregate, stage the records and
+                // skip the look-back and its wait.  Successors look back past
+                // this tile; every kAnchorTiles-th tile resolves its prefix,
+                // so a look-back never runs far.
                 if (lane == 0)
-                    __hip_atomic_store(a.tile_status + tile, kFlagA, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(a.tile_status + tile, kFlagA | total, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                staged = total != 0ull;
             } else {
                 if (lane == 0)
                     __hip_atomic_store(a.tile_status + tile, kFlagA | total, __ATOMIC_RELAXED,
@@ -315,6 +325,7 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
             }
             if (lane == 0) {
                 s_excl = excl;
+                s_staged = staged ? 1u : 0u;
                 if (timeout) atomicOr(a.status, uint32_t(E8Q_STATUS_LOOKBACK_TIMEOUT));
             }
         }
@@ -325,6 +336,7 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
         // block-uniform for them and wave-uniform otherwise).
         uint32_t oflags = 0;
         const unsigned long long excl = s_excl;
+        const bool staged = s_staged != 0u;
         for (int j = 0; j < kItems; ++j) {
             const uint64_t mask = s_ball[j][wv];
             bool any;
@@ -354,20 +366,58 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
                 // records go in group order: count escapes at lower logical positions
                 const uint64_t lmask = logical_lane_mask(mask);
                 const uint32_t rank_in_wave = uint32_t(__popcll(lmask & ((1ull << lane_off) - 1ull)));
-                const unsigned long long pos = excl + s_cnt[j * kWaves + wv] + rank_in_wave;
-                if (pos < a.esc_cap) {
-                    uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
+                const uint32_t local = s_cnt[j * kWaves + wv] + rank_in_wave;
+                const unsigned long long pos = excl + local;
+                uint32_t* dst = nullptr;
+                if (staged)
+                    dst = a.staged + (uint64_t(tile) * kStagedRecs + local) * 5u;   // local < kStagedRecs
+                else if (pos < a.esc_cap)
+                    dst = reinterpret_cast<uint32_t*>(a.esc + pos);
+                else
+                    oflags |= E8Q_STATUS_ESC_OVERFLOW;
+                if (dst) {
                     dst[0] = g - fdiv(g, a.gpb_div) * a.gpb_div.d;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         dst[1 + i] = (uint32_t(t[2 * i]) & 0xFFFFu) | (uint32_t(t[2 * i + 1]) << 16);
-                } else {
-                    oflags |= E8Q_STATUS_ESC_OVERFLOW;
                 }
             }
         }
         flush_status(oflags, a.status);
     }
+}
+
+// Placement of the staged records, after the encode kernel: one wave per
+// kAnchorTiles tiles, the first of which is an anchor with its inclusive
+// prefix resolved; a scan of the per-tile counts gives each tile's first slot.
+__global__ __launch_bounds__(256) void encode_place_kernel(EncodeArgs a) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t first = (uint64_t(blockIdx.x) * 4u + (threadIdx.x >> 6)) * kAnchorTiles;
+    if (first >= a.num_tiles) return;   // wave-uniform
+    const uint64_t t = first + lane;
+    const uint32_t tot = t < a.num_tiles ? a.tile_total[t] : 0u;
+    uint32_t incl = tot;   // at most 64 * 4096
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off, 64);
+        if (lane >= uint32_t(off)) incl += o;
+    }
+    const unsigned long long anchor = a.tile_status[first] & kValMask;
+    const unsigned long long base = anchor - __shfl(tot, 0, 64) + (incl - tot);
+    if (lane == 0u || tot == 0u || tot > kStagedRecs) return;
+    const uint32_t* src = a.staged + t * kStagedRecs * 5u;
+    uint32_t flags = 0;
+    for (uint32_t r = 0; r < tot; ++r) {
+        const unsigned long long pos = base + r;
+        if (pos < a.esc_cap) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
+#pragma unroll
+            for (int i = 0; i < 5; ++i) dst[i] = src[r * 5u + i];
+        } else {
+            flags |= E8Q_STATUS_ESC_OVERFLOW;
+        }
+    }
+    if (flags) atomicOr(a.status, flags);
 }
 
 // ------------------------------------------------------------------ host
@@ -407,9 +457,13 @@ int64_t core_size_host(int32_t bound) {
     return t.size;
 }
 
+// Workspace: [counter][tile status words][row coefficients][per-tile escape
+// counts][staged records, kStagedRecs per tile].
 size_t encode_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
-    return kWsHeader + align256(sizeof(unsigned long long) * size_t(tiles_for(batch, rows, cols))) +
-           align256(sizeof(float) * size_t(batch) * size_t(rows));
+    const size_t tiles = tiles_for(batch, rows, cols);
+    return kWsHeader + align256(sizeof(unsigned long long) * tiles) +
+           align256(sizeof(float) * size_t(batch) * size_t(rows)) + align256(sizeof(uint32_t) * tiles) +
+           align256(sizeof(e8q_escape_t) * kStagedRecs * tiles);
 }
 
 }  // namespace e8q
@@ -475,8 +529,12 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
     a.num_tiles = tiles_for(batch, rows, cols);
     a.tile_counter = reinterpret_cast<uint32_t*>(ws);
     a.tile_status = reinterpret_cast<unsigned long long*>(ws + kWsHeader);
-    float* coef = reinterpret_cast<float*>(ws + kWsHeader + align256(sizeof(unsigned long long) * a.num_tiles));
+    const size_t coef_off = kWsHeader + align256(sizeof(unsigned long long) * a.num_tiles);
+    float* coef = reinterpret_cast<float*>(ws + coef_off);
     a.coef = coef;
+    const size_t total_off = coef_off + align256(sizeof(float) * size_t(rows_total));
+    a.tile_total = reinterpret_cast<uint32_t*>(ws + total_off);
+    a.staged = reinterpret_cast<uint32_t*>(ws + total_off + align256(sizeof(uint32_t) * a.num_tiles));
     a.status = status_dev;
 
     const size_t smask_bytes = (hb > 0 ? size_t(cols / 2) * 4 : 0) + (hb > 128 ? size_t(8 * kBlock) * 4 : 0);
@@ -502,5 +560,7 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
         if (lds_tab) launch_encode<float, true, false>(hb, a, lds, s);
         else launch_encode<float, false, false>(hb, a, lds, s);
     }
+    const uint64_t segments = (uint64_t(a.num_tiles) + kAnchorTiles - 1) / kAnchorTiles;
+    hipLaunchKernelGGL(encode_place_kernel, dim3(unsigned((segments + 3) / 4)), dim3(256), 0, s, a);
     return launch_status();
 }

@@ -53,7 +53,9 @@ def test_workspace_size(L):
     groups = 128 * 4096 * 4096 // 8
     tiles = (groups + 4095) // 4096
     a256 = lambda v: (v + 255) // 256 * 256
-    assert L.e8q_encode_workspace_size(128, 4096, 4096) == 256 + a256(8 * tiles) + a256(4 * 128 * 4096)
+    # counter, tile status words, row coefficients, per-tile counts, 16 staged records per tile
+    assert L.e8q_encode_workspace_size(128, 4096, 4096) == (256 + a256(8 * tiles) + a256(4 * 128 * 4096)
+                                                          + a256(4 * tiles) + a256(20 * 16 * tiles))
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first

@@ -196,3 +196,25 @@ def test_many_small_batch_items(shape):
         ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), None, 0, bound)
         _compare(out, ref)
         assert out["counts"].sum() > shape[0] // 4
+
+
+@pytest.mark.parametrize("cap", [None, 0, 10, 19, 20, 35])
+def test_tile_escape_counts_around_the_staging_limit(cap):
+    """Tiles of 4096 groups with 3, 16, 17, 0 and 1 escapes: tiles with at most
+    16 escapes stage their records for a later placement, tiles with more place
+    them directly; records in order, counts exact, truncation at the capacity."""
+    d = device()
+    w = torch.zeros((1, 320, 512), dtype=torch.float32)
+    gen = np.random.default_rng(77)
+    per_tile = [3, 16, 17, 0, 1]
+    for k, n in enumerate(per_tile):
+        for g in sorted(gen.choice(4096, n, replace=False)):
+            gg = 4096 * k + int(g)
+            w[0, gg // 64, (gg % 64) * 8:(gg % 64) * 8 + 8] = 3.0
+    w = w.to(torch.bfloat16).to(d)
+    s = torch.ones(320, dtype=torch.float32, device=d)
+    out = run_encode(w, s, 16, cap=cap)
+    ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), None, 0, 16,
+                                    esc_capacity=(w.numel() // 8 if cap is None else cap))
+    assert int(ref["counts"].sum()) == sum(per_tile)
+    _compare(out, ref)
