@@ -389,35 +389,39 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
 
 // Placement of the staged records, after the encode kernel: one wave per
 // kAnchorTiles tiles, the first of which is an anchor with its inclusive
-// prefix resolved; a scan of the per-tile counts gives each tile's first slot.
+// prefix resolved; a running scan of the per-tile counts, 64 tiles at a time,
+// gives each tile's first slot.
 __global__ __launch_bounds__(256) void encode_place_kernel(EncodeArgs a) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint64_t first = (uint64_t(blockIdx.x) * 4u + (threadIdx.x >> 6)) * kAnchorTiles;
     if (first >= a.num_tiles) return;   // wave-uniform
-    const uint64_t t = first + lane;
-    const uint32_t tot = t < a.num_tiles ? a.tile_total[t] : 0u;
-    uint32_t incl = tot;   // at most 64 * 4096
+    unsigned long long run = (a.tile_status[first] & kValMask) - a.tile_total[first];
+    for (uint32_t c = 0; c < kAnchorTiles && first + c < a.num_tiles; c += 64u) {
+        const uint64_t t = first + c + lane;
+        const uint32_t tot = t < a.num_tiles ? a.tile_total[t] : 0u;
+        uint32_t incl = tot;   // at most 64 * 4096
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off, 64);
-        if (lane >= uint32_t(off)) incl += o;
-    }
-    const unsigned long long anchor = a.tile_status[first] & kValMask;
-    const unsigned long long base = anchor - __shfl(tot, 0, 64) + (incl - tot);
-    if (lane == 0u || tot == 0u || tot > kStagedRecs) return;
-    const uint32_t* src = a.staged + t * kStagedRecs * 5u;
-    uint32_t flags = 0;
-    for (uint32_t r = 0; r < tot; ++r) {
-        const unsigned long long pos = base + r;
-        if (pos < a.esc_cap) {
-            uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
-#pragma unroll
-            for (int i = 0; i < 5; ++i) dst[i] = src[r * 5u + i];
-        } else {
-            flags |= E8Q_STATUS_ESC_OVERFLOW;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t o = __shfl_up(incl, off, 64);
+            if (lane >= uint32_t(off)) incl += o;
         }
+        const unsigned long long base = run + (incl - tot);
+        run += __shfl(incl, 63, 64);
+        if (t == first || tot == 0u || tot > kStagedRecs) continue;
+        const uint32_t* src = a.staged + t * kStagedRecs * 5u;
+        uint32_t flags = 0;
+        for (uint32_t r = 0; r < tot; ++r) {
+            const unsigned long long pos = base + r;
+            if (pos < a.esc_cap) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
+#pragma unroll
+                for (int i = 0; i < 5; ++i) dst[i] = src[r * 5u + i];
+            } else {
+                flags |= E8Q_STATUS_ESC_OVERFLOW;
+            }
+        }
+        if (flags) atomicOr(a.status, flags);
     }
-    if (flags) atomicOr(a.status, flags);
 }
 
 // ------------------------------------------------------------------ host
