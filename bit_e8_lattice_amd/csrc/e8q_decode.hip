@@ -93,6 +93,7 @@ __device__ __forceinline__ bool find_record(const uint32_t* esc, const uint64_t*
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short gm_u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t bf16x2_rne_dec(float lo, float hi) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -594,13 +595,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
 // groups: lane quarter q = l / 16 loads the 16-byte index word of groups
 // 32c + 8q ... 32c + 8q + 7 (a whole 64-byte row segment per four lanes), and
 // step s of the chunk puts group 32c + 8q + s in K slice q (the order of the
-// groups along K is free).  Index words are loaded five chunks ahead, also
-// across the wave's tiles.  Every step's MFMA starts from 0; the
+// groups along K is free).  Index words are loaded four chunks ahead, also
+// across the wave's tiles, into four fixed registers.  Every step's MFMA starts from 0; the
 // steps are added in float32 in order, 16 steps (512 columns) per partial
 // sum, the partials in order.  Escaped and malformed slots are added per lane
 // in float32 (2z . x~, the same partial scheme).
 constexpr uint32_t kGmRows = 16;
-constexpr int kGmAhead = 5;   // index words (chunks) loaded ahead
+constexpr int kGmAhead = 4;   // index words (chunks) loaded ahead
 
 typedef __bf16 gm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
@@ -701,6 +702,7 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
     const uint4* tab = LDS_TAB ? s_gm : a.tab;
     const uint32_t i16 = lane & 15u, q = lane >> 4;
     const uint32_t nc = a.gpr >> 5;                 // chunks of 32 groups per row
+    const uint32_t ncp = (nc + uint32_t(kGmAhead) - 1u) / uint32_t(kGmAhead) * uint32_t(kGmAhead);
     const uint32_t vcol = i16 / 3u, pcol = i16 - 3u * vcol;
     const bool bcol = i16 < 3u * M;
     const gm_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -723,8 +725,8 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
     while (pf_u < u_end && wave_tile(pf_u) >= a.tiles_per_b) ++pf_u;
     const uint4* pf_ip = pf_u < u_end ? row_words(pf_u) : reinterpret_cast<const uint4*>(a.core_idx) + q;
     const auto next_word = [&]() {
-        const uint4 w = pf_ip[4u * pf_c];
-        if (++pf_c == nc) {
+        const uint4 w = pf_ip[4u * min(pf_c, nc - 1u)];   // padding chunks re-read the last word
+        if (++pf_c == ncp) {
             pf_c = 0;
             if (pf_u < u_end) {
                 do ++pf_u; while (pf_u < u_end && wave_tile(pf_u) >= a.tiles_per_b);
@@ -774,54 +776,68 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
         float sp1[M], sp2[M];
 #pragma unroll
         for (int v = 0; v < M; ++v) sp1[v] = sp2[v] = 0.0f;
-        for (uint32_t c = 0; c < nc; ++c) {
-            const uint4 w = wq[0];
+        // One chunk: the word in its ring slot (loaded kGmAhead chunks ago),
+        // whose refill is issued at once.  Every slot is a fixed register: the
+        // loop body takes the slots in order, and a row's chunk count is padded
+        // to a multiple of kGmAhead (padding chunks only refill), so no slot
+        // rotates -- a rotation's register moves would wait for the newest load.
+        const auto chunk = [&](uint4& slot, uint32_t c) {
+            const uint4 w = slot;
+            slot = next_word();
+            if (c < nc) {
+                // only the 3M lanes of real columns load (the D columns of the
+                // others are never read)
+                if (bcol) {
 #pragma unroll
-            for (int k = 0; k + 1 < kGmAhead; ++k) wq[k] = wq[k + 1];
-            wq[kGmAhead - 1] = next_word();
-            // only the 3M lanes of real columns load (the D columns of the
-            // others are never read)
-            if (bcol) {
+                    for (int s = 0; s < 8; ++s)
+                        xc[s] = X_LDS ? xp[(32u * c + 4u * uint32_t(s)) * 3u * M] : xp[32u * c + uint32_t(s)];
+                }
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+                uint32_t idx[8];
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    xc[s] = X_LDS ? xp[(32u * c + 4u * uint32_t(s)) * 3u * M] : xp[32u * c + uint32_t(s)];
-            }
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-            uint32_t idx[8];
-            bool any = false;
+                for (int s = 0; s < 8; ++s) idx[s] = (wd[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
+                // indices past the table (escapes, bad slots) read its zero entry
+                const auto products = [&]() {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                idx[s] = (wd[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
-                any = any || idx[s] >= a.npts;
-            }
-            if (__ballot(any)) {
-                // rare: one copy of the slow path, stepping through the word
+                    for (int s = 0; s < 8; ++s) {
+                        const uint4 pt = tab[min(idx[s], a.npts)];
+                        const gm_f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(gm_bf16x8, pt), __builtin_bit_cast(gm_bf16x8, xc[s]), zero, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc1[r] = acc1[r] + d[r];
+                    }
+                };
+                // the largest of the eight 16-bit indices (packed 16-bit maxima)
+                const gm_u16x2 mx = __builtin_elementwise_max(
+                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.x), __builtin_bit_cast(gm_u16x2, w.y)),
+                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.z), __builtin_bit_cast(gm_u16x2, w.w)));
+                const bool any = uint32_t(mx.x > mx.y ? mx.x : mx.y) >= a.npts;
+                if (__ballot(any)) {
+                    // rare: one copy of the slow path, stepping through the word
 #pragma unroll 1
-                for (uint32_t s = 0; s < 8; ++s) {
-                    const uint32_t h = s >> 1;
-                    const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
-                    const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
-                    if (id >= a.npts) gm_special<M>(a, b, row, 32u * c + 8u * q + s, id, row_ok, sp1, flags);
+                    for (uint32_t s = 0; s < 8; ++s) {
+                        const uint32_t h = s >> 1;
+                        const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
+                        const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
+                        if (id >= a.npts) gm_special<M>(a, b, row, 32u * c + 8u * q + s, id, row_ok, sp1, flags);
+                    }
+                }
+                products();
+                if ((c & 1u) == 1u || c + 1u == nc) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc2[r] = acc2[r] + acc1[r];
+                    acc1 = zero;
+#pragma unroll
+                    for (int v = 0; v < M; ++v) {
+                        sp2[v] = sp2[v] + sp1[v];
+                        sp1[v] = 0.0f;
+                    }
                 }
             }
+        };
+        for (uint32_t c = 0; c < ncp; c += uint32_t(kGmAhead)) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const uint4 pt = tab[min(idx[s], a.npts)];
-                const gm_f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(gm_bf16x8, pt), __builtin_bit_cast(gm_bf16x8, xc[s]), zero, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc1[r] = acc1[r] + d[r];
-            }
-            if ((c & 1u) == 1u || c + 1u == nc) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc2[r] = acc2[r] + acc1[r];
-                acc1 = zero;
-#pragma unroll
-                for (int v = 0; v < M; ++v) {
-                    sp2[v] = sp2[v] + sp1[v];
-                    sp1[v] = 0.0f;
-                }
-            }
+            for (int k = 0; k < kGmAhead; ++k) chunk(wq[k], c + uint32_t(k));
         }
         // D (16 rows x 16 columns) and the four lane quarters' escaped-slot sums
 #pragma unroll
