@@ -96,6 +96,24 @@ __device__ __forceinline__ uint64_t logical_lane_mask(uint64_t m) {
     return keep | rev;
 }
 
+// Packed bytes b0 (bits 0-7) and b1 (bits 16-23), each 2z + 64, as the int16
+// pair (b0 - 64, b1 - 64).
+__device__ __forceinline__ uint32_t unbias_i16x2(uint32_t v) {
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
+    const i16x2 d = __builtin_bit_cast(i16x2, v) - i16x2{64, 64};
+    return __builtin_bit_cast(uint32_t, d);
+}
+
+// Appends an escape to the tile's LDS list (slots past kStagedRecs are
+// dropped: such a tile writes its records in pass 2).
+__device__ __forceinline__ void list_escape(uint32_t& n, uint32_t* lg, uint4* lz, uint32_t g, const uint4& z) {
+    const uint32_t slot = atomicAdd(&n, 1u);
+    if (slot < kStagedRecs) {
+        lg[slot] = g;
+        lz[slot] = z;
+    }
+}
+
 // Workspace reset and per-row coefficients.
 __global__ void encode_init_kernel(uint32_t* counter, unsigned long long* tile_status, uint32_t num_tiles,
                                    unsigned long long* esc_count, uint32_t batch, const float* scale,
@@ -120,6 +138,12 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
     __shared__ unsigned long long s_ball[kItems][kWaves];
     __shared__ unsigned long long s_excl;
     __shared__ uint32_t s_staged;
+    // the tile's first kStagedRecs escapes as pass 1 finds them (any order):
+    // group index and 2z as four words of int16 pairs
+    __shared__ uint32_t s_nlist;
+    __shared__ uint32_t s_listed;
+    __shared__ uint32_t s_lg[kStagedRecs];
+    __shared__ uint4 s_lz[kStagedRecs];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
@@ -156,7 +180,10 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
 
     for (;;) {
         __syncthreads();
-        if (tid == 0) s_tile = atomicAdd(a.tile_counter, 1u);
+        if (tid == 0) {
+            s_tile = atomicAdd(a.tile_counter, 1u);
+            s_nlist = 0u;
+        }
         __syncthreads();
         const uint32_t tile = s_tile;
         if (tile >= a.num_tiles) break;
@@ -208,6 +235,14 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
                     // outside the core: only points inside it index the rank table
                     const bool outside = norm > a.core_bound;
                     escaped = live && outside;
+                    if (escaped) {
+                        // 2z + 64 bytes -> int16 pairs
+                        const uint4 z = make_uint4(unbias_i16x2(__builtin_amdgcn_perm(0u, t0, 0x0C010C00u)),
+                                                   unbias_i16x2(__builtin_amdgcn_perm(0u, t0, 0x0C030C02u)),
+                                                   unbias_i16x2(__builtin_amdgcn_perm(0u, t1, 0x0C010C00u)),
+                                                   unbias_i16x2(__builtin_amdgcn_perm(0u, t1, 0x0C030C02u)));
+                        list_escape(s_nlist, s_lg, s_lz, g, z);
+                    }
                     const uint32_t na = qa - (sa4 << 7) + 16384u;
                     const uint32_t fi = __builtin_amdgcn_udot4(t0, a.wpk, d8 ? kav[0] : kav[1], false) >> 1;
                     const uint32_t gb = __builtin_amdgcn_udot4(t1, a.wpk, d8 ? kbv[0] : kbv[1], false) >> 1;
@@ -222,6 +257,14 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
                 if (live) flags |= inv;
                 const bool outside = norm_u32(t) > a.core_bound;
                 escaped = live && outside;
+                if (escaped) {
+                    uint4 z;
+                    z.x = (uint32_t(t[0]) & 0xFFFFu) | (uint32_t(t[1]) << 16);
+                    z.y = (uint32_t(t[2]) & 0xFFFFu) | (uint32_t(t[3]) << 16);
+                    z.z = (uint32_t(t[4]) & 0xFFFFu) | (uint32_t(t[5]) << 16);
+                    z.w = (uint32_t(t[6]) & 0xFFFFu) | (uint32_t(t[7]) << 16);
+                    list_escape(s_nlist, s_lg, s_lz, g, z);
+                }
                 if (!outside) cidx = core_rank(t, tab, a.rp);
                 if (a.two_z && live) {
                     uint32_t f8 = 0;
@@ -323,9 +366,34 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
                     __hip_atomic_store(a.tile_status + tile, kFlagP | ((excl + total) & kValMask), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
+            // A tile with at most kStagedRecs escapes has them all in the list:
+            // ranked by group, they go to the staging slot or to their final
+            // slots here, and pass 2 has nothing to do.
+            const bool listed = total <= kStagedRecs;
+            if (listed && lane < uint32_t(total)) {
+                const uint32_t gme = s_lg[lane];
+                uint32_t rank = 0;
+                for (uint32_t k = 0; k < uint32_t(total); ++k) rank += s_lg[k] < gme ? 1u : 0u;
+                uint32_t* dst = nullptr;
+                if (staged)
+                    dst = a.staged + (uint64_t(tile) * kStagedRecs + rank) * 5u;
+                else if (excl + rank < a.esc_cap)
+                    dst = reinterpret_cast<uint32_t*>(a.esc + excl + rank);
+                else
+                    atomicOr(a.status, uint32_t(E8Q_STATUS_ESC_OVERFLOW));
+                if (dst) {
+                    const uint4 z = s_lz[lane];
+                    dst[0] = gme - fdiv(gme, a.gpb_div) * a.gpb_div.d;
+                    dst[1] = z.x;
+                    dst[2] = z.y;
+                    dst[3] = z.z;
+                    dst[4] = z.w;
+                }
+            }
             if (lane == 0) {
                 s_excl = excl;
                 s_staged = staged ? 1u : 0u;
+                s_listed = listed ? 1u : 0u;
                 if (timeout) atomicOr(a.status, uint32_t(E8Q_STATUS_LOOKBACK_TIMEOUT));
             }
         }
@@ -337,7 +405,8 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
         uint32_t oflags = 0;
         const unsigned long long excl = s_excl;
         const bool staged = s_staged != 0u;
-        for (int j = 0; j < kItems; ++j) {
+        const int items2 = s_listed != 0u ? 0 : kItems;   // block-uniform
+        for (int j = 0; j < items2; ++j) {
             const uint64_t mask = s_ball[j][wv];
             bool any;
             if constexpr (HB > 128) {
