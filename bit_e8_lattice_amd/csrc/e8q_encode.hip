@@ -10,10 +10,12 @@
 // every lattice point and core index, stores the indices and counts escapes
 // (wave ballots); a block scan plus a decoupled look-back over per-tile status
 // words (aggregate / inclusive prefix, packed with their flag in one 64-bit
-// word) gives the tile's first record slot; pass 2 recomputes only the
-// (item, wave) slices that contain escapes -- their weights are still in L2 --
-// and writes the records.  Record order is therefore ascending group order
-// whatever the scheduling.  Only tiles with more than kStagedRecs escapes,
+// word) gives the tile's first record slot.  Pass 1 also lists the tile's
+// first kStagedRecs escapes (group, 2z) in LDS; a tile with no more escapes
+// than that writes its records from the list, ranked by group.  Otherwise
+// pass 2 recomputes only the (item, wave) slices that contain escapes -- their
+// weights are still in L2 -- and writes the records.  Record order is
+// therefore ascending group order whatever the scheduling.  Only tiles with more than kStagedRecs escapes,
 // and every kAnchorTiles-th tile, resolve their prefix there; every other
 // tile publishes its aggregate and goes on without waiting for its
 // predecessors, staging its (at most kStagedRecs) records in the workspace.
