@@ -80,6 +80,9 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
     const uint32_t lpos = wv * kWave + lane_off;
     const uint32_t glast = a.groups - 1u;
 
+    // escape counts per batch item, held back per wave while its items stay in
+    // one batch item (wave-uniform, so scalar registers)
+    uint32_t pend_b = 0u, pend_n = 0u;
     for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
         const uint32_t tbase = tile * kTileGroups + lpos;
         uint32_t g1 = tbase, g2 = tbase + kBlock;
@@ -234,10 +237,15 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
                 const uint64_t mask = __ballot(escaped);
                 if (mask) {
                     const uint32_t b = live ? fdiv(g, a.gpb_div) : 0u;
-                    const uint32_t b0 = __shfl(b, 0, 64);
+                    const uint32_t b0 = __builtin_amdgcn_readfirstlane(b);
                     const bool uniform = __ballot(live && b != b0) == 0;
                     if (uniform) {
-                        if (lane == 0) atomicAdd(a.esc + b0, (unsigned long long)__popcll(mask));
+                        if (pend_n != 0u && b0 != pend_b) {
+                            if (lane == 0) atomicAdd(a.esc + pend_b, (unsigned long long)pend_n);
+                            pend_n = 0u;
+                        }
+                        pend_b = b0;
+                        pend_n += uint32_t(__popcll(mask));
                     } else if (escaped) {
                         atomicAdd(a.esc + b, 1ull);
                     }
@@ -246,6 +254,7 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
             flush_status(flags, a.status);
         }
     }
+    if (pend_n != 0u && lane == 0) atomicAdd(a.esc + pend_b, (unsigned long long)pend_n);
 }
 
 __global__ void zero_u64_kernel(unsigned long long* p, uint32_t n) {
