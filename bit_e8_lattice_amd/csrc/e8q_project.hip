@@ -254,7 +254,29 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
             flush_status(flags, a.status);
         }
     }
-    if (pend_n != 0u && lane == 0) atomicAdd(a.esc + pend_b, (unsigned long long)pend_n);
+    if (a.esc) {
+        // the block's waves pass their held counts to one thread, which adds
+        // runs of equal batch items with one atomic each
+        __shared__ uint32_t s_pb[kWaves], s_pn[kWaves];
+        if (lane == 0) {
+            s_pb[wv] = pend_b;
+            s_pn[wv] = pend_n;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t rb = 0u, rn = 0u;
+            for (uint32_t k = 0; k < uint32_t(kWaves); ++k) {
+                if (s_pn[k] == 0u) continue;
+                if (rn != 0u && s_pb[k] != rb) {
+                    atomicAdd(a.esc + rb, (unsigned long long)rn);
+                    rn = 0u;
+                }
+                rb = s_pb[k];
+                rn += s_pn[k];
+            }
+            if (rn != 0u) atomicAdd(a.esc + rb, (unsigned long long)rn);
+        }
+    }
 }
 
 __global__ void zero_u64_kernel(unsigned long long* p, uint32_t n) {
