@@ -187,3 +187,17 @@ def test_decoder_shapes_full_row_blocks():
         ref = oracle.project(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), hb, core_bound=16)
         _compare(out, ref)
         assert out["esc_count"].tolist() == ref["esc_count"].tolist()
+
+
+@pytest.mark.parametrize("shape", [(5000, 1, 8), (250, 37, 8), (900, 1, 72), (40, 300, 64)])
+def test_escape_counts_many_batch_items(shape):
+    """Per-batch escape counts when waves and blocks span many batch items
+    (each wave holds its count while its items stay in one batch item)."""
+    d = device()
+    w = workloads.normal(shape, 17 * shape[0] + shape[2], d)
+    s = workloads.rms_scale(w, 1.0)
+    for bound in (0, 16):
+        out = run_project(w, s, core_bound=bound)
+        ref = oracle.project(wbits(w), s.cpu().numpy(), core_bound=bound)
+        assert out["esc_count"].tolist() == ref["esc_count"].tolist()
+        assert int(out["esc_count"].sum()) > 0
