@@ -165,8 +165,12 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
         }
     }
     if constexpr (LDS_TAB) {
+        // 16-byte copies (both ends are 16-byte aligned), then the tail
         uint16_t* t16 = reinterpret_cast<uint16_t*>(s_dyn + smask_words + wide_words);
-        for (uint32_t i = tid; i < a.rp.entries; i += kBlock) t16[i] = a.tab[i];
+        const uint32_t n16 = a.rp.entries / 8u;
+        for (uint32_t i = tid; i < n16; i += kBlock)
+            reinterpret_cast<uint4*>(t16)[i] = reinterpret_cast<const uint4*>(a.tab)[i];
+        for (uint32_t i = 8u * n16 + tid; i < a.rp.entries; i += kBlock) t16[i] = a.tab[i];
         tab = t16;
     }
     const LaneFwht lf = lane_fwht<(HB > 128 ? 128 : HB)>(lane);
