@@ -281,21 +281,17 @@ __device__ __forceinline__ bool fast_point(const float (&x)[8], uint32_t& t0, ui
     // parity fix: first coordinate with |d| equal to the max (D8) or min (D8+1/2)
     const float tgt = d8 ? amax : amin;
     const bool fixon = (d8 && odd0) || (!d8 && odd1);
-    bool acc = false, f[8];
+    // the first match in each word (later matches are overwritten), and the
+    // second word's only when the first word has none
+    uint32_t sel0 = 0u, sel1 = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const bool e = fabsf(d[i]) == tgt;
-        f[i] = e && !acc && fixon;
-        acc = acc || e;
+    for (int i = 3; i >= 0; --i) {
+        sel0 = fabsf(d[i]) == tgt ? (0xFFu << (8 * i)) : sel0;
+        sel1 = fabsf(d[4 + i]) == tgt ? (0xFFu << (8 * i)) : sel1;
     }
-    uint32_t sel0 = f[3] ? 0xFF000000u : 0u;
-    sel0 = f[2] ? 0x00FF0000u : sel0;
-    sel0 = f[1] ? 0x0000FF00u : sel0;
-    sel0 = f[0] ? 0x000000FFu : sel0;
-    uint32_t sel1 = f[7] ? 0xFF000000u : 0u;
-    sel1 = f[6] ? 0x00FF0000u : sel1;
-    sel1 = f[5] ? 0x0000FF00u : sel1;
-    sel1 = f[4] ? 0x000000FFu : sel1;
+    sel1 = sel0 != 0u ? 0u : sel1;
+    sel0 = fixon ? sel0 : 0u;
+    sel1 = fixon ? sel1 : 0u;
     // D8 moves the coordinate by +2 sgn(d), D8+1/2 by -2 sgn(d)
     const uint32_t dm = d8 ? 0u : 0xFFFFFFFFu;
     const uint32_t mx0 = m0 ^ dm, mx1 = m1 ^ dm;
