@@ -160,11 +160,13 @@ def run_dense_decoder(args, torch, e8q, workloads):
     kernel_ms = sum(sum(r) for r in launch_ms) / args.steps          # per step, all 3 launches
     achieved = sum(alg_bytes) / (kernel_ms * 1e-3) / 1e9
     rho = sum(escapes) / groups
-    traffic = None
+    traffic = None   # measured HBM bytes: per launch (mean of the three) and per step
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
         if tf.get("kernel_hash") == kernel_hash():
-            traffic = tf.get("bytes_per_step")
+            per = [x["read"] + x["write"] for x in tf["per_launch_bytes"]]
+            traffic = {"per_launch": round(sum(per) / len(per)), "per_step": tf.get("bytes_per_step"),
+                       "ratio_to_algorithmic": tf.get("ratio_to_algorithmic")}
     return {
         "weights": weights, "wall": wall, "status": st, "escapes": escapes, "rho": rho,
         "alg_bytes": alg_bytes, "launch_ms": launch_ms, "kernel_ms": kernel_ms, "achieved": achieved,
@@ -618,7 +620,7 @@ def main():
             "peak": round(VALU_PEAK_TOPS, 2),
             "unit": "Tops/s",
             "frac": round(alu / VALU_PEAK_TOPS, 4),
-            "traffic": r["traffic"],
+            "traffic": r["traffic"]["per_launch"] if r["traffic"] else None,
         },
         "cpu_baseline": cpu,
         "detail": {
@@ -629,6 +631,8 @@ def main():
             "kernel_ms_per_step": round(r["kernel_ms"], 4),
             "launch_ms_mean": [round(sum(x[i] for x in r["launch_ms"]) / args.steps, 4) for i in range(3)],
             "alg_bytes_per_step": sum(r["alg_bytes"]),
+            "hbm_traffic_bytes_per_step": r["traffic"]["per_step"] if r["traffic"] else None,
+            "hbm_traffic_ratio_to_algorithmic": r["traffic"]["ratio_to_algorithmic"] if r["traffic"] else None,
             "escapes": sum(r["escapes"]),
             "rho": r["rho"],
             "payload_bits_per_weight": 2 + 20 * r["rho"],
