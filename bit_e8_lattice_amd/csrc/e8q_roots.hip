@@ -107,14 +107,23 @@ __global__ __launch_bounds__(kRootThreads) void pack_kernel(RootArgs a) {
         uint32_t root = 0xFFu, core = 0xFFFFu;
         if (need <= 2 * 131088) {
             const int th = int(need);
-            for (uint32_t j = 0; j < 240u; ++j) {
-                const uint32_t* rr = s_r16 + 4u * j;
-                int dot = 0;
+            // eight roots per step (independent dot products), the first hit
+            // of the step from its bit mask
+            for (uint32_t j0 = 0; j0 < 240u; j0 += 8u) {
+                uint32_t hits = 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    dot = __builtin_amdgcn_sdot2(__builtin_bit_cast(rt_short2, w[q]), __builtin_bit_cast(rt_short2, rr[q]),
-                                                 dot, false);
-                if (2 * dot >= th) {
+                for (uint32_t k = 0; k < 8u; ++k) {
+                    const uint32_t* rr = s_r16 + 4u * (j0 + k);
+                    int dot = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        dot = __builtin_amdgcn_sdot2(__builtin_bit_cast(rt_short2, w[q]),
+                                                     __builtin_bit_cast(rt_short2, rr[q]), dot, false);
+                    hits |= (2 * dot >= th ? 1u : 0u) << k;
+                }
+                if (hits != 0u) {
+                    const uint32_t j = j0 + uint32_t(__builtin_ctz(hits));
+                    const uint32_t* rr = s_r16 + 4u * j;
                     int c[8];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
