@@ -69,13 +69,21 @@ __global__ __launch_bounds__(1024) void decode_offsets_kernel(const int64_t* cou
     if (tid == 1023u) offsets[batch] = min(part[1023], capacity);
 }
 
-// 2z of an escaped slot from its record; false when there is none.
+// 2z of an escaped slot from its record; false when there is none.  The
+// records of a batch item hold increasing group indices below gpb, spread
+// roughly evenly, so the first probes interpolate the position between the
+// bracketing keys (each probe is a dependent load); then it halves.
 __device__ __forceinline__ bool find_record(const uint32_t* esc, const uint64_t* offsets, uint32_t b, uint32_t gib,
-                                            int (&t)[8]) {
+                                            uint32_t gpb, int (&t)[8]) {
     uint64_t lo = offsets[b], hi = offsets[b + 1];
-    // at most 64 halvings: the range never exceeds 2^64 records
+    uint32_t klo = 0u, khi = gpb;   // every key in [lo, hi) lies in [klo, khi) (sorted records)
+    // at most 64 steps: the range never exceeds 2^64 records
     for (int it = 0; it < 64 && lo < hi; ++it) {
-        const uint64_t mid = lo + ((hi - lo) >> 1);
+        uint64_t mid = lo + ((hi - lo) >> 1);
+        if (it < 3 && gib >= klo && gib < khi && hi - lo <= 0xFFFFFFFFull) {
+            // gib - klo < khi - klo, so off < hi - lo (no overflow: both factors < 2^32)
+            mid = lo + uint64_t(gib - klo) * (hi - lo) / uint64_t(khi - klo);
+        }
         const uint32_t key = esc[mid * 5];
         if (key == gib) {
             const uint32_t* r = esc + mid * 5 + 1;
@@ -87,7 +95,13 @@ __device__ __forceinline__ bool find_record(const uint32_t* esc, const uint64_t*
             }
             return true;
         }
-        if (key < gib) lo = mid + 1; else hi = mid;
+        if (key < gib) {
+            lo = mid + 1;
+            klo = key + 1u;
+        } else {
+            hi = mid;
+            khi = key;
+        }
     }
     return false;
 }
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
                 }
             } else if (idx == 0xFFFFu) {
                 const uint32_t b = fdiv(gl, a.gpb_div);
-                if (find_record(a.esc, a.offsets, b, gl - b * a.gpb, tb)) {
+                if (find_record(a.esc, a.offsets, b, gl - b * a.gpb, a.gpb, tb)) {
                     big = true;
                 } else if (live) {
                     flags |= E8Q_STATUS_ESC_MISSING;
@@ -466,7 +480,7 @@ __device__ __forceinline__ void special_point(const GemvArgs& a, uint32_t b, uin
     int tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (idx != 0xFFFFu)
         flags |= E8Q_STATUS_BAD_INDEX;
-    else if (!find_record(a.esc, a.offsets, b, gib, tb))
+    else if (!find_record(a.esc, a.offsets, b, gib, a.rows * a.gpr, tb))
         flags |= E8Q_STATUS_ESC_MISSING;
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = float(tb[i]);
@@ -661,7 +675,7 @@ __device__ __forceinline__ void gm_special(const GemvMfmaArgs& a, uint32_t b, ui
     int tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (idx != 0xFFFFu) {
         if (row_ok) flags |= E8Q_STATUS_BAD_INDEX;
-    } else if (!find_record(a.esc, a.offsets, b, row * a.gpr + g, tb)) {
+    } else if (!find_record(a.esc, a.offsets, b, row * a.gpr + g, a.rows * a.gpr, tb)) {
         if (row_ok) flags |= E8Q_STATUS_ESC_MISSING;
     }
 #pragma unroll
