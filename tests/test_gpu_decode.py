@@ -193,3 +193,26 @@ def test_decode_restore_only_large_escapes_and_malformed():
     for wd in (torch.bfloat16, torch.float32):
         out = run_decode(core, esc, cnt, shape, 16, s_bad, sg, 128, two_z=False, w_hat_dtype=wd)
         _cmp(out, ref, None, wd)
+
+
+@pytest.mark.parametrize("where", ["first_rows", "last_rows", "one_row", "two_ends"])
+def test_decode_clustered_escapes(where):
+    """Escape records bunched in a few rows of each batch item (the record
+    search's interpolated probes land far from them and it falls back to
+    halving): decoded 2z, q and restored weights still match the oracle."""
+    d = device()
+    shape = (3, 40, 512)
+    w = workloads.normal(shape, 4321, d, dtype=torch.float32)
+    s = workloads.rms_scale(w, 3.0)
+    rows = {"first_rows": slice(0, 3), "last_rows": slice(37, 40), "one_row": slice(20, 21),
+            "two_ends": [0, 39]}[where]
+    w[:, rows, ::5] = 6.0 * s.view(3, 40, 1)[:, rows, :]
+    sg = workloads.signs(512, 4322, d)
+    sn = sg.cpu().numpy()
+    wb = wbits(w)
+    enc = oracle.encode_core_escape(wb, s.cpu().numpy(), sn, 128, 16, w_is_bf16=False)
+    assert enc["counts"].min() > 10
+    ref = oracle.decode_outputs(enc["core_idx"], enc["records"], enc["counts"], 16, shape, s.cpu().numpy(), sn, 128)
+    core, esc, cnt = upload_export(enc, d)
+    out = run_decode(core, esc, cnt, shape, 16, s, sg, 128, q_dtype=torch.float32, w_hat_dtype=torch.float32)
+    _cmp(out, ref, torch.float32, torch.float32)

@@ -186,3 +186,24 @@ def test_gemv_matrix_core_few_rows(rows):
     out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
     assert out["status"] == 0
     _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, 256)
+
+
+@pytest.mark.parametrize("where", ["first_rows", "last_rows", "two_ends"])
+def test_gemv_clustered_escapes(where):
+    """Escape records bunched in a few rows (the record search falls back from
+    interpolated probes to halving), on the matrix-core path."""
+    d = device()
+    shape = (3, 40, 2048)
+    w = workloads.normal(shape, 4331, d, dtype=torch.float32)
+    s = workloads.rms_scale(w, 3.0)
+    rows = {"first_rows": slice(0, 3), "last_rows": slice(37, 40), "two_ends": [0, 39]}[where]
+    w[:, rows, ::7] = 6.0 * s.view(3, 40, 1)[:, rows, :]
+    sg = workloads.signs(2048, 4332, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, 16, w_is_bf16=False)
+    assert enc["counts"].min() > 10
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((3, 1, 2048), 4333, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, 2048)
