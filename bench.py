@@ -536,8 +536,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the encode shards by matrix with no exchange; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the encode shards by whole matrices with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     cpu = None if (args.no_cpu_baseline or args.config != "decoder") else cpu_baseline(args.cpu_blocks)

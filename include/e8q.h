@@ -21,7 +21,7 @@
  *       E8Q_OK, E8Q_ERR_INVALID (a bad argument: null required pointer,
  *       non-positive size, cols not a multiple of 8, bad block size or core
  *       bound, too small workspace), E8Q_ERR_UNSUPPORTED (a dtype or size
- *       combination this build does not implement), E8Q_ERR_LAUNCH (the HIP
+ *       combination the library does not implement), E8Q_ERR_LAUNCH (the HIP
  *       launch failed), E8Q_ERR_DEVICE (a device query or the one-time rank
  *       table upload failed).  Nothing is launched when a check fails.
  *   - Conditions that depend on the data are reported by OR-ing E8Q_STATUS_*
