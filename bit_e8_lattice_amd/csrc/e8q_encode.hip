@@ -406,8 +406,8 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
         __syncthreads();
 
         // Pass 2: records of the slices that have escapes (recomputed on the
-        // exact path; wide blocks need the whole block, so the condition is
-        // block-uniform for them and wave-uniform otherwise).
+        // exact path; blocks wider than 512 columns need the whole block, so
+        // the condition is block-uniform for them and wave-uniform otherwise).
         uint32_t oflags = 0;
         const unsigned long long excl = s_excl;
         const bool staged = s_staged != 0u;
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
         for (int j = 0; j < items2; ++j) {
             const uint64_t mask = s_ball[j][wv];
             bool any;
-            if constexpr (HB > 128) {
+            if constexpr (HB > 512) {
                 uint64_t all = 0;
 #pragma unroll
                 for (int k = 0; k < kWaves; ++k) all |= s_ball[j][k];

@@ -42,6 +42,25 @@ __device__ __forceinline__ Raw load_raw(const void* w, uint32_t g) {
     return r;
 }
 
+// Remaining butterfly stages of 256- and 512-column blocks, inside the wave:
+// stride 128 pairs lane l with lane l ^ 16 (the same logical position in the
+// next 16-lane row), stride 256 lane l with l ^ 32.  v holds the true values
+// (lane sign already removed); every lane of the wave takes part.  The lower
+// lane keeps p + q, the upper one p - q (one rounding each, as a butterfly).
+template <int HB>
+__device__ __forceinline__ void wave_stages(float (&v)[8]) {
+    const uint32_t lane = __lane_id();
+#pragma unroll
+    for (int m = 16; m < HB / 8; m <<= 1) {
+        const float eps = (lane & uint32_t(m)) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float o = __shfl_xor(v[i], m, 64);
+            v[i] = fmaf(eps, v[i], o);
+        }
+    }
+}
+
 // Remaining butterfly stages of blocks wider than 128 columns: stride
 // 128 * 2^k for k = 0 .. log2(HB/128) - 1, in that order.  v holds the true
 // values (lane sign already removed) of this thread's group; lpos is the
@@ -125,7 +144,10 @@ __device__ __forceinline__ uint32_t fwht_cross(float (&v)[8], const LaneFwht& lf
     if constexpr (HB > 128) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ lf.sign);
-        wide_stages<HB>(v, s_wide, lpos, tid);
+        if constexpr (HB <= 512)
+            wave_stages<HB>(v);
+        else
+            wide_stages<HB>(v, s_wide, lpos, tid);
         return 0u;
     } else {
         return HB >= 16 ? lf.sign : 0u;
