@@ -65,9 +65,9 @@ __device__ __forceinline__ void wave_stages(float (&v)[8]) {
 // 128 * 2^k for k = 0 .. log2(HB/128) - 1, in that order.  v holds the true
 // values (lane sign already removed) of this thread's group; lpos is the
 // group's position inside the item.  s_wide: 8 * kBlock floats of LDS.
-template <int HB>
+template <int HB, int S = 128>
 __device__ __forceinline__ void wide_stages(float (&v)[8], float* s_wide, uint32_t lpos, uint32_t tid) {
-    constexpr int M = HB / 128;          // 128-column sub-blocks per block
+    constexpr int M = HB / S;            // S-column sub-blocks per block (stages of stride S, 2S, ...)
     constexpr int TPB = HB / 8;          // threads per block
 #pragma unroll
     for (int i = 0; i < 8; ++i) s_wide[lpos * 8 + i] = v[i];
@@ -76,12 +76,13 @@ __device__ __forceinline__ void wide_stages(float (&v)[8], float* s_wide, uint32
     float* blk = s_wide + bi * HB;
     float u[8];
     if constexpr (M <= 8) {
-        // 8/M positions per thread, all M sub-blocks of each
+        // 8/M positions per thread (r, r + TPB, ...: neighbouring threads read
+        // neighbouring words), all M sub-blocks of each
         constexpr int P = 8 / M;
 #pragma unroll
         for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-            for (int s = 0; s < M; ++s) u[pp * M + s] = blk[s * 128 + r * P + pp];
+            for (int s = 0; s < M; ++s) u[pp * M + s] = blk[s * S + pp * TPB + r];
 #pragma unroll
         for (int h = 1; h < M; h <<= 1)
 #pragma unroll
@@ -97,8 +98,9 @@ __device__ __forceinline__ void wide_stages(float (&v)[8], float* s_wide, uint32
 #pragma unroll
         for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-            for (int s = 0; s < M; ++s) blk[s * 128 + r * P + pp] = u[pp * M + s];
+            for (int s = 0; s < M; ++s) blk[s * S + pp * TPB + r] = u[pp * M + s];
     } else {
+        static_assert(S == 128, "sub-blocks of S columns with S > 128 number at most 8");
         // one position, sub-blocks qt*8 .. qt*8+7 in-thread, qt across M/8 adjacent lanes
         constexpr int T = M / 8;
         const uint32_t pos = r / T, qt = r % T;
@@ -144,10 +146,18 @@ __device__ __forceinline__ uint32_t fwht_cross(float (&v)[8], const LaneFwht& lf
     if constexpr (HB > 128) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ lf.sign);
-        if constexpr (HB <= 512)
+        // 256 and 512 columns: inside the wave.  4096: strides 128 and 256
+        // inside the wave, the rest through LDS over 512-column sub-blocks (one
+        // position per thread).  1024 and 2048: all through LDS (measured
+        // faster than with the shuffles first).
+        if constexpr (HB <= 512) {
             wave_stages<HB>(v);
-        else
+        } else if constexpr (HB >= 4096) {
+            wave_stages<512>(v);
+            wide_stages<HB, 512>(v, s_wide, lpos, tid);
+        } else {
             wide_stages<HB>(v, s_wide, lpos, tid);
+        }
         return 0u;
     } else {
         return HB >= 16 ? lf.sign : 0u;
