@@ -9,19 +9,20 @@ weights, N(0, 0.02^2), scale 3 x row RMS, core ||2z||^2 <= 16), issued as
 three launches batched by shape.  Inputs are generated on the GPU and resident
 in HBM before timing starts.
 
-Prints one JSON line.  Also reports the CPU oracle's rate on a bounded sample
-of the same workload (timed before the GPU is touched, in forked workers).
+Prints one JSON line.  ``roofline`` is the encode launches' algorithmic HBM
+bytes per launch over their mean duration (HIP events on the launching stream)
+against the 8 TB/s HBM peak.  ``cpu_baseline`` is the CPU oracle timed on the
+same input bits (block 0 of the decoder), with the oracle's rate on every other
+workload and on one core in ``detail.cpu_oracle``; the oracle's workers are
+forked before the GPU is touched.
 
 ``--config`` picks another workload for manual runs (the default is the one
-above): ``linear`` (4096x4096 rotated projection), ``moe`` (128-expert
-stacks), ``qat`` (one forward projection + fused STE/SGD step on 4096x14336).
-
-The encode kernel is bound by vector-ALU issue, not by HBM (its measured HBM
-traffic is within 2% of the algorithmic bytes), so the roofline reported is
-ALU: the method's arithmetic per weight (7 butterfly additions for 128-wide
-blocks, 1 scale multiplication, about 7 nearest-point decoder operations)
-against 256 CUs x 64 lanes x 2.4 GHz of non-packed vector issue; HBM figures
-are in ``detail``.
+above): ``decoder_alpha1`` (scale 1 x RMS, most groups escape),
+``decoder_wide`` (whole-row 4096 / 256-column rotation blocks), ``linear``
+(4096x4096 rotated projection), ``moe`` / ``moe_alpha1`` (128-expert stacks),
+``qat`` (one forward projection + fused STE/SGD step on 4096x14336, escape
+count of every step in ``detail``), ``qat_restore``, ``qat_rotated_grad``,
+``decode``, ``decode_q``, ``gemv``, ``pack``, ``ptq``.
 """
 
 import argparse
@@ -50,55 +51,166 @@ def kernel_hash():
 
 
 # --------------------------------------------------------------- CPU baseline
+#
+# The oracle runs in single-threaded workers forked before the GPU is touched
+# (a process that has initialised HIP must not fork).  The parent draws the
+# inputs on the GPU, copies their bits into an anonymous shared mapping that
+# the workers inherited, and hands out row chunks by offset, so the oracle
+# sees exactly the bits the GPU encoded and the timing covers compute only.
 
-def _oracle_chunk(job):
+_SHM = None                    # anonymous shared mapping, created before the fork
+SHM_BYTES = 448 << 20          # largest sample: one decoder block (405 MB of bf16) + scales + signs
+
+
+def _oracle_job(job):
+    """One chunk: ``job`` = (kind, (w_off, w_shape, w_dtype), (s_off, n_s), (sg_off, n_sg) or None,
+    had_block, core_bound).  Returns (weights, seconds of compute)."""
     import numpy as np
     import oracle
-    w, s, sg = job
+    kind, (w_off, w_shape, w_dt), (s_off, n_s), sg, hb, bound = job
+    n = int(np.prod(w_shape))
+    w = np.frombuffer(_SHM, dtype=w_dt, count=n, offset=w_off).reshape(w_shape)
+    s = np.frombuffer(_SHM, dtype=np.float32, count=n_s, offset=s_off)
+    signs = None if sg is None else np.frombuffer(_SHM, dtype=np.int8, count=sg[1], offset=sg[0])
     t0 = time.perf_counter()
-    oracle.encode_core_escape(w, s, sg, 128, 16)
-    return w.size, time.perf_counter() - t0
+    if kind == "encode":
+        oracle.encode_core_escape(w, s, signs, hb, bound)
+    else:                       # projection with dequantization (and escape count when bound >= 0)
+        oracle.project(w, s, signs, hb, w_is_bf16=(w_dt == np.uint16), core_bound=bound)
+    return n, time.perf_counter() - t0
 
 
-def cpu_baseline(blocks=1, chunk_rows=512):
-    """Oracle Gweights/s on a bounded sample of the same workload: every
-    matrix of the first ``blocks`` decoder block(s) (q, k, v, o, gate, up,
-    down: 202 M weights per block), same seeds, scales and signs, encoded by
-    the numpy oracle in forked single-threaded workers (one per core, at most
-    16) over chunks of rows.  Runs before the GPU is initialised."""
-    import multiprocessing as mp
+class OraclePool:
+    """Forked oracle workers (one per core, at most 16) and the shared input
+    mapping; must be created before any GPU call."""
+
+    def __init__(self):
+        import multiprocessing as mp
+        import mmap
+        global _SHM
+        _SHM = mmap.mmap(-1, SHM_BYTES)
+        self.cores = min(16, len(os.sched_getaffinity(0)))
+        self.pool = mp.get_context("fork").Pool(self.cores)
+        self.single = mp.get_context("fork").Pool(1)
+
+    def close(self):
+        self.pool.terminate()
+        self.single.terminate()
+
+    def stage(self, tensors):
+        """Copy host numpy arrays into the shared mapping; returns their offsets."""
+        import numpy as np
+        offs, pos = [], 0
+        for a in tensors:
+            a = np.ascontiguousarray(a)
+            if pos + a.nbytes > SHM_BYTES:
+                raise RuntimeError("oracle sample larger than the shared mapping")
+            _SHM[pos:pos + a.nbytes] = a.tobytes()
+            offs.append(pos)
+            pos = (pos + a.nbytes + 255) & ~255
+        return offs
+
+    def run(self, kind, w, s, sg, hb, bound, chunk_rows, single=False):
+        """Time the oracle on ``w`` [batch, rows, cols] (uint16 bf16 bits or float32),
+        chunks of ``chunk_rows`` rows; returns (weights, wall s, cpu s, workers)."""
+        import numpy as np
+        batch, rows, cols = w.shape
+        arrays = [w, s] + ([] if sg is None else [sg])
+        offs = self.stage(arrays)
+        sgd = None if sg is None else (offs[2], int(sg.size))
+        jobs = []
+        for b in range(batch):
+            for lo in range(0, rows, chunk_rows):
+                nr = min(chunk_rows, rows - lo)
+                w_off = offs[0] + (b * rows + lo) * cols * w.dtype.itemsize
+                s_off = offs[1] + (b * rows + lo) * 4
+                jobs.append((kind, (w_off, (1, nr, cols), w.dtype), (s_off, nr), sgd, hb, bound))
+        pool = self.single if single else self.pool
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_job, jobs, chunksize=1)
+        wall = time.perf_counter() - t0
+        return sum(r[0] for r in res), wall, sum(r[1] for r in res), 1 if single else min(self.cores, len(jobs))
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host(t):
+    """Device tensor -> host numpy array of the same bits (bf16 as uint16)."""
     import numpy as np
     import torch
-    from bit_e8_lattice_amd import workloads
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
 
-    torch.set_num_threads(min(16, len(os.sched_getaffinity(0))))
-    jobs = []
-    for blk in range(blocks):
-        for j, (name, rows, cols) in enumerate(workloads.DECODER_MATS):
-            seed = 4100 + blk * len(workloads.DECODER_MATS) + j
-            w = workloads.normal((rows, cols), seed, "cpu")
-            s = workloads.rms_scale(w, 3.0).numpy()
-            sg = workloads.signs(cols, 4001 if cols == 4096 else 4002, "cpu").numpy()
-            wb = w.contiguous().view(torch.int16).numpy().view(np.uint16)
-            for lo in range(0, rows, chunk_rows):
-                jobs.append((wb[lo:lo + chunk_rows].copy(), s[lo:lo + chunk_rows].copy(), sg))
-    torch.set_num_threads(1)
-    cores = min(16, len(os.sched_getaffinity(0)), len(jobs))
-    ctx = mp.get_context("fork")
-    t0 = time.perf_counter()
-    with ctx.Pool(cores) as pool:
-        res = pool.map(_oracle_chunk, jobs, chunksize=1)
-    wall = time.perf_counter() - t0
-    weights = sum(r[0] for r in res)
-    cpu_s = sum(r[1] for r in res)
-    return {
-        "value": weights / wall / 1e9,
+
+def cpu_oracle_rates(pool, torch, workloads, decoder_batches):
+    """The oracle's rate on every workload, on bounded samples of GPU-drawn
+    inputs: the dense decoder's block 0 (all seven matrices; the headline
+    sample), the 256x256 float32 matrix, the 4096x4096 projection (all cores
+    and one core), 8 experts of each MoE kind and the 4096x14336 QAT forward.
+    Returns (headline dict for ``cpu_baseline``, per-workload detail)."""
+    dev = torch.device("cuda:0")
+    per = {}
+
+    def rec(name, r, what):
+        n, wall, cpu_s, workers = r
+        per[name] = {"gweights_per_s": round(n / wall / 1e9, 5), "weights": n, "workers": workers,
+                     "wall_s": round(wall, 2), "cpu_s": round(cpu_s, 2), "sample": what}
+        return r
+
+    # dense decoder block 0: batch index 0-3 of 4096x4096 (q, k, v, o), 0-1 of
+    # 11008x4096 (gate, up), 0 of 4096x11008 (down)
+    firsts = {(4096, 4096): 4, (11008, 4096): 2, (4096, 11008): 1}
+    tot = [0, 0.0, 0.0, 0]
+    for b in decoder_batches:
+        nb, rows, cols = b.w.shape
+        k = firsts[(rows, cols)]
+        r = pool.run("encode", _host(b.w[:k]), _host(b.scale[: k * rows]), _host(b.signs), 128, 16, 512)
+        tot = [tot[0] + r[0], tot[1] + r[1], tot[2] + r[2], max(tot[3], r[3])]
+    rec("dense_decoder", tuple(tot), "decoder block 0: all 7 matrices (q,k,v,o 4096x4096; gate,up 11008x4096; "
+        "down 4096x11008), 128-wide rotation, 3x row RMS, core ||2z||^2<=16 encode")
+
+    w = workloads.small_f32(dev)
+    rec("small_f32", pool.run("project", _host(w.w), _host(w.scale), None, 0, -1, 64),
+        "256x256 float32, no rotation, row RMS: projection + dequantization (whole matrix)")
+    w = workloads.linear_4096(dev)
+    hw, hs, hsg = _host(w.w), _host(w.scale), _host(w.signs)
+    rec("linear_4096", pool.run("project", hw, hs, hsg, 128, -1, 256),
+        "4096x4096 bf16, 128-wide rotation, row RMS: projection + dequantization (whole matrix)")
+    rec("linear_4096_1core", pool.run("project", hw[:, :1024], hs[:1024], hsg, 128, -1, 256, single=True),
+        "first 1024 rows of the 4096x4096 projection, one worker")
+    del w
+    tot = [0, 0.0, 0.0, 0]
+    for kind in ("gate", "up", "down"):
+        m = workloads.moe_experts(dev, kind, experts=8)
+        r = pool.run("encode", _host(m.w), _host(m.scale), _host(m.signs), 128, 16, 256)
+        tot = [tot[0] + r[0], tot[1] + r[1], tot[2] + r[2], max(tot[3], r[3])]
+    rec("moe_experts", tuple(tot), "experts 0-7 of each kind (gate, up 768x2048; down 2048x768), Student-t, "
+        "128-wide rotation, 3x row RMS, core ||2z||^2<=16 encode")
+    q = workloads.qat_loop(dev)
+    rec("qat_forward", pool.run("project", _host(q.w), _host(q.scale), _host(q.signs), 128, 16, 256),
+        "4096x14336 bf16 latents, 128-wide rotation, 3x row RMS: projection + dequantization + escape count "
+        "(one QAT forward, whole matrix)")
+    del q
+    d = per["dense_decoder"]
+    head = {
+        "value": d["gweights_per_s"],
         "unit": "Gweights/s",
-        "cores": cores,
+        "cores": d["workers"],
         "kind": "oracle",
-        "sample": (f"{weights} weights: all 7 matrices of decoder block 0 (same seeds, scales, signs), "
-                   f"{len(jobs)} chunks of {chunk_rows} rows, {cpu_s:.1f} s of CPU time over {wall:.1f} s wall"),
+        "sample": (f"{d['weights']} weights: all 7 matrices of decoder block 0, the GPU's own input bits "
+                   f"(same seeds, scales, signs), {d['cpu_s']:.1f} s of CPU time over {d['wall_s']:.1f} s wall, "
+                   f"single-threaded numpy workers on {_cpu_model()}"),
     }
+    return head, {"cpu_model": _cpu_model(), "per_workload": per}
 
 
 # --------------------------------------------------------------------- GPU
@@ -111,17 +223,23 @@ def encode_bytes(batch, escapes):
     return (2 * weights + 4 * nb * rows + cols + 2 * (weights // 8) + 20 * escapes + 8 * nb)
 
 
-def run_dense_decoder(args, torch, e8q, workloads):
+def run_dense_decoder(args, torch, e8q, workloads, alpha=3.0, wide=False):
+    """All 224 matrices, three launches per step.  ``wide``: whole-row
+    power-of-two rotation blocks (4096 columns on 4096-wide rows, 256 on the
+    11008-wide rows) instead of 128."""
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
-    batches = workloads.dense_decoder(dev)
+    batches = workloads.dense_decoder(dev, alpha=alpha)
+    if wide:
+        for b in batches:
+            b.had_block = 4096 if b.w.shape[2] == 4096 else 256
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     bufs = []
     for b in batches:
         nb, rows, cols = b.w.shape
         groups = nb * rows * cols // 8
-        cap = groups // 16
+        cap = groups // 16 if alpha >= 2.0 else groups
         bufs.append({
             "core": torch.empty(groups, dtype=torch.int16, device=dev),
             "esc": torch.empty(cap * e8q.ESCAPE_RECORD_BYTES, dtype=torch.uint8, device=dev),
@@ -135,7 +253,7 @@ def run_dense_decoder(args, torch, e8q, workloads):
             if evs is not None:
                 evs[i][0].record()
             e8q.e8q_encode_core_escape(b.w, b.scale, 16, o["core"], o["esc"], o["cnt"], o["ws"], status,
-                                       signs=b.signs, had_block=128)
+                                       signs=b.signs, had_block=b.had_block)
             if evs is not None:
                 evs[i][1].record()
 
@@ -161,14 +279,15 @@ def run_dense_decoder(args, torch, e8q, workloads):
     achieved = sum(alg_bytes) / (kernel_ms * 1e-3) / 1e9
     rho = sum(escapes) / groups
     traffic = None   # measured HBM bytes: per launch (mean of the three) and per step
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(TRAFFIC_FILE) and alpha == 3.0 and not wide:
         tf = json.load(open(TRAFFIC_FILE))
         if tf.get("kernel_hash") == kernel_hash():
             per = [x["read"] + x["write"] for x in tf["per_launch_bytes"]]
             traffic = {"per_launch": round(sum(per) / len(per)), "per_step": tf.get("bytes_per_step"),
-                       "ratio_to_algorithmic": tf.get("ratio_to_algorithmic")}
+                       "ratio_to_algorithmic": tf.get("ratio_to_algorithmic"),
+                       "valu_per_group": tf.get("valu_per_group")}
     return {
-        "weights": weights, "wall": wall, "status": st, "escapes": escapes, "rho": rho,
+        "batches": batches, "weights": weights, "wall": wall, "status": st, "escapes": escapes, "rho": rho,
         "alg_bytes": alg_bytes, "launch_ms": launch_ms, "kernel_ms": kernel_ms, "achieved": achieved,
         "traffic": traffic, "gen_s": t_gen,
         "launches": [f"{b.w.shape[0]}x{b.w.shape[1]}x{b.w.shape[2]}" for b in batches],
@@ -412,17 +531,19 @@ def run_linear(args, torch, e8q, workloads):
                           "E8 projection + dequant to bf16")
 
 
-def run_moe(args, torch, e8q, workloads):
+def run_moe(args, torch, e8q, workloads, alpha=3.0):
     """128 experts x {gate, up, down} Student-t weights, 128-wide rotation,
-    scale 3 x RMS, encode (three launches per step)."""
+    scale alpha x RMS (3 by default, 1 for the stress run), encode (three
+    launches per step)."""
     dev = torch.device("cuda:0")
-    batches = [workloads.moe_experts(dev, k) for k in ("gate", "up", "down")]
+    batches = [workloads.moe_experts(dev, k, alpha=alpha) for k in ("gate", "up", "down")]
     bufs = []
     for bt in batches:
         nb, rows, cols = bt.w.shape
         groups = nb * rows * cols // 8
+        cap = groups // 16 if alpha >= 2.0 else groups
         bufs.append((torch.empty(groups, dtype=torch.int16, device=dev),
-                     torch.empty((groups // 16) * e8q.ESCAPE_RECORD_BYTES, dtype=torch.uint8, device=dev),
+                     torch.empty(cap * e8q.ESCAPE_RECORD_BYTES, dtype=torch.uint8, device=dev),
                      torch.empty(nb, dtype=torch.int64, device=dev),
                      torch.empty(e8q.e8q_encode_workspace_size(nb, rows, cols), dtype=torch.uint8, device=dev)))
     status = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -434,7 +555,8 @@ def run_moe(args, torch, e8q, workloads):
     n = sum(bt.w.numel() for bt in batches)
     r = _time_launches(args, torch, launch, n, None, status,
                        "moe 128 experts x (gate 768x2048, up 768x2048, down 2048x768) bf16 Student-t nu=4 std 0.02; "
-                       "128-wide Walsh-Hadamard; scale 3x row RMS; core ||2z||^2<=16 encode, per-expert escapes")
+                       f"128-wide Walsh-Hadamard; scale {alpha:g}x row RMS; core ||2z||^2<=16 encode, "
+                       "per-expert escapes")
     esc = sum(int(b[2].sum().item()) for b in bufs)
     r["alg_bytes"] = sum(encode_bytes(bt, int(b[2].sum().item())) for bt, b in zip(batches, bufs))
     r["escapes"] = esc
@@ -456,16 +578,18 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
     b = workloads.qat_loop(dev)
     w = b.w[0].clone()
     q = torch.empty_like(w)
-    esc = torch.empty(1, dtype=torch.int64, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     nsteps = args.steps + args.warmup
+    esc = torch.zeros(nsteps, dtype=torch.int64, device=dev)    # escape count of every step
     grads = [workloads.qat_grad(k, w.shape, dev) for k in range(nsteps)]
 
     def fwd_rotated(k):
-        e8q.e8q_project_hadamard(w, b.scale, b.signs, 128, status, q_out=q, core_bound=16, esc_count_out=esc)
+        e8q.e8q_project_hadamard(w, b.scale, b.signs, 128, status, q_out=q, core_bound=16,
+                                 esc_count_out=esc[k:k + 1])
 
     def fwd_restore(k):
-        e8q.e8q_project_hadamard_restore(w, b.scale, b.signs, 128, q, status, core_bound=16, esc_count_out=esc)
+        e8q.e8q_project_hadamard_restore(w, b.scale, b.signs, 128, q, status, core_bound=16,
+                                         esc_count_out=esc[k:k + 1])
 
     def bwd_identity(k):
         e8q.e8q_ste_backward(grads[k], w_latent=w, lr=1.0)
@@ -484,9 +608,15 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
                              "fused with SGD"),
     }[mode]
     n = w.numel()
-    return _time_launches(args, torch, parts, n, 10 * n, status,
-                          f"qat step 4096x14336 bf16 latents: {desc} (lr 1, grad N(0,1e-4^2))",
-                          steps_offset=True)
+    r = _time_launches(args, torch, parts, n, 10 * n, status,
+                       f"qat step 4096x14336 bf16 latents: {desc} (lr 1, grad N(0,1e-4^2))",
+                       steps_offset=True)
+    series = esc.cpu().tolist()
+    r["parts"]["escapes_per_step"] = series          # warmup steps first, then the timed steps
+    r["parts"]["escapes_first_last"] = [series[0], series[-1]]
+    r["parts"]["escapes_min_mean_max"] = [min(series), sum(series) / len(series), max(series)]
+    r["escapes"] = series[-1]
+    return r
 
 
 def _time_launches(args, torch, parts, weights, bytes_per_step, status, workload, steps_offset=False):
@@ -516,8 +646,7 @@ def _time_launches(args, torch, parts, weights, bytes_per_step, status, workload
             "status": int(status.item()), "workload": workload, "parts": detail}
 
 
-ALG_OPS_PER_WEIGHT = 15        # 7 butterfly adds (b = 128), 1 scale multiply, ~7 decoder ops
-VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # non-packed VALU lane-ops/s: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+DECODER_CONFIGS = {"decoder": (3.0, False), "decoder_alpha1": (1.0, False), "decoder_wide": (3.0, True)}
 
 
 def main():
@@ -526,11 +655,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder",
-                    choices=["decoder", "linear", "moe", "qat", "qat_restore", "qat_rotated_grad",
-                             "decode", "decode_q", "gemv", "pack", "ptq"])
+                    choices=list(DECODER_CONFIGS) + ["linear", "moe", "moe_alpha1", "qat", "qat_restore",
+                                                     "qat_rotated_grad", "decode", "decode_q", "gemv", "pack",
+                                                     "ptq"])
     ap.add_argument("--gemv-m", type=int, default=1, choices=[1, 2])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=1)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (known bytes) for counter scaling")
     args = ap.parse_args()
@@ -540,7 +669,8 @@ def main():
               "(the encode shards by whole matrices with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
-    cpu = None if (args.no_cpu_baseline or args.config != "decoder") else cpu_baseline(args.cpu_blocks)
+    # the oracle's workers are forked before anything touches the GPU
+    pool = OraclePool() if (not args.no_cpu_baseline and args.config == "decoder") else None
 
     import torch
     import bit_e8_lattice_amd as e8q
@@ -554,7 +684,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.config != "decoder":
+    if args.config not in DECODER_CONFIGS:
         if args.config.startswith("qat"):
             r = run_qat(args, torch, e8q, workloads, args.config)
         elif args.config == "gemv":
@@ -565,8 +695,10 @@ def main():
             r = run_ptq(args, torch, e8q, workloads)
         elif args.config.startswith("decode"):
             r = run_decode(args, torch, e8q, workloads, args.config)
+        elif args.config.startswith("moe"):
+            r = run_moe(args, torch, e8q, workloads, alpha=1.0 if args.config == "moe_alpha1" else 3.0)
         else:
-            r = {"linear": run_linear, "moe": run_moe}[args.config](args, torch, e8q, workloads)
+            r = run_linear(args, torch, e8q, workloads)
         gbs = r["alg_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
         out = {
             "metric": f"{args.config}: {r.get('unit_override', 'Gweights/s')} and % of HBM peak BW, 1xMI355X",
@@ -584,14 +716,27 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
-    r = run_dense_decoder(args, torch, e8q, workloads)
+    alpha, wide = DECODER_CONFIGS[args.config]
+    r = run_dense_decoder(args, torch, e8q, workloads, alpha=alpha, wide=wide)
     if r["status"] != 0:
         print(f"warning: device status bits {r['status']:#x}", file=sys.stderr)
+    cpu, cpu_detail = None, None
+    if pool is not None:
+        try:
+            cpu, cpu_detail = cpu_oracle_rates(pool, torch, workloads, r["batches"])
+        finally:
+            pool.close()
 
     ms_per_step = r["wall"] * 1e3 / args.steps
     value = r["weights"] * args.steps / r["wall"] / 1e9
-    hbm_gbs = r["achieved"]
-    alu = ALG_OPS_PER_WEIGHT * r["weights"] / (r["kernel_ms"] * 1e-3) / 1e12
+    # roofline of the encode launches: algorithmic bytes per launch over the
+    # launch's mean duration (HIP events on the launching stream, timed steps only)
+    nl = len(r["launches"])
+    launch_mean_ms = [sum(x[i] for x in r["launch_ms"]) / args.steps for i in range(nl)]
+    bytes_per_launch = sum(r["alg_bytes"]) / nl
+    ms_per_launch = sum(launch_mean_ms) / nl
+    achieved = bytes_per_launch / (ms_per_launch * 1e-3) / 1e9
+    blocks = "4096 (4096-column rows) / 256 (11008-column rows)" if wide else "128"
     out = {
         "metric": "Gweights/s projected+encoded and % of HBM peak BW, 1xMI355X vs CPU oracle",
         "value": round(value, 3),
@@ -607,38 +752,39 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": ("dense decoder 32 blocks x (q,k,v,o 4096x4096; gate,up 11008x4096; down 4096x11008) "
-                         "bf16 N(0,0.02^2); sign flip + 128-wide Walsh-Hadamard; scale 3x row RMS; "
-                         "E8 projection + core ||2z||^2<=16 index + escape records"),
+                         f"bf16 N(0,0.02^2); sign flip + {blocks}-column Walsh-Hadamard blocks; "
+                         f"scale {alpha:g}x row RMS; E8 projection + core ||2z||^2<=16 index + escape records"),
             "weights": r["weights"],
             "launches": r["launches"],
             "core_bound": 16,
-            "had_block": 128,
+            "had_block": 0 if wide else 128,
+            "alpha": alpha,
         },
         "roofline": {
-            "bound": "alu",
-            "achieved": round(alu, 3),
-            "peak": round(VALU_PEAK_TOPS, 2),
-            "unit": "Tops/s",
-            "frac": round(alu / VALU_PEAK_TOPS, 4),
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": r["traffic"]["per_launch"] if r["traffic"] else None,
         },
         "cpu_baseline": cpu,
         "detail": {
-            "hbm_achieved_gbs": round(hbm_gbs, 1),
-            "hbm_peak_gbs": HBM_PEAK_GBS,
-            "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-            "alg_ops_per_weight": ALG_OPS_PER_WEIGHT,
+            "target_frac": 0.70,
             "kernel_ms_per_step": round(r["kernel_ms"], 4),
-            "launch_ms_mean": [round(sum(x[i] for x in r["launch_ms"]) / args.steps, 4) for i in range(3)],
+            "launch_ms_mean": [round(x, 4) for x in launch_mean_ms],
             "alg_bytes_per_step": sum(r["alg_bytes"]),
+            "alg_bytes_per_launch": round(bytes_per_launch),
             "hbm_traffic_bytes_per_step": r["traffic"]["per_step"] if r["traffic"] else None,
             "hbm_traffic_ratio_to_algorithmic": r["traffic"]["ratio_to_algorithmic"] if r["traffic"] else None,
+            "valu_per_group": r["traffic"].get("valu_per_group") if r["traffic"] else None,
             "escapes": sum(r["escapes"]),
             "rho": r["rho"],
             "payload_bits_per_weight": 2 + 20 * r["rho"],
             "status": r["status"],
             "input_gen_s": round(r["gen_s"], 1),
             "kernel_hash": kernel_hash(),
+            "cpu_oracle": cpu_detail,
         },
     }
     print(json.dumps(out), flush=True)
