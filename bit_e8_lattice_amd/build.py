@@ -18,8 +18,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libe8q.so")
 
-SOURCES = ["e8q_common.hip", "e8q_project.hip", "e8q_encode.hip", "e8q_ste.hip", "e8q_decode.hip",
-           "e8q_roots.hip", "e8q_ptq.hip", "e8q_core_table.cpp"]
+SOURCES = ["e8q_common.hip", "e8q_tables.hip", "e8q_project.hip", "e8q_encode.hip", "e8q_ste.hip",
+           "e8q_decode.hip", "e8q_roots.hip", "e8q_ptq.hip"]
+# host program run before the library is compiled: writes the device table
+# blob and its layout header (embedded by e8q_tables.hip)
+TABLEGEN_SOURCES = ["e8q_tablegen.cpp", "e8q_tables_build.cpp", "e8q_core_table.cpp"]
 
 # -ffp-contract=off: every float32 step is one IEEE operation (no fused
 # multiply-add), which the bit-exact contract in include/e8q.h relies on.
@@ -49,13 +52,33 @@ def _filtered(res):
                      if "packed-fp32-ops" not in l and l.strip())
 
 
+def gen_tables(tmpdir, verbose=False):
+    """Compile and run the table generator; the blob and header land in tmpdir."""
+    exe = os.path.join(tmpdir, "e8q_tablegen")
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if not cxx:
+        raise RuntimeError("no host C++ compiler for the table generator")
+    cmd = [cxx, "-O2", "-std=c++17", "-I", CSRC, "-o", exe] + [os.path.join(CSRC, s) for s in TABLEGEN_SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"table generator build failed:\n{res.stdout}{res.stderr}")
+    res = subprocess.run([exe, tmpdir], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"table generator failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+
+
 def build(verbose=False, jobs=None):
     jobs = jobs or min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with tempfile.TemporaryDirectory(prefix="e8q_build_") as tmpdir:
+        gen_tables(tmpdir, verbose)
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmpdir, src + ".o")
-            cmd = [hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-I", INCLUDE, "-I", CSRC, "-I", tmpdir,
+                                                                   f"--embed-dir={tmpdir}", "-c",
+                                                                   os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             objs.append(obj)

@@ -20,6 +20,7 @@
 // state)*nh, nstate = 2*(B/4 + 1).
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <vector>

@@ -321,7 +321,7 @@ template <typename K>
 static void launch_restore(K kernel, const DecodeArgs& a, size_t lds, hipStream_t st) {
     const uint64_t resident = resident_grid(reinterpret_cast<const void*>(kernel), kBlock, lds, a.num_tiles);
     const uint64_t grid = std::min<uint64_t>(a.num_tiles, std::max<uint64_t>(resident, (uint64_t(a.num_tiles) + 15) / 16));
-    hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kBlock), lds, st, a);
+    launch(kernel, dim3(unsigned(grid)), dim3(kBlock), lds, st, a);
 }
 
 template <bool RESTORE, bool LDS_PTS>
@@ -331,7 +331,7 @@ static void launch_decode(int hb, const DecodeArgs& a, size_t lds, hipStream_t s
         // is one copy of the point table: one block per tile (the hardware
         // dispatcher keeps every CU full) decodes faster than resident blocks
         // that loop over tiles.
-        hipLaunchKernelGGL((decode_kernel<8, false, LDS_PTS>), dim3(a.num_tiles), dim3(kBlock), lds, st, a);
+        launch((decode_kernel<8, false, LDS_PTS>), dim3(a.num_tiles), dim3(kBlock), lds, st, a);
         return;
     }
     switch (hb) {
@@ -408,7 +408,7 @@ extern "C" e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx, const e
     a.cols = uint32_t(cols);
     a.pts = tab->dpoints;
     a.h8 = tab->dh8;
-    a.npts = uint32_t(tab->host.size);
+    a.npts = uint32_t(tab->size);
     a.two_z = two_z_out;
     a.q = q_out;
     a.q_bf16 = q_dtype == E8Q_BF16;
@@ -418,7 +418,7 @@ extern "C" e8q_status_t e8q_decode_core_escape(const uint16_t* core_idx, const e
     a.num_tiles = uint32_t((uint64_t(a.groups) + kTileGroups - 1) / kTileGroups);
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
+    launch(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
                        uint64_t(esc_capacity), static_cast<uint64_t*>(workspace));
     const bool need_2z = q_out != nullptr || two_z_out != nullptr;
     const size_t pts_lds = size_t(a.npts) * 8 * ((need_2z ? 1 : 0) + (restore ? 1 : 0));
@@ -892,9 +892,9 @@ static size_t gemv_ws_bytes(int64_t batch, int64_t m, int64_t cols) {
 template <int M>
 static void launch_gemv(bool lds_pts, const GemvArgs& a, dim3 grid, size_t lds, hipStream_t st) {
     if (lds_pts)
-        hipLaunchKernelGGL((gemv_kernel<M, true>), grid, dim3(kGemvThreads), lds, st, a);
+        launch((gemv_kernel<M, true>), grid, dim3(kGemvThreads), lds, st, a);
     else
-        hipLaunchKernelGGL((gemv_kernel<M, false>), grid, dim3(kGemvThreads), lds, st, a);
+        launch((gemv_kernel<M, false>), grid, dim3(kGemvThreads), lds, st, a);
 }
 
 template <int M>
@@ -960,7 +960,7 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint64_t* offsets = static_cast<uint64_t*>(workspace);
     float* xt = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ws_bytes(batch));
-    hipLaunchKernelGGL(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
+    launch(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
                        uint64_t(esc_capacity), offsets);
 
     RotArgs ra;
@@ -984,7 +984,7 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
         // the matrix-core path
         uint4* xb = reinterpret_cast<uint4*>(reinterpret_cast<char*>(xt) + gemv_xt_bytes(batch, m, cols));
         const uint32_t xg = uint32_t(uint64_t(batch) * uint64_t(m) * gpr);
-        hipLaunchKernelGGL(gemv_split_kernel, dim3(grid_for(xg, 256, 8)), dim3(256), 0, s, xt, xb, gpr, xg);
+        launch(gemv_split_kernel, dim3(grid_for(xg, 256, 8)), dim3(256), 0, s, xt, xb, gpr, xg);
         GemvMfmaArgs gm;
         gm.core_idx = core_idx;
         gm.esc = reinterpret_cast<const uint32_t*>(esc);
@@ -993,7 +993,7 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
         gm.xb = xb;
         gm.scale = row_scale;
         gm.tab = tab->dpts_bf16;
-        gm.npts = uint32_t(tab->host.size);
+        gm.npts = uint32_t(tab->size);
         gm.rows = uint32_t(rows);
         gm.gpr = gpr;
         gm.tiles_per_b = uint32_t((rows + kGmRows - 1) / kGmRows);
@@ -1013,7 +1013,7 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
     ga.xt = xt;
     ga.scale = row_scale;
     ga.pts = tab->dpoints;
-    ga.npts = uint32_t(tab->host.size);
+    ga.npts = uint32_t(tab->size);
     ga.rows = uint32_t(rows);
     ga.cols = uint32_t(cols);
     ga.gpr = uint32_t(cols / 8);

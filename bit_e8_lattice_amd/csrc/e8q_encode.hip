@@ -530,12 +530,6 @@ void launch_encode(int hb, const EncodeArgs& a, size_t lds, hipStream_t st) {
 
 }  // namespace
 
-int64_t core_size_host(int32_t bound) {
-    CoreTable t;
-    if (!build_core_table(bound, t)) return -1;
-    return t.size;
-}
-
 // Workspace: [counter][tile status words][row coefficients][per-tile escape
 // counts][staged records, kStagedRecs per tile].
 size_t encode_ws_bytes(int64_t batch, int64_t rows, int64_t cols) {
@@ -552,15 +546,14 @@ extern "C" size_t e8q_encode_workspace_size(int64_t batch, int64_t rows, int64_t
     return e8q::encode_ws_bytes(batch, rows, cols);
 }
 
-extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtype, int64_t batch,
-                                               int64_t rows, int64_t cols, const float* row_scale,
-                                               const int8_t* signs, int32_t had_block,
-                                               int32_t core_bound, uint16_t* core_idx_out,
-                                               e8q_escape_t* esc_out, int64_t esc_capacity,
-                                               int64_t* esc_count_out, int8_t* two_z_out,
-                                               void* workspace, size_t workspace_bytes,
-                                               uint32_t* status_dev, void* stream) {
-    using namespace e8q;
+namespace e8q {
+namespace {
+
+e8q_status_t encode_impl(const void* w, e8q_dtype_t w_dtype, int64_t batch, int64_t rows, int64_t cols,
+                         const float* row_scale, const int8_t* signs, int32_t had_block, int32_t core_bound,
+                         uint16_t* core_idx_out, e8q_escape_t* esc_out, int64_t esc_capacity,
+                         int64_t* esc_count_out, int8_t* two_z_out, void* workspace, size_t workspace_bytes,
+                         uint32_t* status_dev, void* stream) {
     e8q_status_t st = check_shape(w, w_dtype, batch, rows, cols, row_scale, status_dev);
     if (st != E8Q_OK) return st;
     if (!core_idx_out || !esc_count_out || !workspace) return E8Q_ERR_INVALID;
@@ -576,7 +569,7 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
     }
     const DevTable* tab = get_table(core_bound, st);
     if (!tab) return st;
-    const RankParams& rp = tab->host.p;
+    const RankParams& rp = tab->p;
 
     const uint32_t gpr = uint32_t(cols / 8);
     const uint32_t rows_total = uint32_t(batch * rows);
@@ -624,7 +617,7 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
     uint32_t init_items = a.num_tiles;
     if (uint32_t(batch) > init_items) init_items = uint32_t(batch);
     if (rows_total > init_items) init_items = rows_total;
-    hipLaunchKernelGGL(encode_init_kernel, dim3(grid_for(init_items, 256, 4)), dim3(256), 0, s, a.tile_counter,
+    launch(encode_init_kernel, dim3(grid_for(init_items, 256, 4)), dim3(256), 0, s, a.tile_counter,
                        a.tile_status, a.num_tiles, a.esc_count, uint32_t(batch), row_scale, coef, rows_total,
                        kappa_for(hb));
 
@@ -640,6 +633,22 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
         else launch_encode<float, false, false>(hb, a, lds, s);
     }
     const uint64_t segments = (uint64_t(a.num_tiles) + kAnchorTiles - 1) / kAnchorTiles;
-    hipLaunchKernelGGL(encode_place_kernel, dim3(unsigned((segments + 3) / 4)), dim3(256), 0, s, a);
+    launch(encode_place_kernel, dim3(unsigned((segments + 3) / 4)), dim3(256), 0, s, a);
     return launch_status();
+}
+
+}  // namespace
+}  // namespace e8q
+
+extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtype, int64_t batch,
+                                               int64_t rows, int64_t cols, const float* row_scale,
+                                               const int8_t* signs, int32_t had_block,
+                                               int32_t core_bound, uint16_t* core_idx_out,
+                                               e8q_escape_t* esc_out, int64_t esc_capacity,
+                                               int64_t* esc_count_out, int8_t* two_z_out,
+                                               void* workspace, size_t workspace_bytes,
+                                               uint32_t* status_dev, void* stream) {
+    return e8q::encode_impl(w, w_dtype, batch, rows, cols, row_scale, signs, had_block, core_bound, core_idx_out,
+                            esc_out, esc_capacity, esc_count_out, two_z_out, workspace, workspace_bytes, status_dev,
+                            stream);
 }

@@ -8,20 +8,23 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
+#include <utility>
 
 #include "e8q.h"
 #include "e8q_core_table.hpp"
+#include "e8q_tables_build.hpp"
 
 namespace e8q {
 
-// Core tables of one core bound on one device: the rank table (uint16) and the
-// points in rank order (two uint32 words per point), uploaded on first use
-// and kept for the life of the process.
+// Core tables of one core bound on one device: pointers into the table blob
+// that the device code object carries (built with the library, see
+// e8q_tables_build.hpp), and the host-side rank parameters.
 struct DevTable {
-    uint16_t* dptr = nullptr;
-    uint32_t* dpoints = nullptr;
-    uint32_t* droots = nullptr;   // the 240 roots (same word layout as the points)
-    double* dpts64 = nullptr;     // points in rank order as 9 doubles: t_0..t_7 (= 2z), ||t||^2 / 4
+    const uint16_t* dptr = nullptr;      // rank table
+    const uint32_t* dpoints = nullptr;   // points in rank order, two words each (2z + 64 bytes)
+    const uint32_t* droots = nullptr;    // the 240 roots (same word layout as the points)
+    const double* dpts64 = nullptr;      // points in rank order as 9 doubles: t_0..t_7 (= 2z), ||t||^2 / 4
     // The points grouped by norm shell into tiles of 32 rows for the
     // matrix-core search, one of each pair +-t (first nonzero coordinate
     // positive; the origin alone); a shell's last tile is padded with zero
@@ -33,21 +36,21 @@ struct DevTable {
     //   ntiles * 768 : 32 uint16 core indices of t (pads: the origin's)  64 B
     //   ntiles * 832 : 32 uint16 core indices of -t (pads: the origin's) 64 B
     //   ntiles * 896 : the shell's ||t||^2 / 4 as float        4 B per tile
-    uint8_t* dtiles = nullptr;
+    const uint8_t* dtiles = nullptr;
     uint32_t ntiles = 0;
     // The points in rank order as 8 bfloat16 (2z) each, plus a zero entry at
     // index |C(B)| (the GEMV's matrix-core operand table).
-    uint4* dpts_bf16 = nullptr;
+    const uint4* dpts_bf16 = nullptr;
     // H_8 (2z) of every point (natural-order 8-point Walsh-Hadamard transform,
     // exact in integers, |entry| <= 48 for any supported core) as signed bytes,
     // two words per point in the layout of the points.
-    uint32_t* dh8 = nullptr;
-    CoreTable host;
+    const uint32_t* dh8 = nullptr;
+    RankParams p{};      // rank parameters of the canonical bound 8 * floor(B / 8)
+    int64_t size = 0;    // |C(B)|
 };
 
-constexpr uint32_t kTileRows = 32;
-
-// Tables for (current device, bound); nullptr with err set on failure.
+// Tables for (current device, bound), bound in [0, 40]; nullptr with err set
+// on failure.  A host-side lookup: nothing is allocated or enqueued.
 const DevTable* get_table(int32_t bound, e8q_status_t& err);
 
 // Number of compute units of the current device (cached per device).
@@ -93,11 +96,31 @@ inline unsigned resident_grid(const void* func, unsigned block, size_t lds, uint
 }
 
 
+// First launch error of the entry point running on this thread; launch()
+// records it and launch_status() reports and clears it, so a failure is
+// reported by the call whose launch failed and never by a later one.
+inline thread_local hipError_t g_launch_err = hipSuccess;
+
+// Enqueues `kernel` with `args` (converted to its parameter types) and records
+// a failed launch.
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st, Args&&... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<std::decay_t<KArgs>...> conv(std::forward<Args>(args)...);
+    void* argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1] = {nullptr};
+    std::apply([&argv](auto&... a) {
+        size_t i = 0;
+        ((argv[i++] = static_cast<void*>(&a)), ...);
+    }, conv);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, st);
+    if (e != hipSuccess && g_launch_err == hipSuccess) g_launch_err = e;
+}
+
 template <typename A>
 inline void launch_tiles(void (*kernel)(A), const A& args, uint64_t tiles, unsigned block, size_t lds,
                          hipStream_t st) {
     const unsigned grid = resident_grid(reinterpret_cast<const void*>(kernel), block, lds, tiles);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), lds, st, args);
+    launch(kernel, dim3(grid), dim3(block), lds, st, args);
 }
 
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -127,8 +150,11 @@ inline float kappa_for(int32_t had_block) {
     return had_block > 0 ? float(1.0 / __builtin_sqrt(double(had_block))) : 1.0f;
 }
 
+// Result of the launches made since the last call (see launch()).
 inline e8q_status_t launch_status() {
-    return hipGetLastError() == hipSuccess ? E8Q_OK : E8Q_ERR_LAUNCH;
+    const hipError_t e = g_launch_err;
+    g_launch_err = hipSuccess;
+    return e == hipSuccess ? E8Q_OK : E8Q_ERR_LAUNCH;
 }
 
 }  // namespace e8q

@@ -345,7 +345,7 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (esc_count_out) {
-        hipLaunchKernelGGL(zero_u64_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, s,
+        launch(zero_u64_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, s,
                            a.esc, uint32_t(batch));
     }
     if (w_hat_out) {

@@ -448,20 +448,20 @@ extern "C" e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype, int64_t
     a.kappa = kappa_for(hb);
     a.core_bound = core_bound;
     a.pts64 = tab->dpts64;
-    a.npts = uint32_t(tab->host.size);
+    a.npts = uint32_t(tab->size);
     a.tiles = tab->dtiles;
     a.ntiles = tab->ntiles;
     a.tmax = floorf(sqrtf(float(core_bound)));
     a.nmax4 = float(core_bound) / 4.0f;
     a.big = 3.0e38f;
     a.tab = tab->dptr;
-    a.rp = tab->host.p;
+    a.rp = tab->p;
     a.scale_out = scale_out;
     a.choice_out = choice_out;
     a.err_out = err_out;
     a.core_idx = core_idx_out;
     a.two_z = two_z_out;
     a.status = status_dev;
-    hipLaunchKernelGGL(ptq_kernel, dim3(unsigned(rows_total)), dim3(kPtqThreads), lds, s, a);
+    launch(ptq_kernel, dim3(unsigned(rows_total)), dim3(kPtqThreads), lds, s, a);
     return launch_status();
 }

@@ -272,8 +272,8 @@ static e8q_status_t prepare(RootArgs& a, int64_t n, int32_t core_bound, void* wo
     a.n = uint64_t(n);
     a.roots = tab->droots;
     a.tab = tab->dptr;
-    a.rp = tab->host.p;
-    a.npts = uint32_t(tab->host.size);
+    a.rp = tab->p;
+    a.npts = uint32_t(tab->size);
     a.pts = tab->dpoints;
     a.core_bound = core_bound;
     a.block_counts = static_cast<uint64_t*>(workspace);
@@ -308,13 +308,13 @@ extern "C" e8q_status_t e8q_pack_escapes(const e8q_escape_t* esc, int64_t n, int
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const uint64_t nb = (uint64_t(n) + kRootBlock - 1) / kRootBlock;
     if (nb == 0) {
-        hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, s, a.block_counts, uint64_t(0),
+        launch(scan_counts_kernel, dim3(1), dim3(1024), 0, s, a.block_counts, uint64_t(0),
                            wide_count_out);
         return launch_status();
     }
-    hipLaunchKernelGGL(pack_kernel, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
-    hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, s, a.block_counts, nb, wide_count_out);
-    hipLaunchKernelGGL(place_kernel<true>, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
+    launch(pack_kernel, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
+    launch(scan_counts_kernel, dim3(1), dim3(1024), 0, s, a.block_counts, nb, wide_count_out);
+    launch(place_kernel<true>, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
     return launch_status();
 }
 
@@ -337,8 +337,8 @@ extern "C" e8q_status_t e8q_unpack_escapes(const e8q_escape_packed_t* packed, in
     a.wide_cap = uint64_t(wide_count);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const uint64_t nb = (uint64_t(n) + kRootBlock - 1) / kRootBlock;
-    hipLaunchKernelGGL(unpack_count_kernel, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
-    hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, s, a.block_counts, nb, nullptr);
-    hipLaunchKernelGGL(place_kernel<false>, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
+    launch(unpack_count_kernel, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
+    launch(scan_counts_kernel, dim3(1), dim3(1024), 0, s, a.block_counts, nb, nullptr);
+    launch(place_kernel<false>, dim3(unsigned(nb)), dim3(kRootThreads), 0, s, a);
     return launch_status();
 }

@@ -256,11 +256,11 @@ extern "C" e8q_status_t e8q_ste_backward(const void* grad_q, void* grad_w, void*
     if (vec) {
         const unsigned grid = grid_for(vec, 256, 8);
         if (dtype == E8Q_BF16)
-            hipLaunchKernelGGL(ste_bf16_kernel, dim3(grid), dim3(256), 0, s,
+            launch(ste_bf16_kernel, dim3(grid), dim3(256), 0, s,
                                static_cast<const uint4*>(grad_q), static_cast<uint4*>(grad_w),
                                static_cast<uint4*>(w_latent), lr, vec);
         else
-            hipLaunchKernelGGL(ste_f32_kernel, dim3(grid), dim3(256), 0, s,
+            launch(ste_f32_kernel, dim3(grid), dim3(256), 0, s,
                                static_cast<const float4*>(grad_q), static_cast<float4*>(grad_w),
                                static_cast<float4*>(w_latent), lr, vec);
     }
@@ -268,7 +268,7 @@ extern "C" e8q_status_t e8q_ste_backward(const void* grad_q, void* grad_w, void*
     if (done < uint64_t(n)) {
         const uint64_t rest = uint64_t(n) - done;
         const unsigned grid = grid_for(rest, 256, 4);
-        hipLaunchKernelGGL(ste_tail_kernel, dim3(grid), dim3(256), 0, s, grad_q, grad_w, w_latent, lr,
+        launch(ste_tail_kernel, dim3(grid), dim3(256), 0, s, grad_q, grad_w, w_latent, lr,
                            int(dtype == E8Q_BF16), done, uint64_t(n));
     }
     return launch_status();

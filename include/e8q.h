@@ -22,8 +22,9 @@
  *       non-positive size, cols not a multiple of 8, bad block size or core
  *       bound, too small workspace), E8Q_ERR_UNSUPPORTED (a dtype or size
  *       combination the library does not implement), E8Q_ERR_LAUNCH (the HIP
- *       launch failed), E8Q_ERR_DEVICE (a device query or the one-time rank
- *       table upload failed).  Nothing is launched when a check fails.
+ *       launch failed), E8Q_ERR_DEVICE (a device query failed).  Nothing is
+ *       launched when a check fails; E8Q_ERR_LAUNCH comes from this call's own
+ *       launches, never from an error left by other code.
  *   - Conditions that depend on the data are reported by OR-ing E8Q_STATUS_*
  *     bits into `*status_dev` (a device uint32 the caller zeroes beforehand).
  *   - Weights are [batch, rows, cols] row-major; a group is 8 consecutive
@@ -32,7 +33,10 @@
  *   - Lattice points are reported as 2z (integers): z is in E8 = D8 u (D8+1/2)
  *     iff all 2z_i are even or all odd and sum(2z) = 0 mod 4.
  *   - Calls on different streams may run concurrently; the library keeps no
- *     mutable device state between calls except the read-only rank tables.
+ *     mutable device state between calls.  Its read-only tables (core ranks,
+ *     points, roots) are generated when the library is built and are part of
+ *     its device code object: no call allocates, frees, uploads or
+ *     synchronizes.
  *
  * Numerics (bit-exact contract; the CPU oracle computes the same):
  *   v = w (float32, bf16 widened exactly)

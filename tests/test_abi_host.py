@@ -143,3 +143,52 @@ def test_ste_hadamard_rejects(L):
         assert L.e8q_ste_backward_hadamard(*args) == 1, args
     # rows wider than the LDS sign table
     assert L.e8q_ste_backward_hadamard(FAKE, 1, 4, 65536, FAKE, 128, FAKE, None, 1.0, None) == 2
+
+
+def _device_code_objects(path):
+    """The gfx950 code objects inside the library's fat binaries (one per
+    source file): ELF images found in the .hip_fatbin section."""
+    objcopy = "/opt/rocm/llvm/bin/llvm-objcopy"
+    if not os.path.exists(objcopy):
+        pytest.skip("llvm-objcopy not available")
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "fatbin")
+        subprocess.run([objcopy, "--dump-section=.hip_fatbin=" + out, path, os.path.join(d, "stripped")],
+                       check=True, capture_output=True)
+        data = open(out, "rb").read()
+    objs, i = [], data.find(b"\x7fELF")
+    while i >= 0:
+        objs.append(data[i:])
+        i = data.find(b"\x7fELF", i + 4)
+    return objs
+
+
+def _symbols(elf):
+    """(name, size, section index) of every symbol of a 64-bit ELF image."""
+    import struct
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum = struct.unpack_from("<HH", elf, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQIIQQ", elf, shoff + k * shentsize) for k in range(shnum)]
+    out = []
+    for (_, typ, _, _, off, size, link, _, _, entsize) in secs:
+        if typ != 2:                                  # SHT_SYMTAB
+            continue
+        stroff = secs[link][4]
+        for k in range(size // entsize):
+            name_off, _, _, shndx, _, sz = struct.unpack_from("<IBBHQQ", elf, off + k * entsize)
+            end = elf.index(b"\0", stroff + name_off)
+            out.append((elf[stroff + name_off:end].decode(), sz, shndx))
+    return out
+
+
+def test_device_tables_in_code_object(L):
+    """The read-only tables live in the device code object (no call uploads
+    them): a defined device symbol of the generated blob's size."""
+    import bit_e8_lattice_amd as e8q
+    found = [(n, sz, ndx) for elf in _device_code_objects(e8q.library_path) for (n, sz, ndx) in _symbols(elf)
+             if "g_table_blob" in n]
+    assert found, "table blob missing from the device code objects"
+    assert all(ndx != 0 for (_, _, ndx) in found)
+    assert max(sz for (_, sz, _) in found) > 10_000_000
