@@ -15,7 +15,8 @@ import torch
 __all__ = [
     "E8QError", "lib", "library_path",
     "e8q_project", "e8q_project_hadamard", "e8q_project_hadamard_restore",
-    "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_ste_backward",
+    "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_encode_core_escape_noalloc",
+    "ENCODE_NOALLOC_SCRATCH_BYTES", "e8q_ste_backward",
     "e8q_ste_backward_hadamard", "e8q_decode_core_escape", "e8q_decode_workspace_size",
     "e8q_gemv_core_escape", "e8q_gemv_workspace_size", "e8q_pack_escapes", "e8q_unpack_escapes",
     "e8q_pack_workspace_size", "PACKED_RECORD_BYTES", "e8q_ptq_init", "e8q_ptq_workspace_size",
@@ -26,6 +27,7 @@ __all__ = [
 
 F32, BF16 = 0, 1
 ESCAPE_RECORD_BYTES = 20
+ENCODE_NOALLOC_SCRATCH_BYTES = 64 << 20      # E8Q_ENCODE_NOALLOC_SCRATCH_BYTES
 PACKED_RECORD_BYTES = 8
 STATUS_BITS = {
     "NONFINITE": 1, "BAD_SCALE": 2, "INT8_RANGE": 4, "ESC_OVERFLOW": 8,
@@ -85,6 +87,9 @@ def lib():
     L.e8q_encode_core_escape.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
                                          vp, sz, vp, vp]
     L.e8q_encode_core_escape.restype = e
+    L.e8q_encode_core_escape_noalloc.argtypes = [vp, e, i64, i64, i64, vp, vp, i32, i32, vp, vp, i64, vp, vp,
+                                                 vp, vp]
+    L.e8q_encode_core_escape_noalloc.restype = e
     L.e8q_encode_workspace_size.argtypes = [i64, i64, i64]
     L.e8q_encode_workspace_size.restype = sz
     L.e8q_ste_backward.argtypes = [vp, vp, vp, f32, e, i64, vp]
@@ -210,6 +215,24 @@ def e8q_encode_core_escape(w, row_scale, core_bound, core_idx_out, esc_out, esc_
                                         _ptr(workspace), workspace.numel(), _ptr(status),
                                         _stream(w, stream))
     _check("e8q_encode_core_escape", code)
+
+
+def e8q_encode_core_escape_noalloc(w, row_scale, core_bound, core_idx_out, esc_out, esc_count_out,
+                                   status, signs=None, had_block=0, two_z_out=None, stream=None):
+    """``e8q_encode_core_escape_noalloc``: ``e8q_encode_core_escape`` without a
+    workspace (the library's fixed per-GPU scratch; calls that overlap on one
+    GPU race)."""
+    _dev(w, "w", _WDT); _dev(row_scale, "row_scale", (torch.float32,))
+    _dev(signs, "signs", (torch.int8,)); _dev(core_idx_out, "core_idx_out", (torch.int16,))
+    _dev(esc_out, "esc_out", (torch.uint8,)); _dev(esc_count_out, "esc_count_out", (torch.int64,))
+    _dev(two_z_out, "two_z_out", (torch.int8,)); _dev(status, "status", (torch.int32,))
+    b, r, c = _shape3(w)
+    cap = 0 if esc_out is None else esc_out.numel() // ESCAPE_RECORD_BYTES
+    code = lib().e8q_encode_core_escape_noalloc(_ptr(w), _dtype_code(w), b, r, c, _ptr(row_scale), _ptr(signs),
+                                                int(had_block), int(core_bound), _ptr(core_idx_out),
+                                                _ptr(esc_out), cap, _ptr(esc_count_out), _ptr(two_z_out),
+                                                _ptr(status), _stream(w, stream))
+    _check("e8q_encode_core_escape_noalloc", code)
 
 
 def e8q_ste_backward(grad_q, grad_w=None, w_latent=None, lr=1.0, stream=None):

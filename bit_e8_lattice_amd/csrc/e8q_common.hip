@@ -85,6 +85,7 @@ extern "C" const char* e8q_status_string(e8q_status_t s) {
         case E8Q_ERR_UNSUPPORTED: return "unsupported dtype or size";
         case E8Q_ERR_LAUNCH: return "kernel launch failed";
         case E8Q_ERR_DEVICE: return "device query failed";
+        case E8Q_ERR_SCRATCH: return "input too large for the allocation-free entry point's fixed scratch";
         default: return "unknown status";
     }
 }

@@ -637,6 +637,31 @@ e8q_status_t encode_impl(const void* w, e8q_dtype_t w_dtype, int64_t batch, int6
     return launch_status();
 }
 
+// Scratch of the allocation-free entry point: one array per device, part of
+// the device code object (so it exists from load time on and is never
+// allocated by a call), shared by every call on that device.  Marked used: no
+// kernel names it (they get its address as an argument), and the device
+// compiler would otherwise drop it.
+constexpr size_t kScratchBytes = size_t(E8Q_ENCODE_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) __attribute__((used)) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (the array's host-side name is not a
+// device address).
+void* scratch_address() {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 }  // namespace
 }  // namespace e8q
 
@@ -650,5 +675,22 @@ extern "C" e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtyp
                                                uint32_t* status_dev, void* stream) {
     return e8q::encode_impl(w, w_dtype, batch, rows, cols, row_scale, signs, had_block, core_bound, core_idx_out,
                             esc_out, esc_capacity, esc_count_out, two_z_out, workspace, workspace_bytes, status_dev,
+                            stream);
+}
+
+extern "C" e8q_status_t e8q_encode_core_escape_noalloc(const void* w, e8q_dtype_t w_dtype, int64_t batch,
+                                                       int64_t rows, int64_t cols, const float* row_scale,
+                                                       const int8_t* signs, int32_t had_block,
+                                                       int32_t core_bound, uint16_t* core_idx_out,
+                                                       e8q_escape_t* esc_out, int64_t esc_capacity,
+                                                       int64_t* esc_count_out, int8_t* two_z_out,
+                                                       uint32_t* status_dev, void* stream) {
+    const size_t need = e8q_encode_workspace_size(batch, rows, cols);
+    if (need == 0) return E8Q_ERR_INVALID;
+    if (need > e8q::kScratchBytes) return E8Q_ERR_SCRATCH;   // checked before anything touches the device
+    void* ws = e8q::scratch_address();
+    if (!ws) return E8Q_ERR_DEVICE;
+    return e8q::encode_impl(w, w_dtype, batch, rows, cols, row_scale, signs, had_block, core_bound, core_idx_out,
+                            esc_out, esc_capacity, esc_count_out, two_z_out, ws, e8q::kScratchBytes, status_dev,
                             stream);
 }

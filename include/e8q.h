@@ -75,7 +75,8 @@ typedef enum {
     E8Q_ERR_INVALID = 1,
     E8Q_ERR_UNSUPPORTED = 2,
     E8Q_ERR_LAUNCH = 3,
-    E8Q_ERR_DEVICE = 4
+    E8Q_ERR_DEVICE = 4,
+    E8Q_ERR_SCRATCH = 5      /* e8q_encode_core_escape_noalloc: input too large for its fixed scratch */
 } e8q_status_t;
 
 /* Bits OR-ed into *status_dev by the kernels. */
@@ -218,6 +219,35 @@ e8q_status_t e8q_encode_core_escape(const void* w, e8q_dtype_t w_dtype,
 
 /* Workspace bytes e8q_encode_core_escape needs for this shape (0 on bad sizes). */
 size_t e8q_encode_workspace_size(int64_t batch, int64_t rows, int64_t cols);
+
+/* ---------------------------------------------------------------------------
+ * e8q_encode_core_escape_noalloc -- e8q_encode_core_escape for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments and results
+ * without `workspace`; its scratch is a fixed array in the library's device
+ * code object, E8Q_ENCODE_NOALLOC_SCRATCH_BYTES per GPU, held from load time
+ * until the process ends.  The call allocates and frees nothing.
+ *   - Shapes with e8q_encode_workspace_size(batch, rows, cols) above
+ *     E8Q_ENCODE_NOALLOC_SCRATCH_BYTES return E8Q_ERR_SCRATCH before anything
+ *     is enqueued (64 MiB covers about 6 G weights per call, e.g. 64 matrices
+ *     of 11008 x 4096).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *     a GPU (different streams, or threads) race and give undefined results;
+ *     calls ordered on one stream are fine.  Each call clears what must start
+ *     at zero with a kernel (no memset), so stale contents never leak.
+ * ------------------------------------------------------------------------- */
+#define E8Q_ENCODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+e8q_status_t e8q_encode_core_escape_noalloc(const void* w, e8q_dtype_t w_dtype,
+                                            int64_t batch, int64_t rows, int64_t cols,
+                                            const float* row_scale,
+                                            const int8_t* signs, int32_t had_block,
+                                            int32_t core_bound,
+                                            uint16_t* core_idx_out,
+                                            e8q_escape_t* esc_out, int64_t esc_capacity,
+                                            int64_t* esc_count_out,
+                                            int8_t* two_z_out,
+                                            uint32_t* status_dev, void* stream);
 
 /* ---------------------------------------------------------------------------
  * e8q_ste_backward -- identity straight-through estimator (E8-QAT Figure 2(b)

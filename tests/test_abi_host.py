@@ -192,3 +192,19 @@ def test_device_tables_in_code_object(L):
     assert found, "table blob missing from the device code objects"
     assert all(ndx != 0 for (_, _, ndx) in found)
     assert max(sz for (_, sz, _) in found) > 10_000_000
+
+
+def test_noalloc_scratch_in_code_object_and_size_check(L):
+    """The allocation-free encode's scratch is a device array of the stated
+    size in the code object, and a shape past it is refused by the host check
+    (before any pointer is touched or anything is enqueued)."""
+    import bit_e8_lattice_amd as e8q
+    found = [sz for elf in _device_code_objects(e8q.library_path) for (n, sz, ndx) in _symbols(elf)
+             if n.endswith("scratch") or "7scratch" in n]
+    assert e8q.ENCODE_NOALLOC_SCRATCH_BYTES in found
+    rows, cols = 1 << 20, 8192
+    assert L.e8q_encode_workspace_size(1, rows, cols) > e8q.ENCODE_NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20
+    code = L.e8q_encode_core_escape_noalloc(fake, 1, 1, rows, cols, fake, None, 0, 16, fake, None, 0, fake, None,
+                                            fake, None)
+    assert code == 5 and b"scratch" in L.e8q_status_string(code)
