@@ -12,11 +12,24 @@
 //     to the lower core index.  This is the one explicit-codebook search of
 //     the method, done once at initialization.
 //   * scale search: s_k = fl32(alpha_k * s0_r) for the given multipliers; the
-//     row error is sum (fl64(kappa_b * v) - s_k z)^2 over the row in a fixed
-//     order (group sums pairwise; group g into partial g mod 64 in increasing
-//     g; a butterfly over the 64 partials); the smallest error wins, NaN
-//     counts as +inf, ties go to the smaller k, a candidate with an invalid
-//     scale (the projection's bad-row rule) has error +inf.
+//     row error is the exact rational E_k = sum_i (kappa v_i - s_k t_i/2)^2;
+//     the smallest error wins, NaN counts as +inf, ties go to the smaller k,
+//     a candidate with an invalid scale (the projection's bad-row rule) has
+//     error +inf.
+//
+// Exact choice by a float64 screen.  Each candidate's error is first summed in
+// float64: kappa v_i and s_k t_i/2 are exact products, so every term carries
+// two roundings (the difference and its square) and a sum of n non-negative
+// terms in any order stays within gamma_{n+2} = (n+2)u/(1-(n+2)u) of E_k
+// (u = 2^-53).  With cols <= 52216 that is below 6e-12, so a candidate whose
+// float64 error is below the best's by the factor 1 + 2^-32 is certainly
+// better, one above it by that factor certainly worse.  Anything in between is
+// decided exactly: E_k - E_j = sum_i (c_ki^2 - 2 a_i c_ki) 2^(..)
+// - (same for j), with a_i = 2 kappa v_i and c_ki = s_k t_ki as integers times
+// powers of two (the a_i^2 terms are equal and cancel), summed without
+// rounding into a 1024-bit fixed-point accumulator in LDS (32 limbs of 32 bits
+// held in 64-bit words, so that carries wait until the end).  err_out holds
+// the float64 errors, within gamma_{cols+2} of the exact ones.
 //
 // One block of four waves per row.  The un-normalized transform v of the
 // weights is computed once (e8q_rotate.hpp) into the workspace.  Per
@@ -28,7 +41,7 @@
 // split of the groups in one 32x32x16 MFMA per tile, which screens the
 // float64 keys to within a bound; only the best tile's 32 points (and, on a
 // near tie, the other tiles within the bound) are then evaluated exactly.  The
-// row error is then summed from LDS in the fixed order.
+// row error is then summed from LDS.
 #include "e8q_device.hpp"
 #include "e8q_host.hpp"
 #include "e8q_point.hpp"
@@ -38,6 +51,16 @@ namespace e8q {
 
 constexpr int kPtqWaves = 4;   // waves per block; one block per row
 constexpr uint32_t kPtqThreads = kPtqWaves * kWave;
+
+// Exact comparison of two candidates' errors: value = sum_i acc[i] 2^(32 i - kAccBase).
+// Every term is an integer times 2^p with p >= -446 (products of float32
+// values, each a multiple of 2^-149) and below 2^262 (|v| < 2^128, kappa <= 1,
+// |t| <= 12); with the bit offset of a term below 2^31 and at most 2^18 terms
+// per limb, no 64-bit limb overflows and the total fits the 1024 bits.
+constexpr int kAccLimbs = 32;
+constexpr int kAccBase = 608;
+constexpr double kScreenFactor = 1.0 + 0x1p-32;   // > (1 + gamma)/(1 - gamma), gamma = gamma_{cols+2}
+enum PassMode { kScreen = 0, kWrite = 1, kExact = 2 };
 
 struct PtqArgs {
     const float* v;            // [rows_total, cols] un-normalized rotated weights
@@ -249,30 +272,79 @@ __device__ __forceinline__ uint32_t screen_group(const PtqArgs& a, const float (
     return bi;
 }
 
-// The group's error (and, with WRITE, its point) for core point bi.
-template <bool WRITE>
-__device__ __forceinline__ void finish_group(const PtqArgs& a, const float (&v)[8], uint32_t bi, uint32_t g,
-                                             uint64_t gbase, double k64, double s64, double* s_e) {
-    const double* tp = a.pts64 + uint64_t(bi) * 9;
-    int t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = int(tp[i]);
-    s_e[g] = group_error(v, t, k64, s64);
-    if constexpr (WRITE) {
-        uint32_t f8 = 0;
-        *reinterpret_cast<uint2*>(a.two_z + (gbase + g) * 8) = pack_i8x8(t, f8);
-        a.core_idx[gbase + g] = uint16_t(bi);
+// A finite float32 as m * 2^e with m an integer, |m| < 2^24, e >= -149.
+__device__ __forceinline__ void f32_parts(float f, int64_t& m, int& e) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t ex = (u >> 23) & 0xFFu;
+    const int64_t mag = int64_t(ex ? ((u & 0x7FFFFFu) | 0x800000u) : (u & 0x7FFFFFu));
+    e = ex ? int(ex) - 150 : -149;
+    m = (u >> 31) ? -mag : mag;
+}
+
+// acc += y * 2^p (|y| < 2^96, y * 2^(p mod 32) held in 128 bits), split
+// over four limbs: three unsigned 32-bit chunks and a signed top.
+__device__ __forceinline__ void acc_add(unsigned long long* acc, __int128 y, int p) {
+    const int pos = p + kAccBase;
+    const int l = pos >> 5;
+    const unsigned __int128 z = static_cast<unsigned __int128>(y) << (pos & 31);
+    const __int128 zs = static_cast<__int128>(z);
+    atomicAdd(acc + l, (unsigned long long)uint32_t(z));
+    atomicAdd(acc + l + 1, (unsigned long long)uint32_t(z >> 32));
+    atomicAdd(acc + l + 2, (unsigned long long)uint32_t(z >> 64));
+    atomicAdd(acc + l + 3, (unsigned long long)int64_t(zs >> 96));
+}
+
+// What one pass over a row needs besides the arguments.
+struct PassCtx {
+    double k64, s64;          // kappa and the candidate scale
+    double* s_e;              // [gpr] group errors (screen and write passes)
+    unsigned long long* acc;  // exact accumulator (exact passes)
+    int64_t mk, ms;           // kappa = mk 2^ek, s = ms 2^es
+    int ek, es;
+    int sign;                 // +1 or -1: the candidate's side of the difference
+};
+
+// Exact pass: adds sign * sum_i (c_i^2 - 2 a_i c_i) for the group, with
+// a_i = 2 kappa v_i = (mk m_i) 2^(ek + e_i + 1), c_i = s t_i = (ms t_i) 2^es.
+__device__ __forceinline__ void exact_group(const PassCtx& cx, const float (&v)[8], const int (&t)[8]) {
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i) {
+        if (t[i] == 0) continue;
+        int64_t mv;
+        int ev;
+        f32_parts(v[i], mv, ev);
+        const __int128 ai = __int128(cx.mk * mv);               // |a| < 2^48
+        const __int128 ci = __int128(cx.ms * int64_t(t[i]));   // |c| < 2^27
+        acc_add(cx.acc, cx.sign * ci * ci, 2 * cx.es);
+        acc_add(cx.acc, -cx.sign * ai * ci, cx.ek + ev + cx.es + 2);
     }
 }
 
-// One candidate scale over one row.  Returns the row error (valid on every
-// lane); with WRITE the points of the row are stored.
-template <bool WRITE>
-__device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, double* s_e, uint16_t* s_list,
+// The group's result for point t (core index idx): its float64 error, its
+// stored point (write pass) or its exact terms (exact pass).
+template <int MODE>
+__device__ __forceinline__ void group_done(const PtqArgs& a, const PassCtx& cx, const float (&v)[8], const int (&t)[8],
+                                           uint32_t idx, uint32_t g, uint64_t gbase) {
+    if constexpr (MODE == kExact) {
+        exact_group(cx, v, t);
+    } else {
+        cx.s_e[g] = group_error(v, t, cx.k64, cx.s64);
+        if constexpr (MODE == kWrite) {
+            uint32_t f8 = 0;
+            *reinterpret_cast<uint2*>(a.two_z + (gbase + g) * 8) = pack_i8x8(t, f8);
+            a.core_idx[gbase + g] = uint16_t(idx);
+        }
+    }
+}
+
+// One candidate scale over one row.  Screen and write passes return the
+// float64 row error (valid on every lane; the write pass also stores the
+// points); an exact pass adds its terms to cx.acc and returns 0.
+template <int MODE>
+__device__ double row_pass(const PtqArgs& a, uint32_t row, float c, const PassCtx& cx, uint16_t* s_list,
                            uint32_t* s_cnt, uint32_t& flags) {
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
     const float* vrow = a.v + uint64_t(row) * a.cols;
-    const double k64 = double(a.kappa), s64 = double(s);
     const uint64_t gbase = uint64_t(row) * a.gpr;
     for (uint32_t g0 = 0; g0 < a.gpr; g0 += kPtqThreads) {
         const uint32_t g = g0 + tid;
@@ -287,18 +359,14 @@ __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, dou
             if (inv) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) t[i] = 0;
-                if (WRITE) flags |= inv;
+                if (MODE == kWrite) flags |= inv;
             } else {
                 nearest_e8(x, t);
             }
             outside = norm_u32(t) > uint32_t(a.core_bound);
             if (!outside) {
-                s_e[g] = group_error(v, t, k64, s64);
-                if constexpr (WRITE) {
-                    uint32_t f8 = 0;
-                    *reinterpret_cast<uint2*>(a.two_z + (gbase + g) * 8) = pack_i8x8(t, f8);
-                    a.core_idx[gbase + g] = uint16_t(core_rank(t, a.tab, a.rp));
-                }
+                const uint32_t idx = MODE == kWrite ? core_rank(t, a.tab, a.rp) : 0u;
+                group_done<MODE>(a, cx, v, t, idx, g, gbase);
             }
         }
         // the list is a work queue: its order does not affect any result
@@ -318,26 +386,77 @@ __device__ double row_pass(const PtqArgs& a, uint32_t row, float s, float c, dou
         float v[8];
         load_v(vrow, g, v);
         const uint32_t bi = screen_group(a, v, c, lane);
-        if (act && lane < 32u) finish_group<WRITE>(a, v, bi, g, gbase, k64, s64, s_e);
+        if (act && lane < 32u) {
+            const double* tp = a.pts64 + uint64_t(bi) * 9;
+            int t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t[i] = int(tp[i]);
+            group_done<MODE>(a, cx, v, t, bi, g, gbase);
+        }
     }
     __syncthreads();
     if (tid == 0) *s_cnt = 0;
-    // the row error in the fixed order (every wave computes the same value)
     double acc = 0.0;
-    for (uint32_t g = lane; g < a.gpr; g += kWave) acc = acc + s_e[g];
+    if constexpr (MODE != kExact) {
+        // the row error (every wave computes the same value)
+        for (uint32_t g = lane; g < a.gpr; g += kWave) acc = acc + cx.s_e[g];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_xor(acc, off, 64);
-    __syncthreads();   // the buffers are reused by the next candidate
+        for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_xor(acc, off, 64);
+    }
+    __syncthreads();   // the buffers are reused by the next pass
     return acc;
+}
+
+__device__ __forceinline__ PassCtx make_ctx(const PtqArgs& a, float s, double* s_e, unsigned long long* acc,
+                                            int sign) {
+    PassCtx cx;
+    cx.k64 = double(a.kappa);
+    cx.s64 = double(s);
+    cx.s_e = s_e;
+    cx.acc = acc;
+    f32_parts(a.kappa, cx.mk, cx.ek);
+    f32_parts(s, cx.ms, cx.es);
+    cx.sign = sign;
+    return cx;
+}
+
+// Exact sign of E_k - E_j for two candidates with valid scales: -1, 0 or +1
+// (the same on every thread).
+__device__ int exact_compare(const PtqArgs& a, uint32_t row, float sk, float ck, float sj, float cj,
+                             double* s_e, unsigned long long* acc, uint16_t* s_list, uint32_t* s_cnt,
+                             int* s_sign) {
+    const uint32_t tid = threadIdx.x;
+    if (tid < uint32_t(kAccLimbs)) acc[tid] = 0ull;
+    __syncthreads();
+    uint32_t dummy = 0;
+    (void)row_pass<kExact>(a, row, ck, make_ctx(a, sk, s_e, acc, 1), s_list, s_cnt, dummy);
+    (void)row_pass<kExact>(a, row, cj, make_ctx(a, sj, s_e, acc, -1), s_list, s_cnt, dummy);
+    if (tid == 0) {
+        // carries: value = sum_i d_i 2^(32 i) + top 2^1024 with 0 <= d_i < 2^32
+        int64_t carry = 0;
+        bool nonzero = false;
+        for (int i = 0; i < kAccLimbs; ++i) {
+            const int64_t x = int64_t(acc[i]) + carry;
+            nonzero = nonzero || uint32_t(x) != 0u;
+            carry = x >> 32;
+        }
+        *s_sign = carry < 0 ? -1 : (carry > 0 || nonzero) ? 1 : 0;
+    }
+    __syncthreads();
+    const int sg = *s_sign;
+    __syncthreads();
+    return sg;
 }
 
 __global__ __launch_bounds__(kPtqThreads, 4) void ptq_kernel(PtqArgs a) {
     extern __shared__ uint32_t s_dyn[];
     const uint32_t tid = threadIdx.x;
     const uint32_t row = blockIdx.x;
-    double* s_e = reinterpret_cast<double*>(s_dyn);
+    unsigned long long* acc = reinterpret_cast<unsigned long long*>(s_dyn);
+    double* s_e = reinterpret_cast<double*>(acc + kAccLimbs);
     uint32_t* s_cnt = reinterpret_cast<uint32_t*>(s_e + a.gpr);
-    uint16_t* s_list = reinterpret_cast<uint16_t*>(s_cnt + 1);
+    int* s_sign = reinterpret_cast<int*>(s_cnt + 1);
+    uint16_t* s_list = reinterpret_cast<uint16_t*>(s_sign + 1);
     if (tid == 0) *s_cnt = 0;
     __syncthreads();
     const float s0 = a.s0[row];
@@ -349,10 +468,28 @@ __global__ __launch_bounds__(kPtqThreads, 4) void ptq_kernel(PtqArgs a) {
         bool bad;
         const float c = row_coef(s, a.kappa, bad);
         double e = __builtin_inf();
-        if (!bad) e = row_pass<false>(a, row, s, c, s_e, s_list, s_cnt, flags);
+        if (!bad) e = row_pass<kScreen>(a, row, c, make_ctx(a, s, s_e, acc, 1), s_list, s_cnt, flags);
         if (a.err_out && tid == 0) a.err_out[uint64_t(row) * uint32_t(a.n_alpha) + uint32_t(k)] = e;
         const double key = e != e ? __builtin_inf() : e;
-        if (key < best) {
+        // key and best are the same on every thread, so every branch is uniform
+        bool take;
+        if (k == 0) {
+            take = true;
+        } else if (key == __builtin_inf()) {
+            take = false;                  // cannot beat anything; equal +inf keeps the smaller k
+        } else if (best == __builtin_inf()) {
+            take = true;
+        } else if (key * kScreenFactor < best) {
+            take = true;
+        } else if (best * kScreenFactor < key) {
+            take = false;
+        } else {
+            const float sb = a.alphas[kbest] * s0;
+            bool bad_b;
+            const float cb = row_coef(sb, a.kappa, bad_b);
+            take = exact_compare(a, row, s, c, sb, cb, s_e, acc, s_list, s_cnt, s_sign) < 0;
+        }
+        if (take) {
             best = key;
             kbest = k;
         }
@@ -370,7 +507,7 @@ __global__ __launch_bounds__(kPtqThreads, 4) void ptq_kernel(PtqArgs a) {
         }
         flags |= E8Q_STATUS_BAD_SCALE;
     } else {
-        (void)row_pass<true>(a, row, s, c, s_e, s_list, s_cnt, flags);
+        (void)row_pass<kWrite>(a, row, c, make_ctx(a, s, s_e, acc, 1), s_list, s_cnt, flags);
     }
     if (tid == 0) {
         a.scale_out[row] = s;
@@ -410,7 +547,7 @@ extern "C" e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype, int64_t
         return E8Q_ERR_INVALID;
     const uint64_t rows_total = uint64_t(batch) * uint64_t(rows);
     const uint32_t gpr = uint32_t(cols / 8);
-    const size_t lds = size_t(gpr) * (8 + 2) + 4;
+    const size_t lds = size_t(kAccLimbs) * 8 + size_t(gpr) * (8 + 2) + 8;
     if (lds > 64 * 1024 || rows_total >= (uint64_t(1) << 31)) return E8Q_ERR_UNSUPPORTED;
     const int hb = signs ? had_block : 0;
     const size_t rot_lds = (hb > 0 ? size_t(cols / 2) * 4 : 0) + (hb > 128 ? size_t(8 * kBlock) * 4 : 0);

@@ -410,9 +410,13 @@ size_t e8q_pack_workspace_size(int64_t n);
  * QAT then starts with no escapes).  Per row: a scale search over
  * s_k = fl32(alphas[k] * base_scale[r]) by the row's squared error, then the
  * finite-core projection at the chosen scale (the nearest E8 point when it is
- * in C(B), else the nearest point of C(B) by exhaustive search).  Comparisons
- * are exact-order float64 evaluations (see the source header); ties go to
- * the lower core index and to the smaller k; NaN errors count as +inf.
+ * in C(B), else the nearest point of C(B) by exhaustive search; the search
+ * compares float64 keys evaluated in a fixed order, ties to the lower core
+ * index).  The scale is chosen on the exact rational row errors
+ * E_k = sum (kappa v - s_k z)^2 (v the un-normalized rotated row, kappa the
+ * float32 1/sqrt(had_block), z the projection at s_k): the smallest wins,
+ * ties go to the smaller k, an invalid scale has E = +inf, a row with a
+ * non-finite transform has NaN errors, which count as +inf.
  *   w, w_dtype, batch, rows, cols   as e8q_project
  *   base_scale   [batch*rows] float32 s0 (e.g. the row RMS)
  *   alphas       device float32 [n_alpha] candidate multipliers
@@ -420,13 +424,16 @@ size_t e8q_pack_workspace_size(int64_t n);
  *   core_bound   B in [0, 40]
  *   scale_out    [batch*rows] float32 chosen scales (required)
  *   choice_out   [batch*rows] int32 chosen k, or NULL
- *   err_out      [batch*rows, n_alpha] float64 row errors (+inf for an invalid
- *                scale), or NULL
+ *   err_out      [batch*rows, n_alpha] float64 row errors, or NULL: each within
+ *                relative (cols+2)u/(1-(cols+2)u), u = 2^-53, of the exact
+ *                E_k (+inf for an invalid scale, NaN for a non-finite row)
  *   core_idx_out [batch*rows*cols/8] uint16 (required): the exported form with
  *                no escapes; decode it with e8q_decode_core_escape and zero counts
  *   two_z_out    [batch, rows, cols] int8 2z (required)
  *   workspace    e8q_ptq_workspace_size(batch, rows, cols) bytes, 256-aligned
- * Limits: cols <= 26208 (LDS per row); rotation blocks as e8q_project_hadamard.
+ * Limits: cols <= 52216 (the row's group errors and work list sit in LDS);
+ * with a rotation also cols <= 30720 (had_block <= 128) or 22528 (larger
+ * blocks); rotation blocks as e8q_project_hadamard.
  * Status bits as the projection at the chosen scale.
  * ------------------------------------------------------------------------- */
 e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype,

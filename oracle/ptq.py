@@ -17,16 +17,18 @@ reading, used here:
   ``||t||^2 / 4`` (exact) -- and equal keys go to the lower core index;
 * per-row scale search: candidate scales ``s_k = fl32(alpha_k * s0_r)`` for
   given multipliers ``alpha_k``; the row's squared error in the rotated basis
-  (equal to the weight-space error, the rotation being orthogonal) is
-  ``E = sum_g sum_i d_gi^2`` with ``d = fl64(kappa_b * v) - s_k * z`` (``v`` the
-  un-normalized transform, ``kappa_b`` the float32 value, every product exact
-  in float64, one rounding per subtraction and square, group sums in the fixed
-  pairwise order), summed over the groups of the row as 64 interleaved partial
-  sums (group g into partial g mod 64, in increasing g) combined by a butterfly
-  (offsets 32, 16, ..., 1); the candidate with the smallest E wins, NaN counts
-  as +inf, ties go to the smaller k, a candidate whose scale is invalid (the
-  projection's bad-row rule) has E = +inf.
+  (equal to the weight-space error, the rotation being orthogonal) is the
+  exact rational number ``E_k = sum_i (kappa_b v_i - s_k t_i / 2)^2`` over the
+  row (``v`` the un-normalized float32 transform, ``kappa_b`` and ``s_k`` their
+  float32 values, ``t`` the finite-core projection at ``s_k``).  The candidate
+  with the smallest ``E_k`` wins, ties go to the smaller k; a candidate whose
+  scale is invalid (the projection's bad-row rule) has ``E_k = +inf``; a row
+  with a non-finite ``v`` has no defined error (NaN), which counts as +inf.
+  The errors are computed exactly with scaled integers: every float32 value is
+  a multiple of 2^-149, so ``2^300 (2 kappa_b v_i - s_k t_i)`` is an integer.
 """
+
+from fractions import Fraction
 
 import numpy as np
 
@@ -35,9 +37,6 @@ from .hadamard import fwht_blocks, kappa
 from .lattice import nearest_e8_two_z
 from .pipeline import (STATUS_BAD_SCALE, STATUS_NONFINITE, STATUS_X_RANGE, X_LIMIT, _shape3, _widen,
                        row_coefficients)
-
-LANES = 64
-
 
 def core_search_two_z(x, core_bound, chunk=4096):
     """Nearest point of C(B) to each row of ``x`` (float32 [G, 8]) by the
@@ -95,27 +94,43 @@ def _project_rows(v, s, had_block, core_bound):
     return tz, bad, nonfinite, xrange
 
 
-def row_error(v, s, tz, had_block):
-    """E per row (float64 [R]) for rows ``v`` [R, cols], scales ``s`` [R] and
-    points ``tz`` [R, cols/8, 8], in the fixed order of the module docstring."""
+_SHIFT = 300      # 2^300 * (2 kappa v - s t) is an integer for float32 kappa, v, s
+
+
+def _scaled(x):
+    """``x * 2^_SHIFT`` as an exact integer for a finite float that is a
+    multiple of 2^-_SHIFT."""
+    n, d = float(x).as_integer_ratio()          # d is a power of two
+    return (n << _SHIFT) // d
+
+
+def exact_row_errors(v, s, tz, had_block):
+    """Exact ``E = sum_i (kappa_b v_i - s t_i / 2)^2`` of every row, as a
+    ``Fraction`` (None for a row with a non-finite ``v``): rows ``v`` float32
+    [R, cols], scales ``s`` float32 [R], points ``tz`` (2z) [R, cols/8, 8].
+    With ``U_i = 2^300 (2 kappa_b v_i - s t_i)`` (an integer),
+    ``E = sum_i U_i^2 / (4 * 2^600)``."""
     rows, cols = v.shape
-    gpr = cols // 8
-    k64 = np.float64(kappa(had_block))
-    s64 = np.asarray(s, dtype=np.float32).astype(np.float64)
-    with np.errstate(over="ignore", invalid="ignore"):
-        d = k64 * v.astype(np.float64).reshape(rows, gpr, 8) - s64[:, None, None] * (0.5 * tz.astype(np.float64))
-        q = d * d
-        e = ((q[..., 0] + q[..., 1]) + (q[..., 2] + q[..., 3])) + ((q[..., 4] + q[..., 5]) + (q[..., 6] + q[..., 7]))
-    part = np.zeros((rows, LANES), dtype=np.float64)
-    with np.errstate(over="ignore", invalid="ignore"):
-        for g in range(gpr):
-            part[:, g % LANES] = part[:, g % LANES] + e[:, g]
-        lanes = np.arange(LANES)
-        off = LANES // 2
-        while off >= 1:
-            part = part + part[:, lanes ^ off]
-            off //= 2
-    return part[:, 0]
+    k = float(kappa(had_block))
+    kn, kd = k.as_integer_ratio()
+    t_all = np.asarray(tz, dtype=np.int64).reshape(rows, cols)
+    out = []
+    for r in range(rows):
+        vr = np.asarray(v[r], dtype=np.float32)
+        if not np.isfinite(vr).all():
+            out.append(None)
+            continue
+        a = []
+        for x in vr.astype(np.float64):
+            n, d = float(x).as_integer_ratio()
+            a.append(((2 * kn * n) << _SHIFT) // (kd * d))     # 2^300 * 2 kappa v, exact
+        sc = _scaled(np.float32(s[r]))
+        total = 0
+        for ai, ti in zip(a, t_all[r].tolist()):
+            u = ai - sc * ti
+            total += u * u
+        out.append(Fraction(total, 4 << (2 * _SHIFT)))
+    return out
 
 
 def ptq_init(w, s0, alphas, signs=None, had_block=0, core_bound=16, w_is_bf16=True):
@@ -123,23 +138,32 @@ def ptq_init(w, s0, alphas, signs=None, had_block=0, core_bound=16, w_is_bf16=Tr
 
     ``w`` [batch, rows, cols] (bf16 bits or float32), ``s0`` float32
     [batch*rows], ``alphas`` float32 [K].  Returns a dict with ``scale``
-    (float32 [batch*rows]), ``k`` (int64), ``err`` (float64 [batch*rows, K]),
-    ``two_z`` (int64 [G, 8]), ``core_idx`` (uint16 [G]) and ``status``.
+    (float32 [batch*rows]), ``k`` (int64), ``err_exact`` (per row, per k: a
+    Fraction, ``inf`` for an invalid scale, None for a row with a non-finite
+    transform), ``err`` (float64 [batch*rows, K]: the nearest float64 to each
+    exact error, +inf, or NaN), ``two_z`` (int64 [G, 8]), ``core_idx``
+    (uint16 [G]) and ``status``.
     """
     batch, rows, cols = _shape3(w)
-    v = _rotated(w, signs, had_block, w_is_bf16).reshape(batch * rows, cols)
+    R = batch * rows
+    v = _rotated(w, signs, had_block, w_is_bf16).reshape(R, cols)
     s0 = np.asarray(s0, dtype=np.float32).reshape(-1)
     alphas = np.asarray(alphas, dtype=np.float32)
     K = len(alphas)
-    err = np.zeros((batch * rows, K), dtype=np.float64)
+    exact = [[None] * K for _ in range(R)]
+    err = np.zeros((R, K), dtype=np.float64)
     for k in range(K):
         with np.errstate(over="ignore", invalid="ignore"):
             sk = (alphas[k] * s0).astype(np.float32)
         tz, bad, _, _ = _project_rows(v, sk, had_block, core_bound)
-        e = row_error(v, sk, tz, had_block)
-        err[:, k] = np.where(bad, np.inf, e)
-    key = np.where(np.isnan(err), np.inf, err)
-    kbest = np.argmin(key, axis=1)
+        e = exact_row_errors(v, sk, tz, had_block)
+        for r in range(R):
+            exact[r][k] = float("inf") if bad[r] else e[r]
+            err[r, k] = np.nan if exact[r][k] is None else float(exact[r][k])
+    kbest = np.zeros(R, dtype=np.int64)
+    for r in range(R):
+        keys = [float("inf") if x is None else x for x in exact[r]]     # NaN counts as +inf
+        kbest[r] = min(range(K), key=lambda j: (keys[j], j))           # ties: smaller k
     with np.errstate(over="ignore", invalid="ignore"):
         scale = (alphas[kbest] * s0).astype(np.float32)
     tz, bad, nonfinite, xrange = _project_rows(v, scale, had_block, core_bound)
@@ -152,5 +176,5 @@ def ptq_init(w, s0, alphas, signs=None, had_block=0, core_bound=16, w_is_bf16=Tr
         status |= STATUS_X_RANGE
     tz = tz.reshape(-1, 8)
     core_idx = core_rank(tz, core_bound).astype(np.uint16)
-    return {"scale": scale, "k": kbest.astype(np.int64), "err": err, "two_z": tz, "core_idx": core_idx,
+    return {"scale": scale, "k": kbest, "err": err, "err_exact": exact, "two_z": tz, "core_idx": core_idx,
             "status": status}

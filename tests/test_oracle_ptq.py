@@ -1,7 +1,9 @@
 """Pins for the oracle's PTQ initialization: the finite-core search against
 exact rational distances, the finite-core projection's agreement with the
-unconstrained projection inside the core, the row error against the plain
-weight-space error, and the scale search recovering an exact lattice scale."""
+unconstrained projection inside the core, the exact row error against plain
+Fraction arithmetic and the float64 weight-space error, the scale choice on a
+constructed exact tie and near tie (where float64 sums disagree with each
+other), and the scale search recovering an exact lattice scale."""
 
 from fractions import Fraction
 
@@ -9,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+from ptq_cases import tie_row
 
 
 def _exact_best(x, pts):
@@ -50,6 +53,34 @@ def test_core_projection_matches_the_projection_inside_the_core():
         assert np.array_equal(tz[i], _exact_best(x[i], pts))
 
 
+def _fraction_error(v_row, s, t_row, hb):
+    """sum (kappa v - s t/2)^2 in Fractions, term by term."""
+    k = Fraction(float(oracle.kappa(hb)))
+    sf = Fraction(float(np.float32(s)))
+    return sum(((k * Fraction(float(x)) - sf * Fraction(int(t), 2)) ** 2 for x, t in zip(v_row, t_row)),
+               Fraction(0))
+
+
+@pytest.mark.parametrize("hb", [0, 64, 128])
+def test_exact_row_error_against_fractions(hb):
+    """Rows of ordinary, tiny (subnormal) and huge values; points from the
+    projection and arbitrary small integers; a non-finite row gives None."""
+    rng = np.random.default_rng(10 + hb)
+    rows, cols = 5, 128
+    v = (rng.standard_normal((rows, cols)) * 0.05).astype(np.float32)
+    v[1, :4] = [1e-45, -3e-42, 7e-39, 1e-30]
+    v[2] = (rng.standard_normal(cols) * 2.0 ** rng.integers(-100, 100, cols)).astype(np.float32)
+    v[3, 7] = np.inf
+    s = np.array([0.01, 2.0 ** -130, 3.0e10, 0.5, 1e-3], np.float32)
+    tz = rng.integers(-6, 7, size=(rows, cols // 8, 8))
+    got = oracle.exact_row_errors(v, s, tz, hb)
+    for r in range(rows):
+        if r == 3:
+            assert got[r] is None
+            continue
+        assert got[r] == _fraction_error(v[r], s[r], tz[r].reshape(-1), hb), r
+
+
 @pytest.mark.parametrize("hb,rtol", [(0, 1e-12), (64, 1e-6), (128, 1e-5)])
 def test_row_error_is_the_weight_space_error(hb, rtol):
     """Exact up to float64 rounding without rotation; with it, within the
@@ -62,10 +93,54 @@ def test_row_error_is_the_weight_space_error(hb, rtol):
     out = oracle.project(w[None], s, sig, hb, w_is_bf16=False)
     v = w if not hb else oracle.fwht_blocks(w * sig.astype(np.float32), hb)
     tz = out["two_z"].reshape(rows, cols // 8, 8)
-    e = oracle.row_error(v.astype(np.float32), s, tz, hb)
+    e = np.array([float(x) for x in oracle.exact_row_errors(v.astype(np.float32), s, tz, hb)])
     W = oracle.exact_restored(tz.reshape(1, rows, cols), s, sig, hb)[0]
     plain = ((w.astype(np.float64) - W) ** 2).sum(1)
     assert np.allclose(e, plain, rtol=rtol, atol=0)
+
+
+def _float64_sums(w, alphas):
+    """Each candidate's float64 terms (exact here: no rotation, products of
+    float32 values near 1) summed forward and in reverse."""
+    v = w.reshape(-1).astype(np.float64)
+    fwd, rev = [], []
+    for a in alphas:
+        tz = oracle.core_project_two_z(w.reshape(-1, 8), 16).reshape(-1)
+        d = v - float(a) * 0.5 * tz
+        q = (d * d).tolist()
+        fwd.append(sum(q))
+        rev.append(sum(q[::-1]))
+    return fwd, rev
+
+
+def test_scale_choice_on_a_constructed_exact_tie():
+    """Exactly equal errors (tie: the smaller k) that float64 sums in forward
+    and reverse order rank in opposite ways."""
+    w, s0, al = tie_row()
+    out = oracle.ptq_init(w, s0, al, None, 0, 16, w_is_bf16=False)
+    e = [_fraction_error(w.reshape(-1), np.float32(a), out["two_z"].reshape(-1), 0) for a in al]
+    assert e[0] == e[1] and out["err_exact"][0] == e
+    fwd, rev = _float64_sums(w, al)
+    assert (fwd[0] < fwd[1]) != (rev[0] < rev[1]) or (fwd[0] == fwd[1]) != (rev[0] == rev[1])
+    assert out["k"][0] == 0 and out["scale"][0] == al[0]
+
+
+def test_scale_choice_on_a_constructed_near_tie():
+    """E_0 - E_1 = 2^-46 exactly (closed form of the construction), half a
+    float64 ulp of E: the second candidate wins, though a float64 sum in one
+    of the two orders ranks it last."""
+    w, s0, al = tie_row(eta_units=1)
+    out = oracle.ptq_init(w, s0, al, None, 0, 16, w_is_bf16=False)
+    e = out["err_exact"][0]
+    assert e[0] - e[1] == Fraction(1, 2 ** 46)
+    assert 128 < e[1] < 256                     # float64 ulp 2^-45
+    fwd, rev = _float64_sums(w, al)
+    assert not (fwd[0] > fwd[1] and rev[0] > rev[1])
+    assert out["k"][0] == 1 and out["scale"][0] == al[1]
+    # the points are the same at both scales
+    for a in al:
+        tz = oracle.core_project_two_z((w.reshape(-1, 8) / np.float32(a)).astype(np.float32), 16)
+        assert np.array_equal(tz, out["two_z"])
 
 
 def test_scale_search_recovers_an_exact_lattice_scale():
