@@ -69,39 +69,74 @@ def gen_tables(tmpdir, verbose=False):
         raise RuntimeError(f"table generator failed ({res.returncode}):\n{res.stdout}{res.stderr}")
 
 
+# Host-only sanitizers for the CPU checks of the C ABI: the host code gets
+# AddressSanitizer and UndefinedBehaviorSanitizer (every report fatal); the
+# device code is built as usual (at -O1, since it never runs there).
+SANITIZE_HOST = ["-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SANITIZE_LINK = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"]
+
+
+def _compile_and_link(tmpdir, out, flags, link_flags, verbose, jobs):
+    gen_tables(tmpdir, verbose)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(tmpdir, src + ".o")
+        cmd = [hipcc()] + flags + SOURCE_FLAGS.get(src, []) + ["-I", INCLUDE, "-I", CSRC, "-I", tmpdir,
+                                                               f"--embed-dir={tmpdir}", "-c",
+                                                               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+        while sum(p.poll() is None for p in procs) >= jobs:
+            procs[[p.poll() is None for p in procs].index(True)].wait()
+    failed = []
+    for src, p in zip(SOURCES, procs):
+        o, e = p.communicate()
+        res = subprocess.CompletedProcess(p.args, p.returncode, o, e)
+        if p.returncode != 0:
+            failed.append(f"{src}:\n{_filtered(res)}")
+        elif verbose and _filtered(res):
+            print(_filtered(res), file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + link_flags + ["-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed ({res.returncode}):\n{_filtered(res)}")
+    os.replace(tmp, out)
+    return out
+
+
+def _jobs(jobs):
+    return jobs or min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+
+
 def build(verbose=False, jobs=None):
-    jobs = jobs or min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with tempfile.TemporaryDirectory(prefix="e8q_build_") as tmpdir:
-        gen_tables(tmpdir, verbose)
-        objs, procs = [], []
-        for src in SOURCES:
-            obj = os.path.join(tmpdir, src + ".o")
-            cmd = [hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-I", INCLUDE, "-I", CSRC, "-I", tmpdir,
-                                                                   f"--embed-dir={tmpdir}", "-c",
-                                                                   os.path.join(CSRC, src), "-o", obj]
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            objs.append(obj)
-            procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
-            while sum(p.poll() is None for p in procs) >= jobs:
-                procs[[p.poll() is None for p in procs].index(True)].wait()
-        failed = []
-        for src, p in zip(SOURCES, procs):
-            out, err = p.communicate()
-            res = subprocess.CompletedProcess(p.args, p.returncode, out, err)
-            if p.returncode != 0:
-                failed.append(f"{src}:\n{_filtered(res)}")
-            elif verbose and _filtered(res):
-                print(_filtered(res), file=sys.stderr)
-        if failed:
-            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
-        tmp = LIB + ".tmp"
-        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"link failed ({res.returncode}):\n{_filtered(res)}")
-        os.replace(tmp, LIB)
-    return LIB
+        return _compile_and_link(tmpdir, LIB, FLAGS, [], verbose, _jobs(jobs))
+
+
+def build_host_sanitized(out_dir, verbose=False, jobs=None):
+    """``out_dir/libe8q_sanitized.so``: the library with its host code under
+    ASan + UBSan (load it with the ASan runtime preloaded; see
+    ``asan_runtime``)."""
+    flags = ["-O1" if f == "-O3" else f for f in FLAGS] + SANITIZE_HOST
+    with tempfile.TemporaryDirectory(prefix="e8q_build_san_") as tmpdir:
+        return _compile_and_link(tmpdir, os.path.join(out_dir, "libe8q_sanitized.so"), flags, SANITIZE_LINK,
+                                 verbose, _jobs(jobs))
+
+
+def asan_runtime():
+    """Path of the compiler's shared ASan runtime."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip().splitlines()[-1] if res.returncode == 0 and res.stdout.strip() else ""
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("ASan runtime not found")
+    return path
 
 
 if __name__ == "__main__":

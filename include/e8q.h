@@ -70,14 +70,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Return codes (an int32_t, so that any value a caller passes back, e.g. to
+ * e8q_status_string, is well-defined). */
+typedef int32_t e8q_status_t;
+enum {
     E8Q_OK = 0,
     E8Q_ERR_INVALID = 1,
     E8Q_ERR_UNSUPPORTED = 2,
     E8Q_ERR_LAUNCH = 3,
     E8Q_ERR_DEVICE = 4,
     E8Q_ERR_SCRATCH = 5      /* e8q_encode_core_escape_noalloc: input too large for its fixed scratch */
-} e8q_status_t;
+};
 
 /* Bits OR-ed into *status_dev by the kernels. */
 enum {
@@ -91,7 +94,9 @@ enum {
     E8Q_STATUS_ESC_MISSING = 128u    /* decode: an escaped slot had no record (decoded as 0) */
 };
 
-typedef enum { E8Q_F32 = 0, E8Q_BF16 = 1 } e8q_dtype_t;
+/* Element type codes (an int32_t: any other value is rejected with E8Q_ERR_INVALID). */
+typedef int32_t e8q_dtype_t;
+enum { E8Q_F32 = 0, E8Q_BF16 = 1 };
 
 /* One escape record, 20 bytes.  E8-QAT stores groups outside the core exactly
  * as 20-byte coordinate records (Table 10; Figure 6(c): payload 2 + 20 rho
