@@ -29,8 +29,9 @@
 //    constant 1.5*2^23 + 32, whose low byte is then n_i + 32; the candidates
 //    2z + 64 are assembled four coordinates per 32-bit word with v_perm, the
 //    parity fix is located with per-element lane masks (first match = lowest
-//    index) and applied as a +-2 byte delta, and norm, sums and the two table
-//    indices come from v_dot4_u32_u8 on the packed words;
+//    index) and applied as a +-2 byte delta; squares and the two table
+//    indices come from v_dot4_u32_u8 on the packed words, byte sums from
+//    v_sad_u8;
 //  * exact path (everything else, and the escape records): the decoder of
 //    nearest_e8() on eight int32 coordinates, float64 decision when close.
 #include <map>
@@ -232,9 +233,9 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
                 bool d8;
                 if (fast_point(x, t0, t1, d8)) {
                     const uint32_t qa = __builtin_amdgcn_udot4(t0, t0, 0u, false);
-                    const uint32_t sa4 = __builtin_amdgcn_udot4(t0, 0x01010101u, 0u, false);
+                    const uint32_t sa4 = __builtin_amdgcn_sad_u8(t0, 0u, 0u);
                     const uint32_t qt = __builtin_amdgcn_udot4(t1, t1, qa, false);
-                    const uint32_t st = __builtin_amdgcn_udot4(t1, 0x01010101u, sa4, false);
+                    const uint32_t st = __builtin_amdgcn_sad_u8(t1, 0u, sa4);
                     // sum (t + 64)^2 - 128 sum (t + 64) + 8 * 64^2 = ||2z||^2
                     const uint32_t norm = qt - (st << 7) + 32768u;
                     // lanes past the end hold the last group's point, which may be

@@ -284,8 +284,9 @@ __device__ __forceinline__ bool fast_point(const float (&x)[8], uint32_t& t0, ui
     const uint32_t m0 = __builtin_amdgcn_perm(db[1], db[0], 0x0C0C0B09u) | __builtin_amdgcn_perm(db[3], db[2], 0x0B090C0Cu);
     const uint32_t m1 = __builtin_amdgcn_perm(db[5], db[4], 0x0C0C0B09u) | __builtin_amdgcn_perm(db[7], db[6], 0x0B090C0Cu);
     // parity of sum(n) and of sum(floor) = sum(n) - #(d < 0)
-    const uint32_t nsum =
-        __builtin_amdgcn_udot4(n0, 0x01010101u, __builtin_amdgcn_udot4(n1, 0x01010101u, 0u, false), false);
+    // byte sums with v_sad_u8 (sum of |byte - 0|): it pairs with other VALU
+    // instructions, v_dot4 does not
+    const uint32_t nsum = __builtin_amdgcn_sad_u8(n0, 0u, __builtin_amdgcn_sad_u8(n1, 0u, 0u));
     const uint32_t negs8 = uint32_t(__builtin_popcount(m0)) + uint32_t(__builtin_popcount(m1));
     const bool odd0 = (nsum & 1u) != 0u;
     const bool odd1 = ((nsum + (negs8 >> 3)) & 1u) != 0u;

@@ -166,8 +166,7 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
                     }
                     if (a.esc) {
                         const uint32_t qt = __builtin_amdgcn_udot4(t1, t1, __builtin_amdgcn_udot4(t0, t0, 0u, false), false);
-                        const uint32_t st = __builtin_amdgcn_udot4(
-                            t1, 0x01010101u, __builtin_amdgcn_udot4(t0, 0x01010101u, 0u, false), false);
+                        const uint32_t st = __builtin_amdgcn_sad_u8(t1, 0u, __builtin_amdgcn_sad_u8(t0, 0u, 0u));
                         norm = qt - (st << 7) + 32768u;
                     }
                     done = true;
