@@ -567,8 +567,10 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
     """One step of the simulated QAT loop on 4096x14336 bf16 latents (lr 1,
     gradients N(0, 1e-4^2) drawn before timing, one per step):
 
-    * ``qat``: projection in the rotated basis (q bf16 + escape count), identity
-      STE fused with SGD;
+    * ``qat``: one kernel per step: the identity STE with SGD on the latents
+      (the previous step's gradient) fused with the projection in the rotated
+      basis (q bf16 + escape count);
+    * ``qat_unfused``: the same step as two kernels, projection then STE + SGD;
     * ``qat_restore``: projection restored to the original basis, identity STE
       (exact for the composite) fused with SGD;
     * ``qat_rotated_grad``: rotated projection, gradient taken back through the
@@ -597,9 +599,18 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
     def bwd_rotated(k):
         e8q.e8q_ste_backward_hadamard(grads[k], b.signs, 128, w_latent=w, lr=1.0)
 
+    def sgd_fwd(k):
+        # the previous step's gradient applied to the latents, then this step's projection
+        e8q.e8q_sgd_project_hadamard(w, grads[k - 1] if k > 0 else grads[-1], 1.0, b.scale, status, signs=b.signs,
+                                     had_block=128, q_out=q, core_bound=16, esc_count_out=esc[k:k + 1])
+
     parts, desc = {
-        "qat": ([("project_hadamard", fwd_rotated, 4), ("ste_backward", bwd_identity, 6)],
-                "128-wide rotated projection + escape count, identity STE fused with SGD"),
+        "qat": ([("sgd_project_hadamard", sgd_fwd, 8)],
+                "identity STE with SGD on the latents fused with the next 128-wide rotated projection + escape "
+                "count (one kernel per step)"),
+        "qat_unfused": ([("project_hadamard", fwd_rotated, 4), ("ste_backward", bwd_identity, 6)],
+                        "128-wide rotated projection + escape count, then identity STE fused with SGD (two "
+                        "kernels per step)"),
         "qat_restore": ([("project_hadamard_restore", fwd_restore, 4), ("ste_backward", bwd_identity, 6)],
                         "128-wide projection restored to the original basis + escape count, "
                         "identity STE fused with SGD"),
@@ -655,7 +666,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder",
-                    choices=list(DECODER_CONFIGS) + ["linear", "moe", "moe_alpha1", "qat", "qat_restore",
+                    choices=list(DECODER_CONFIGS) + ["linear", "moe", "moe_alpha1", "qat", "qat_unfused", "qat_restore",
                                                      "qat_rotated_grad", "decode", "decode_q", "gemv", "pack",
                                                      "ptq"])
     ap.add_argument("--gemv-m", type=int, default=1, choices=[1, 2])

@@ -11,6 +11,12 @@
 // straight from the packed 2z + 64 bytes: q_i = fma(byte_i, s/2, -32 s), which
 // is the single rounding of the exact product s z_i.
 //
+// e8q_sgd_project_hadamard fuses a QAT step's update with the next forward:
+// each lane first applies the identity STE with SGD to its group of bf16
+// latents (w <- bf16(fl32(w) - fl32(lr g)), NaN -> 0x7FC0, exactly as
+// e8q_ste_backward), stores the new latents in place, and projects them: the
+// latents are read once instead of twice per training step.
+//
 // e8q_project_hadamard_restore writes the projection back in the original
 // basis instead: w_hat = sigma * fl32(T * c2), T = H_b (2z) with float32
 // butterflies in the forward stage order, c2 = fl32(fl32(s kappa_b) / 2).  The
@@ -45,6 +51,8 @@ struct ProjectArgs {
     uint32_t num_tiles;
     void* w_hat;              // restored weights (original basis), or null
     int w_hat_bf16;
+    const void* grad;         // SGD: bf16 gradient of the latents (same layout as w)
+    float lr;
 };
 
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
@@ -62,7 +70,44 @@ __device__ __forceinline__ uint32_t unbias_i8x4(uint32_t t) {
     return x | ((x & 0x40404040u) << 1);
 }
 
-template <typename WT, int HB, bool FAST, bool RESTORE>
+// SGD on one word of two bf16 latents; `nan` is set when a result is NaN
+// (the caller then redoes the group with the scalar rule).
+__device__ __forceinline__ uint32_t sgd_word(uint32_t w2, uint32_t g2, float lr, bool& nan) {
+    const float w0 = __uint_as_float(w2 << 16), w1 = __uint_as_float(w2 & 0xFFFF0000u);
+    const float g0 = __uint_as_float(g2 << 16), g1 = __uint_as_float(g2 & 0xFFFF0000u);
+    const float n0 = w0 - lr * g0;
+    const float n1 = w1 - lr * g1;
+    nan = nan || (n0 != n0) || (n1 != n1);
+    return bf16x2_rne(n0, n1);
+}
+
+__device__ __forceinline__ uint32_t sgd_bf16_scalar(uint32_t w, uint32_t g, float lr) {
+    const float n = __uint_as_float(w << 16) - lr * __uint_as_float(g << 16);
+    const uint32_t u = __float_as_uint(n);
+    return n != n ? 0x7FC0u : (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The identity STE with SGD on one group of bf16 latents.
+__device__ __forceinline__ uint4 sgd_group(const uint4& w, const uint4& g, float lr) {
+    bool nan = false;
+    uint4 r;
+    r.x = sgd_word(w.x, g.x, lr, nan);
+    r.y = sgd_word(w.y, g.y, lr, nan);
+    r.z = sgd_word(w.z, g.z, lr, nan);
+    r.w = sgd_word(w.w, g.w, lr, nan);
+    if (nan) {   // rare: the bf16 NaN the STE writes
+        const uint32_t wv[4] = {w.x, w.y, w.z, w.w}, gv[4] = {g.x, g.y, g.z, g.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[i] = sgd_bf16_scalar(wv[i] & 0xFFFFu, gv[i] & 0xFFFFu, lr) |
+                   (sgd_bf16_scalar(wv[i] >> 16, gv[i] >> 16, lr) << 16);
+        r = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    return r;
+}
+
+template <typename WT, int HB, bool FAST, bool RESTORE, bool SGD = false>
 __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
     extern __shared__ uint32_t s_dyn[];
     const uint32_t tid = threadIdx.x;
@@ -88,6 +133,11 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
         uint32_t g1 = tbase, g2 = tbase + kBlock;
         uint32_t r1 = fdiv(min(g1, glast), a.gpr_div), r2 = fdiv(min(g2, glast), a.gpr_div);
         Raw w1 = load_raw<WT>(a.w, min(g1, glast)), w2 = load_raw<WT>(a.w, min(g2, glast));
+        uint4 d1 = make_uint4(0u, 0u, 0u, 0u), d2 = d1;   // SGD: the gradient, loaded with the latents
+        if constexpr (SGD) {
+            d1 = load_raw<uint16_t>(a.grad, min(g1, glast)).p;
+            d2 = load_raw<uint16_t>(a.grad, min(g2, glast)).p;
+        }
         float s1 = a.scale[r1], s2 = a.scale[r2];
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
@@ -95,15 +145,21 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
             const bool live = g < a.groups;
             const uint32_t gl = min(g, glast);
             const uint32_t row = r1;
-            const Raw raw = w1;
+            Raw raw = w1;
+            const uint4 dg = d1;
             const float s = s1;
-            g1 = g2; r1 = r2; w1 = w2; s1 = s2;
+            g1 = g2; r1 = r2; w1 = w2; s1 = s2; d1 = d2;
             if (j + 2 < kItems) {
                 g2 = g + 2u * kBlock;
                 const uint32_t gn = min(g2, glast);
                 r2 = fdiv(gn, a.gpr_div);
                 w2 = load_raw<WT>(a.w, gn);
+                if constexpr (SGD) d2 = load_raw<uint16_t>(a.grad, gn).p;
                 s2 = a.scale[r2];
+            }
+            if constexpr (SGD) {
+                raw.p = sgd_group(raw.p, dg, a.lr);
+                if (live) *reinterpret_cast<uint4*>(const_cast<uint16_t*>(static_cast<const uint16_t*>(a.w)) + uint64_t(g) * 8) = raw.p;
             }
             float v[8];
             const uint32_t vsign = rotate_group<WT, HB>(s_smask, s_wide, raw, gl - row * a.gpr, lf, lpos, tid, v);
@@ -282,23 +338,23 @@ __global__ void zero_u64_kernel(unsigned long long* p, uint32_t n) {
     for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0ull;
 }
 
-template <typename WT, bool FAST, bool RESTORE>
+template <typename WT, bool FAST, bool RESTORE, bool SGD = false>
 static void launch_project(int hb, const ProjectArgs& a, size_t lds, hipStream_t st) {
     switch (hb) {
         case 0:
             if constexpr (!RESTORE)
-                launch_tiles(project_kernel<WT, 0, FAST, false>, a, a.num_tiles, kBlock, lds, st);
+                launch_tiles(project_kernel<WT, 0, FAST, false, SGD>, a, a.num_tiles, kBlock, lds, st);
             break;
-        case 8: launch_tiles(project_kernel<WT, 8, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 16: launch_tiles(project_kernel<WT, 16, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 32: launch_tiles(project_kernel<WT, 32, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 64: launch_tiles(project_kernel<WT, 64, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 128: launch_tiles(project_kernel<WT, 128, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 256: launch_tiles(project_kernel<WT, 256, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 512: launch_tiles(project_kernel<WT, 512, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 1024: launch_tiles(project_kernel<WT, 1024, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 2048: launch_tiles(project_kernel<WT, 2048, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
-        case 4096: launch_tiles(project_kernel<WT, 4096, FAST, RESTORE>, a, a.num_tiles, kBlock, lds, st); break;
+        case 8: launch_tiles(project_kernel<WT, 8, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 16: launch_tiles(project_kernel<WT, 16, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 32: launch_tiles(project_kernel<WT, 32, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 64: launch_tiles(project_kernel<WT, 64, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 128: launch_tiles(project_kernel<WT, 128, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 256: launch_tiles(project_kernel<WT, 256, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 512: launch_tiles(project_kernel<WT, 512, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 1024: launch_tiles(project_kernel<WT, 1024, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 2048: launch_tiles(project_kernel<WT, 2048, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
+        case 4096: launch_tiles(project_kernel<WT, 4096, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
         default: break;
     }
 }
@@ -308,7 +364,8 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
                                  int32_t had_block, void* q_out, e8q_dtype_t q_dtype,
                                  int8_t* two_z_out, float* rotated_out, int32_t core_bound,
                                  int64_t* esc_count_out, uint32_t* status_dev, void* stream,
-                                 void* w_hat_out = nullptr, e8q_dtype_t w_hat_dtype = E8Q_F32) {
+                                 void* w_hat_out = nullptr, e8q_dtype_t w_hat_dtype = E8Q_F32,
+                                 const void* grad = nullptr, float lr = 0.0f) {
     e8q_status_t st = check_shape(w, w_dtype, batch, rows, cols, row_scale, status_dev);
     if (st != E8Q_OK) return st;
     if (!q_out && !two_z_out && !esc_count_out && !rotated_out && !w_hat_out) return E8Q_ERR_INVALID;
@@ -341,13 +398,17 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
     a.num_tiles = uint32_t((groups + kTileGroups - 1) / kTileGroups);
     a.w_hat = w_hat_out;
     a.w_hat_bf16 = w_hat_dtype == E8Q_BF16;
+    a.grad = grad;
+    a.lr = lr;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (esc_count_out) {
         launch(zero_u64_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, s,
                            a.esc, uint32_t(batch));
     }
-    if (w_hat_out) {
+    if (grad) {
+        launch_project<uint16_t, true, false, true>(had_block, a, lds, s);
+    } else if (w_hat_out) {
         if (w_dtype == E8Q_BF16)
             launch_project<uint16_t, true, true>(had_block, a, lds, s);
         else
@@ -396,4 +457,19 @@ extern "C" e8q_status_t e8q_project_hadamard_restore(const void* w, e8q_dtype_t 
     return e8q::project_impl(w, w_dtype, batch, rows, cols, row_scale, signs, had_block, nullptr, E8Q_F32,
                              two_z_out, nullptr, core_bound, esc_count_out, status_dev, stream, w_hat_out,
                              w_hat_dtype);
+}
+
+extern "C" e8q_status_t e8q_sgd_project_hadamard(void* w_latent, const void* grad, float lr, int64_t batch,
+                                                 int64_t rows, int64_t cols, const float* row_scale,
+                                                 const int8_t* signs, int32_t had_block, void* q_out,
+                                                 e8q_dtype_t q_dtype, int8_t* two_z_out, int32_t core_bound,
+                                                 int64_t* esc_count_out, uint32_t* status_dev, void* stream) {
+    if (!w_latent || !grad) return E8Q_ERR_INVALID;
+    if (signs) {
+        const e8q_status_t st = e8q::check_block(signs, had_block, cols);
+        if (st != E8Q_OK) return st;
+    }
+    return e8q::project_impl(w_latent, E8Q_BF16, batch, rows, cols, row_scale, signs, signs ? had_block : 0, q_out,
+                             q_dtype, two_z_out, nullptr, core_bound, esc_count_out, status_dev, stream, nullptr,
+                             E8Q_F32, grad, lr);
 }

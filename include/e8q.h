@@ -255,6 +255,32 @@ e8q_status_t e8q_encode_core_escape_noalloc(const void* w, e8q_dtype_t w_dtype,
                                             uint32_t* status_dev, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * e8q_sgd_project_hadamard -- a QAT step's latent update fused with the next
+ * forward projection (E8-QAT Figure 2(b) caption: the identity STE hands the
+ * gradient to the latent weights, which the next forward projects again;
+ * Table 4: BF16 latents).  For every element of the bf16 latents
+ *   w <- bf16_RNE(fl32(w) - fl32(lr * g))     (NaN -> 0x7FC0),
+ * the rule of e8q_ste_backward, stored in place; then the outputs of
+ * e8q_project_hadamard (e8q_project when signs is NULL) for the updated
+ * latents, bit for bit.  The latents are read once per step instead of twice.
+ *   w_latent    [batch, rows, cols] bf16, read and overwritten (required)
+ *   grad        [batch, rows, cols] bf16 gradient dL/dq, passed through the
+ *               identity STE as dL/dw (required; may not alias w_latent)
+ *   lr          learning rate
+ *   row_scale, signs, had_block, q_out, q_dtype, two_z_out, core_bound,
+ *   esc_count_out, status_dev, stream   as e8q_project_hadamard (signs NULL:
+ *               no rotation, had_block ignored); at least one output
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_sgd_project_hadamard(void* w_latent, const void* grad, float lr,
+                                      int64_t batch, int64_t rows, int64_t cols,
+                                      const float* row_scale,
+                                      const int8_t* signs, int32_t had_block,
+                                      void* q_out, e8q_dtype_t q_dtype,
+                                      int8_t* two_z_out, int32_t core_bound,
+                                      int64_t* esc_count_out,
+                                      uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
  * e8q_ste_backward -- identity straight-through estimator (E8-QAT Figure 2(b)
  * caption), optionally fused with a plain SGD step on the latent weights
  * (Table 4: latents are BF16).

@@ -219,3 +219,17 @@ def test_noalloc_scratch_in_code_object_and_size_check(L):
     code = L.e8q_encode_core_escape_noalloc(fake, 1, 1, rows, cols, fake, None, 0, 16, fake, None, 0, fake, None,
                                             fake, None)
     assert code == 5 and b"scratch" in L.e8q_status_string(code)
+
+
+def test_sgd_project_rejects(L):
+    """Missing latents or gradient, or a bad rotation block, are refused on the
+    host before anything is launched."""
+    fake = 1 << 20
+    assert L.e8q_sgd_project_hadamard(None, fake, 1.0, 1, 8, 64, fake, None, 0, fake, 1, None, 16, None, fake,
+                                      None) == 1
+    assert L.e8q_sgd_project_hadamard(fake, None, 1.0, 1, 8, 64, fake, None, 0, fake, 1, None, 16, None, fake,
+                                      None) == 1
+    assert L.e8q_sgd_project_hadamard(fake, fake, 1.0, 1, 8, 64, fake, fake, 48, fake, 1, None, 16, None, fake,
+                                      None) == 1
+    assert L.e8q_sgd_project_hadamard(fake, fake, 1.0, 1, 8, 60, fake, None, 0, fake, 1, None, 16, None, fake,
+                                      None) == 1
