@@ -619,7 +619,7 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
                              "fused with SGD"),
     }[mode]
     n = w.numel()
-    r = _time_launches(args, torch, parts, n, 10 * n, status,
+    r = _time_launches(args, torch, parts, n, sum(p[2] for p in parts) * n, status,
                        f"qat step 4096x14336 bf16 latents: {desc} (lr 1, grad N(0,1e-4^2))",
                        steps_offset=True)
     series = esc.cpu().tolist()
