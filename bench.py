@@ -20,8 +20,9 @@ forked before the GPU is touched.
 above): ``decoder_alpha1`` (scale 1 x RMS, most groups escape),
 ``decoder_wide`` (whole-row 4096 / 256-column rotation blocks), ``linear``
 (4096x4096 rotated projection), ``moe`` / ``moe_alpha1`` (128-expert stacks),
-``qat`` (one forward projection + fused STE/SGD step on 4096x14336, escape
-count of every step in ``detail``), ``qat_restore``, ``qat_rotated_grad``,
+``qat`` (STE/SGD fused with the next forward projection on 4096x14336, one
+kernel per step, escape count of every step in ``detail``), ``qat_unfused``,
+``qat_restore``, ``qat_restore_unfused``, ``qat_rotated_grad``,
 ``decode``, ``decode_q``, ``gemv``, ``pack``, ``ptq``.
 """
 
@@ -571,8 +572,9 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
       (the previous step's gradient) fused with the projection in the rotated
       basis (q bf16 + escape count);
     * ``qat_unfused``: the same step as two kernels, projection then STE + SGD;
-    * ``qat_restore``: projection restored to the original basis, identity STE
-      (exact for the composite) fused with SGD;
+    * ``qat_restore``: one kernel per step: the identity STE (exact for the
+      composite) with SGD fused with the projection restored to the original
+      basis; ``qat_restore_unfused`` the same step as two kernels;
     * ``qat_rotated_grad``: rotated projection, gradient taken back through the
       rotation (R^T) fused with SGD.
     """
@@ -599,6 +601,10 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
     def bwd_rotated(k):
         e8q.e8q_ste_backward_hadamard(grads[k], b.signs, 128, w_latent=w, lr=1.0)
 
+    def sgd_fwd_restore(k):
+        e8q.e8q_sgd_project_hadamard_restore(w, grads[k - 1] if k > 0 else grads[-1], 1.0, b.scale, b.signs, 128, q,
+                                             status, core_bound=16, esc_count_out=esc[k:k + 1])
+
     def sgd_fwd(k):
         # the previous step's gradient applied to the latents, then this step's projection
         e8q.e8q_sgd_project_hadamard(w, grads[k - 1] if k > 0 else grads[-1], 1.0, b.scale, status, signs=b.signs,
@@ -611,9 +617,12 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
         "qat_unfused": ([("project_hadamard", fwd_rotated, 4), ("ste_backward", bwd_identity, 6)],
                         "128-wide rotated projection + escape count, then identity STE fused with SGD (two "
                         "kernels per step)"),
-        "qat_restore": ([("project_hadamard_restore", fwd_restore, 4), ("ste_backward", bwd_identity, 6)],
-                        "128-wide projection restored to the original basis + escape count, "
-                        "identity STE fused with SGD"),
+        "qat_restore": ([("sgd_project_hadamard_restore", sgd_fwd_restore, 8)],
+                        "identity STE with SGD on the latents fused with the next 128-wide projection restored to "
+                        "the original basis + escape count (one kernel per step)"),
+        "qat_restore_unfused": ([("project_hadamard_restore", fwd_restore, 4), ("ste_backward", bwd_identity, 6)],
+                                "128-wide projection restored to the original basis + escape count, then "
+                                "identity STE fused with SGD (two kernels per step)"),
         "qat_rotated_grad": ([("project_hadamard", fwd_rotated, 4), ("ste_backward_hadamard", bwd_rotated, 6)],
                              "128-wide rotated projection + escape count, gradient through R^T "
                              "fused with SGD"),
@@ -666,7 +675,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder",
-                    choices=list(DECODER_CONFIGS) + ["linear", "moe", "moe_alpha1", "qat", "qat_unfused", "qat_restore",
+                    choices=list(DECODER_CONFIGS) + ["linear", "moe", "moe_alpha1", "qat", "qat_unfused", "qat_restore", "qat_restore_unfused",
                                                      "qat_rotated_grad", "decode", "decode_q", "gemv", "pack",
                                                      "ptq"])
     ap.add_argument("--gemv-m", type=int, default=1, choices=[1, 2])

@@ -17,6 +17,9 @@
 // e8q_ste_backward), stores the new latents in place, and projects them: the
 // latents are read once instead of twice per training step.
 //
+// e8q_sgd_project_hadamard_restore does the same before the restored
+// projection below.
+//
 // e8q_project_hadamard_restore writes the projection back in the original
 // basis instead: w_hat = sigma * fl32(T * c2), T = H_b (2z) with float32
 // butterflies in the forward stage order, c2 = fl32(fl32(s kappa_b) / 2).  The
@@ -406,7 +409,9 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
         launch(zero_u64_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, s,
                            a.esc, uint32_t(batch));
     }
-    if (grad) {
+    if (grad && w_hat_out) {
+        launch_project<uint16_t, true, true, true>(had_block, a, lds, s);
+    } else if (grad) {
         launch_project<uint16_t, true, false, true>(had_block, a, lds, s);
     } else if (w_hat_out) {
         if (w_dtype == E8Q_BF16)
@@ -472,4 +477,18 @@ extern "C" e8q_status_t e8q_sgd_project_hadamard(void* w_latent, const void* gra
     return e8q::project_impl(w_latent, E8Q_BF16, batch, rows, cols, row_scale, signs, signs ? had_block : 0, q_out,
                              q_dtype, two_z_out, nullptr, core_bound, esc_count_out, status_dev, stream, nullptr,
                              E8Q_F32, grad, lr);
+}
+
+extern "C" e8q_status_t e8q_sgd_project_hadamard_restore(void* w_latent, const void* grad, float lr, int64_t batch,
+                                                         int64_t rows, int64_t cols, const float* row_scale,
+                                                         const int8_t* signs, int32_t had_block, void* w_hat_out,
+                                                         e8q_dtype_t w_hat_dtype, int8_t* two_z_out,
+                                                         int32_t core_bound, int64_t* esc_count_out,
+                                                         uint32_t* status_dev, void* stream) {
+    if (!w_latent || !grad || !w_hat_out) return E8Q_ERR_INVALID;
+    const e8q_status_t st = e8q::check_block(signs, had_block, cols);
+    if (st != E8Q_OK) return st;
+    return e8q::project_impl(w_latent, E8Q_BF16, batch, rows, cols, row_scale, signs, had_block, nullptr, E8Q_F32,
+                             two_z_out, nullptr, core_bound, esc_count_out, status_dev, stream, w_hat_out,
+                             w_hat_dtype, grad, lr);
 }

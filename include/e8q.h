@@ -281,6 +281,25 @@ e8q_status_t e8q_sgd_project_hadamard(void* w_latent, const void* grad, float lr
                                       uint32_t* status_dev, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * e8q_sgd_project_hadamard_restore -- the same fused step with the projection
+ * written back in the original basis: the latent update of
+ * e8q_sgd_project_hadamard, then the outputs of e8q_project_hadamard_restore
+ * for the updated latents, bit for bit (E8-QAT Figure 2 caption: the
+ * transforms surround the projection).
+ *   w_latent, grad, lr   as e8q_sgd_project_hadamard
+ *   other arguments as e8q_project_hadamard_restore (signs and w_hat_out
+ *   required)
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_sgd_project_hadamard_restore(void* w_latent, const void* grad, float lr,
+                                              int64_t batch, int64_t rows, int64_t cols,
+                                              const float* row_scale,
+                                              const int8_t* signs, int32_t had_block,
+                                              void* w_hat_out, e8q_dtype_t w_hat_dtype,
+                                              int8_t* two_z_out, int32_t core_bound,
+                                              int64_t* esc_count_out,
+                                              uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
  * e8q_ste_backward -- identity straight-through estimator (E8-QAT Figure 2(b)
  * caption), optionally fused with a plain SGD step on the latent weights
  * (Table 4: latents are BF16).

@@ -118,3 +118,29 @@ def test_fused_qat_loop_matches_unfused():
     assert torch.equal(w1.view(torch.int16), w2.view(torch.int16))
     _same(o1, o2)
     assert all(torch.equal(x, y) for x, y in zip(esc1, esc2))
+
+
+@pytest.mark.parametrize("hb,wh_dtype", [(128, torch.bfloat16), (64, torch.float32), (4096, torch.bfloat16)])
+def test_fused_restore_matches_unfused(hb, wh_dtype):
+    """The restored-basis variant: latents, w_hat, 2z, escape counts and status
+    bit for bit as e8q_ste_backward + e8q_project_hadamard_restore."""
+    d = device()
+    shape = (2, 24, 4096) if hb == 4096 else (2, 24, 1024)
+    w = workloads.normal(shape, 730 + hb, d)
+    s = workloads.rms_scale(w, 1.5)
+    sg = workloads.signs(shape[2], 731, d)
+    w1, w2 = w.clone(), w.clone()
+    o1 = {"wh": torch.empty(shape, dtype=wh_dtype, device=d), "tz": torch.empty(shape, dtype=torch.int8, device=d),
+          "esc": torch.zeros(shape[0], dtype=torch.int64, device=d), "st": torch.zeros(1, dtype=torch.int32, device=d)}
+    o2 = {k: v.clone() for k, v in o1.items()}
+    for k in range(3):
+        g = workloads.normal(shape, 740 + k, d, std=0.05)
+        e8q.e8q_ste_backward(g, w_latent=w1, lr=0.5)
+        e8q.e8q_project_hadamard_restore(w1, s, sg, hb, o1["wh"], o1["st"], two_z_out=o1["tz"], core_bound=16,
+                                         esc_count_out=o1["esc"])
+        e8q.e8q_sgd_project_hadamard_restore(w2, g, 0.5, s, sg, hb, o2["wh"], o2["st"], two_z_out=o2["tz"],
+                                             core_bound=16, esc_count_out=o2["esc"])
+        torch.cuda.synchronize()
+        assert torch.equal(w1.view(torch.int16), w2.view(torch.int16)), f"latents, step {k}"
+        _same({"q": o1["wh"], "tz": o1["tz"], "esc": o1["esc"], "st": o1["st"]},
+              {"q": o2["wh"], "tz": o2["tz"], "esc": o2["esc"], "st": o2["st"]})
