@@ -22,7 +22,7 @@ above): ``decoder_alpha1`` (scale 1 x RMS, most groups escape),
 (4096x4096 rotated projection), ``moe`` / ``moe_alpha1`` (128-expert stacks),
 ``qat`` (STE/SGD fused with the next forward projection on 4096x14336, one
 kernel per step, escape count of every step in ``detail``), ``qat_unfused``,
-``qat_restore``, ``qat_restore_unfused``, ``qat_rotated_grad``,
+``qat_restore``, ``qat_restore_unfused``, ``qat_rotated_grad``, ``qat_rotated_grad_unfused``,
 ``decode``, ``decode_q``, ``gemv``, ``pack``, ``ptq``.
 """
 
@@ -575,8 +575,9 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
     * ``qat_restore``: one kernel per step: the identity STE (exact for the
       composite) with SGD fused with the projection restored to the original
       basis; ``qat_restore_unfused`` the same step as two kernels;
-    * ``qat_rotated_grad``: rotated projection, gradient taken back through the
-      rotation (R^T) fused with SGD.
+    * ``qat_rotated_grad``: one kernel per step: the gradient taken back through
+      the rotation (R^T) with SGD fused with the rotated projection;
+      ``qat_rotated_grad_unfused`` the same step as two kernels.
     """
     dev = torch.device("cuda:0")
     b = workloads.qat_loop(dev)
@@ -605,6 +606,10 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
         e8q.e8q_sgd_project_hadamard_restore(w, grads[k - 1] if k > 0 else grads[-1], 1.0, b.scale, b.signs, 128, q,
                                              status, core_bound=16, esc_count_out=esc[k:k + 1])
 
+    def sgd_fwd_rotated(k):
+        e8q.e8q_sgd_rotated_project_hadamard(w, grads[k - 1] if k > 0 else grads[-1], 1.0, b.scale, b.signs, 128,
+                                             status, q_out=q, core_bound=16, esc_count_out=esc[k:k + 1])
+
     def sgd_fwd(k):
         # the previous step's gradient applied to the latents, then this step's projection
         e8q.e8q_sgd_project_hadamard(w, grads[k - 1] if k > 0 else grads[-1], 1.0, b.scale, status, signs=b.signs,
@@ -623,7 +628,10 @@ def run_qat(args, torch, e8q, workloads, mode="qat"):
         "qat_restore_unfused": ([("project_hadamard_restore", fwd_restore, 4), ("ste_backward", bwd_identity, 6)],
                                 "128-wide projection restored to the original basis + escape count, then "
                                 "identity STE fused with SGD (two kernels per step)"),
-        "qat_rotated_grad": ([("project_hadamard", fwd_rotated, 4), ("ste_backward_hadamard", bwd_rotated, 6)],
+        "qat_rotated_grad": ([("sgd_rotated_project_hadamard", sgd_fwd_rotated, 8)],
+                             "gradient through R^T with SGD on the latents fused with the next 128-wide rotated "
+                             "projection + escape count (one kernel per step)"),
+        "qat_rotated_grad_unfused": ([("project_hadamard", fwd_rotated, 4), ("ste_backward_hadamard", bwd_rotated, 6)],
                              "128-wide rotated projection + escape count, gradient through R^T "
                              "fused with SGD"),
     }[mode]
@@ -675,8 +683,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decoder",
-                    choices=list(DECODER_CONFIGS) + ["linear", "moe", "moe_alpha1", "qat", "qat_unfused", "qat_restore", "qat_restore_unfused",
-                                                     "qat_rotated_grad", "decode", "decode_q", "gemv", "pack",
+                    choices=list(DECODER_CONFIGS) + ["linear", "moe", "moe_alpha1", "qat", "qat_unfused", "qat_restore",
+                                                     "qat_restore_unfused", "qat_rotated_grad",
+                                                     "qat_rotated_grad_unfused", "decode", "decode_q", "gemv", "pack",
                                                      "ptq"])
     ap.add_argument("--gemv-m", type=int, default=1, choices=[1, 2])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -14,7 +14,8 @@ import torch
 
 __all__ = [
     "E8QError", "lib", "library_path",
-    "e8q_project", "e8q_project_hadamard", "e8q_project_hadamard_restore", "e8q_sgd_project_hadamard", "e8q_sgd_project_hadamard_restore",
+    "e8q_project", "e8q_project_hadamard", "e8q_project_hadamard_restore", "e8q_sgd_project_hadamard",
+    "e8q_sgd_project_hadamard_restore", "e8q_sgd_rotated_project_hadamard",
     "e8q_encode_core_escape", "e8q_encode_workspace_size", "e8q_encode_core_escape_noalloc",
     "ENCODE_NOALLOC_SCRATCH_BYTES", "e8q_ste_backward",
     "e8q_ste_backward_hadamard", "e8q_decode_core_escape", "e8q_decode_workspace_size",
@@ -97,6 +98,9 @@ def lib():
     L.e8q_sgd_project_hadamard_restore.argtypes = [vp, vp, f32, i64, i64, i64, vp, vp, i32, vp, e, vp, i32, vp, vp,
                                                    vp]
     L.e8q_sgd_project_hadamard_restore.restype = e
+    L.e8q_sgd_rotated_project_hadamard.argtypes = [vp, vp, f32, i64, i64, i64, vp, vp, i32, vp, e, vp, i32, vp, vp,
+                                                   vp]
+    L.e8q_sgd_rotated_project_hadamard.restype = e
     L.e8q_ste_backward.argtypes = [vp, vp, vp, f32, e, i64, vp]
     L.e8q_ste_backward.restype = e
     L.e8q_core_size.argtypes = [i32]
@@ -198,6 +202,26 @@ def e8q_sgd_project_hadamard(w_latent, grad, lr, row_scale, status, signs=None, 
                                           _ptr(two_z_out), int(core_bound), _ptr(esc_count_out), _ptr(status),
                                           _stream(w_latent, stream))
     _check("e8q_sgd_project_hadamard", code)
+
+
+def e8q_sgd_rotated_project_hadamard(w_latent, grad_q, lr, row_scale, signs, had_block, status, q_out=None,
+                                     two_z_out=None, core_bound=-1, esc_count_out=None, stream=None):
+    """``e8q_sgd_rotated_project_hadamard``: the rotated-basis gradient taken
+    back through the rotation, SGD on the bf16 latents (in place), then the
+    rotated projection of the updated latents."""
+    _dev(w_latent, "w_latent", (torch.bfloat16,)); _dev(grad_q, "grad_q", (torch.bfloat16,))
+    _dev(row_scale, "row_scale", (torch.float32,)); _dev(signs, "signs", (torch.int8,))
+    _dev(q_out, "q_out", _WDT); _dev(two_z_out, "two_z_out", (torch.int8,))
+    _dev(esc_count_out, "esc_count_out", (torch.int64,)); _dev(status, "status", (torch.int32,))
+    if grad_q.shape != w_latent.shape:
+        raise ValueError("grad_q must have the shape of w_latent")
+    b, r, c = _shape3(w_latent)
+    code = lib().e8q_sgd_rotated_project_hadamard(_ptr(w_latent), _ptr(grad_q), float(lr), b, r, c, _ptr(row_scale),
+                                                  _ptr(signs), int(had_block), _ptr(q_out),
+                                                  _dtype_code(q_out) if q_out is not None else F32,
+                                                  _ptr(two_z_out), int(core_bound), _ptr(esc_count_out), _ptr(status),
+                                                  _stream(w_latent, stream))
+    _check("e8q_sgd_rotated_project_hadamard", code)
 
 
 def e8q_sgd_project_hadamard_restore(w_latent, grad, lr, row_scale, signs, had_block, w_hat_out, status,

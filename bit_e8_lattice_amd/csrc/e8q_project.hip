@@ -18,7 +18,10 @@
 // latents are read once instead of twice per training step.
 //
 // e8q_sgd_project_hadamard_restore does the same before the restored
-// projection below.
+// projection below, and e8q_sgd_rotated_project_hadamard first takes a
+// rotated-basis gradient back through the rotation on the same lanes
+// (sigma * fl32(kappa_b H_b g), as e8q_ste_backward_hadamard) and steps the
+// latents with that float32 gradient.
 //
 // e8q_project_hadamard_restore writes the projection back in the original
 // basis instead: w_hat = sigma * fl32(T * c2), T = H_b (2z) with float32
@@ -110,7 +113,26 @@ __device__ __forceinline__ uint4 sgd_group(const uint4& w, const uint4& g, float
     return r;
 }
 
-template <typename WT, int HB, bool FAST, bool RESTORE, bool SGD = false>
+// SGD on one group of bf16 latents with a float32 gradient y (the rotated
+// STE's): w <- bf16(fl32(w) - fl32(lr y)), NaN -> 0x7FC0.
+__device__ __forceinline__ uint4 sgd_group_f32(const uint4& w, const float (&y)[8], float lr) {
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float n0 = __uint_as_float(wv[i] << 16) - lr * y[2 * i];
+        const float n1 = __uint_as_float(wv[i] & 0xFFFF0000u) - lr * y[2 * i + 1];
+        const uint32_t u0 = __float_as_uint(n0), u1 = __float_as_uint(n1);
+        const uint32_t b0 = n0 != n0 ? 0x7FC0u : (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;
+        const uint32_t b1 = n1 != n1 ? 0x7FC0u : (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
+        o[i] = b0 | (b1 << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// SGD: 0 none, 1 identity STE with SGD, 2 the gradient taken back through the
+// rotation, then SGD (latents updated in place before they are projected).
+template <typename WT, int HB, bool FAST, bool RESTORE, int SGD = 0>
 __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
     extern __shared__ uint32_t s_dyn[];
     const uint32_t tid = threadIdx.x;
@@ -160,8 +182,22 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
                 if constexpr (SGD) d2 = load_raw<uint16_t>(a.grad, gn).p;
                 s2 = a.scale[r2];
             }
-            if constexpr (SGD) {
+            if constexpr (SGD == 1) {
                 raw.p = sgd_group(raw.p, dg, a.lr);
+                if (live) *reinterpret_cast<uint4*>(const_cast<uint16_t*>(static_cast<const uint16_t*>(a.w)) + uint64_t(g) * 8) = raw.p;
+            } else if constexpr (SGD == 2 && HB > 0) {
+                // dL/dw = R^T dL/dq = sigma * fl32(kappa_b H_b g) (as e8q_ste_backward_hadamard), then SGD
+                Raw graw;
+                graw.p = dg;
+                graw.q = make_uint4(0u, 0u, 0u, 0u);
+                float y[8];
+                widen_raw<uint16_t>(graw, y);
+                const uint32_t ys = fwht_group<HB>(y, lf, s_wide, lpos, tid);
+                const float kk = __uint_as_float(__float_as_uint(a.kappa) ^ ys);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = fmaf(y[i], kk, 0.0f);   // every zero becomes +0
+                flip_f32(y, *reinterpret_cast<const uint4*>(s_smask + (gl - row * a.gpr) * 4u));
+                raw.p = sgd_group_f32(raw.p, y, a.lr);
                 if (live) *reinterpret_cast<uint4*>(const_cast<uint16_t*>(static_cast<const uint16_t*>(a.w)) + uint64_t(g) * 8) = raw.p;
             }
             float v[8];
@@ -341,11 +377,11 @@ __global__ void zero_u64_kernel(unsigned long long* p, uint32_t n) {
     for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0ull;
 }
 
-template <typename WT, bool FAST, bool RESTORE, bool SGD = false>
+template <typename WT, bool FAST, bool RESTORE, int SGD = 0>
 static void launch_project(int hb, const ProjectArgs& a, size_t lds, hipStream_t st) {
     switch (hb) {
-        case 0:
-            if constexpr (!RESTORE)
+        case 0:  // no rotation: neither the restore nor the rotated gradient applies
+            if constexpr (!RESTORE && SGD != 2)
                 launch_tiles(project_kernel<WT, 0, FAST, false, SGD>, a, a.num_tiles, kBlock, lds, st);
             break;
         case 8: launch_tiles(project_kernel<WT, 8, FAST, RESTORE, SGD>, a, a.num_tiles, kBlock, lds, st); break;
@@ -368,7 +404,7 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
                                  int8_t* two_z_out, float* rotated_out, int32_t core_bound,
                                  int64_t* esc_count_out, uint32_t* status_dev, void* stream,
                                  void* w_hat_out = nullptr, e8q_dtype_t w_hat_dtype = E8Q_F32,
-                                 const void* grad = nullptr, float lr = 0.0f) {
+                                 const void* grad = nullptr, float lr = 0.0f, bool rotate_grad = false) {
     e8q_status_t st = check_shape(w, w_dtype, batch, rows, cols, row_scale, status_dev);
     if (st != E8Q_OK) return st;
     if (!q_out && !two_z_out && !esc_count_out && !rotated_out && !w_hat_out) return E8Q_ERR_INVALID;
@@ -409,10 +445,12 @@ static e8q_status_t project_impl(const void* w, e8q_dtype_t w_dtype, int64_t bat
         launch(zero_u64_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, s,
                            a.esc, uint32_t(batch));
     }
-    if (grad && w_hat_out) {
-        launch_project<uint16_t, true, true, true>(had_block, a, lds, s);
+    if (grad && rotate_grad) {
+        launch_project<uint16_t, true, false, 2>(had_block, a, lds, s);
+    } else if (grad && w_hat_out) {
+        launch_project<uint16_t, true, true, 1>(had_block, a, lds, s);
     } else if (grad) {
-        launch_project<uint16_t, true, false, true>(had_block, a, lds, s);
+        launch_project<uint16_t, true, false, 1>(had_block, a, lds, s);
     } else if (w_hat_out) {
         if (w_dtype == E8Q_BF16)
             launch_project<uint16_t, true, true>(had_block, a, lds, s);
@@ -491,4 +529,18 @@ extern "C" e8q_status_t e8q_sgd_project_hadamard_restore(void* w_latent, const v
     return e8q::project_impl(w_latent, E8Q_BF16, batch, rows, cols, row_scale, signs, had_block, nullptr, E8Q_F32,
                              two_z_out, nullptr, core_bound, esc_count_out, status_dev, stream, w_hat_out,
                              w_hat_dtype, grad, lr);
+}
+
+extern "C" e8q_status_t e8q_sgd_rotated_project_hadamard(void* w_latent, const void* grad_q, float lr, int64_t batch,
+                                                         int64_t rows, int64_t cols, const float* row_scale,
+                                                         const int8_t* signs, int32_t had_block, void* q_out,
+                                                         e8q_dtype_t q_dtype, int8_t* two_z_out, int32_t core_bound,
+                                                         int64_t* esc_count_out, uint32_t* status_dev,
+                                                         void* stream) {
+    if (!w_latent || !grad_q) return E8Q_ERR_INVALID;
+    const e8q_status_t st = e8q::check_block(signs, had_block, cols);
+    if (st != E8Q_OK) return st;
+    return e8q::project_impl(w_latent, E8Q_BF16, batch, rows, cols, row_scale, signs, had_block, q_out, q_dtype,
+                             two_z_out, nullptr, core_bound, esc_count_out, status_dev, stream, nullptr, E8Q_F32,
+                             grad_q, lr, true);
 }

@@ -300,6 +300,28 @@ e8q_status_t e8q_sgd_project_hadamard_restore(void* w_latent, const void* grad, 
                                               uint32_t* status_dev, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * e8q_sgd_rotated_project_hadamard -- the fused step for a forward whose
+ * output q lives in the rotated basis: the gradient dL/dq is taken back
+ * through the rotation exactly as e8q_ste_backward_hadamard does
+ * (dL/dw = sigma * fl32(kappa_b H_b g), float32), the latents step with it
+ * (w <- bf16_RNE(fl32(w) - fl32(lr * dL/dw)), NaN -> 0x7FC0) in place, and
+ * the outputs of e8q_project_hadamard for the updated latents follow, bit for
+ * bit the two calls in sequence (E8-QAT Figure 2 caption: the transforms
+ * surround the projection; Figure 2(b): the STE).
+ *   w_latent, lr   as e8q_sgd_project_hadamard
+ *   grad_q         [batch, rows, cols] bf16 gradient with respect to q (required)
+ *   other arguments as e8q_project_hadamard (signs required)
+ * ------------------------------------------------------------------------- */
+e8q_status_t e8q_sgd_rotated_project_hadamard(void* w_latent, const void* grad_q, float lr,
+                                              int64_t batch, int64_t rows, int64_t cols,
+                                              const float* row_scale,
+                                              const int8_t* signs, int32_t had_block,
+                                              void* q_out, e8q_dtype_t q_dtype,
+                                              int8_t* two_z_out, int32_t core_bound,
+                                              int64_t* esc_count_out,
+                                              uint32_t* status_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
  * e8q_ste_backward -- identity straight-through estimator (E8-QAT Figure 2(b)
  * caption), optionally fused with a plain SGD step on the latent weights
  * (Table 4: latents are BF16).

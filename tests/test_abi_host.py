@@ -233,3 +233,10 @@ def test_sgd_project_rejects(L):
                                       None) == 1
     assert L.e8q_sgd_project_hadamard(fake, fake, 1.0, 1, 8, 60, fake, None, 0, fake, 1, None, 16, None, fake,
                                       None) == 1
+    # the rotated-gradient step needs the rotation: signs and a valid block
+    f = L.e8q_sgd_rotated_project_hadamard
+    assert f(None, fake, 1.0, 1, 8, 128, fake, fake, 128, fake, 1, None, 16, None, fake, None) == 1
+    assert f(fake, None, 1.0, 1, 8, 128, fake, fake, 128, fake, 1, None, 16, None, fake, None) == 1
+    assert f(fake, fake, 1.0, 1, 8, 128, fake, None, 128, fake, 1, None, 16, None, fake, None) == 1
+    assert f(fake, fake, 1.0, 1, 8, 128, fake, fake, 0, fake, 1, None, 16, None, fake, None) == 1
+    assert f(fake, fake, 1.0, 1, 8, 136, fake, fake, 128, fake, 1, None, 16, None, fake, None) == 1
