@@ -380,7 +380,7 @@ def run_gemv(args, torch, e8q, workloads):
                     "signs": b.signs, "x": x, "xt": x.transpose(1, 2).contiguous(), "w_hat": wh,
                     "y": torch.empty((nb, m, rows), dtype=torch.float32, device=dev),
                     "yb": torch.empty((nb, rows, m), dtype=torch.bfloat16, device=dev),
-                    "ws": torch.empty(e8q.e8q_gemv_workspace_size(nb, m, cols), dtype=torch.uint8, device=dev)})
+                    "ws": torch.empty(e8q.e8q_gemv_workspace_size(nb, m, rows, cols), dtype=torch.uint8, device=dev)})
         b.w = None
         del ws, dws
     torch.cuda.synchronize()

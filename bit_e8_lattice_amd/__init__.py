@@ -73,7 +73,7 @@ def lib():
     L.e8q_gemv_core_escape.argtypes = [vp, vp, i64, vp, i64, i64, i64, i32, vp, vp, i32, vp, e, i64, vp,
                                        vp, sz, vp, vp]
     L.e8q_gemv_core_escape.restype = e
-    L.e8q_gemv_workspace_size.argtypes = [i64, i64, i64]
+    L.e8q_gemv_workspace_size.argtypes = [i64, i64, i64, i64]
     L.e8q_gemv_workspace_size.restype = sz
     L.e8q_pack_escapes.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp, sz, vp, vp]
     L.e8q_pack_escapes.restype = e
@@ -355,8 +355,8 @@ def e8q_decode_core_escape(core_idx, esc, esc_count, shape, core_bound, workspac
     _check("e8q_decode_core_escape", code)
 
 
-def e8q_gemv_workspace_size(batch, m, cols):
-    return int(lib().e8q_gemv_workspace_size(batch, m, cols))
+def e8q_gemv_workspace_size(batch, m, rows, cols):
+    return int(lib().e8q_gemv_workspace_size(batch, m, rows, cols))
 
 
 def e8q_gemv_core_escape(core_idx, esc, esc_count, shape, core_bound, row_scale, x, y_out, workspace, status,

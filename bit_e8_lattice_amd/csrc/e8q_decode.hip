@@ -612,8 +612,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
 // groups along K is free).  Index words are loaded four chunks ahead, also
 // across the wave's tiles, into four fixed registers.  Every step's MFMA starts from 0; the
 // steps are added in float32 in order, 16 steps (512 columns) per partial
-// sum, the partials in order.  Escaped and malformed slots are added per lane
-// in float32 (2z . x~, the same partial scheme).
+// sum, the partials in order.  Escaped and malformed slots read the table's
+// zero entry; the sweep only counts the escaped ones (per tile, in the
+// workspace) and flags the malformed ones, and gemv_escape_kernel then adds
+// the escaped slots' records to the finished rows.
 constexpr uint32_t kGmRows = 16;
 constexpr int kGmAhead = 4;   // index words (chunks) loaded ahead
 
@@ -623,9 +625,11 @@ typedef float gm_f32x4 __attribute__((ext_vector_type(4)));
 struct GemvMfmaArgs {
     const uint16_t* core_idx;
     const uint32_t* esc;
-    const uint64_t* offsets;
+    const int64_t* esc_count;
+    uint64_t esc_capacity;
     const float* xt;           // [batch, m, cols] x~ (float32), for the escaped slots
     const uint4* xb;           // [batch, m, 3, gpr] x~ parts hi, mid, lo (8 bf16 per group)
+    uint32_t* tile_esc;        // [batch, tiles_per_b] escaped slots per 16-row tile
     const float* scale;
     const uint4* tab;          // [npts + 1] points as 8 bf16 (entry npts: zero)
     uint32_t npts;
@@ -636,57 +640,6 @@ struct GemvMfmaArgs {
     float* y;
     uint32_t* status;
 };
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
-}
-
-// x~ parts: per group, hi, mid and lo as 8 bf16 each ([batch, m, 3, gpr]).
-__global__ __launch_bounds__(256) void gemv_split_kernel(const float* xt, uint4* xb, uint32_t gpr, uint32_t groups) {
-    for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < groups; g += gridDim.x * 256u) {
-        const float4* src = reinterpret_cast<const float4*>(xt + uint64_t(g) * 8);
-        const float4 x0 = src[0], x1 = src[1];
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        uint32_t h[8], m[8], l[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t hb = bf16_rne_bits(x[i]);
-            const float d = x[i] - __uint_as_float(hb);          // exact
-            const uint32_t mb = bf16_rne_bits(d);
-            const float e = d - __uint_as_float(mb);             // exact
-            h[i] = hb >> 16;
-            m[i] = mb >> 16;
-            l[i] = bf16_rne_bits(e) >> 16;
-        }
-        const uint32_t vec = g / gpr, gi = g - vec * gpr;
-        uint4* dst = xb + uint64_t(vec) * 3 * gpr + gi;
-        dst[0] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-        dst[gpr] = make_uint4(m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16));
-        dst[2 * gpr] =
-            make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
-    }
-}
-
-// The float32 contribution of an escaped or malformed slot, per vector.
-template <int M>
-__device__ __forceinline__ void gm_special(const GemvMfmaArgs& a, uint32_t b, uint32_t row, uint32_t g, uint32_t idx,
-                                           bool row_ok, float* sp, uint32_t& flags) {
-    int tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (idx != 0xFFFFu) {
-        if (row_ok) flags |= E8Q_STATUS_BAD_INDEX;
-    } else if (!find_record(a.esc, a.offsets, b, row * a.gpr + g, a.rows * a.gpr, tb)) {
-        if (row_ok) flags |= E8Q_STATUS_ESC_MISSING;
-    }
-#pragma unroll
-    for (int v = 0; v < M; ++v) {
-        const float* xv = a.xt + ((uint64_t(b) * M + v) * a.gpr + g) * 8;
-        float s0 = float(tb[0]) * xv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) s0 = fmaf(float(tb[i]), xv[i], s0);
-        sp[v] += s0;
-    }
-}
 
 // LDS accesses of one wave, ordered across its lanes.
 __device__ __forceinline__ void gm_wave_sync() {
@@ -708,7 +661,7 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
     const uint32_t tab_n = LDS_TAB ? a.npts + 1u : 0u;
     const uint32_t xs_n = X_LDS ? uint32_t(M) * 3u * a.gpr : 0u;
     uint4* s_x = s_gm + tab_n;
-    float* s_red = reinterpret_cast<float*>(s_gm + tab_n + xs_n) + wv * (256u + 64u * M);
+    float* s_red = reinterpret_cast<float*>(s_gm + tab_n + xs_n) + wv * 256u;
     if constexpr (LDS_TAB) {
         for (uint32_t i = tid; i <= a.npts; i += kThreads) s_gm[i] = a.tab[i];
         __syncthreads();
@@ -787,9 +740,7 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
         // the row scale of lane (row) l < 16, loaded now and used at the end
         const float s_row = a.scale[uint64_t(b) * a.rows + min(r0 + (lane & 15u), a.rows - 1u)];
         gm_f32x4 acc1 = zero, acc2 = zero;
-        float sp1[M], sp2[M];
-#pragma unroll
-        for (int v = 0; v < M; ++v) sp1[v] = sp2[v] = 0.0f;
+        uint32_t nesc = 0;
         // One chunk: the word in its ring slot (loaded kGmAhead chunks ago),
         // whose refill is issued at once.  Every slot is a fixed register: the
         // loop body takes the slots in order, and a row's chunk count is padded
@@ -825,15 +776,18 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
                 const gm_u16x2 mx = __builtin_elementwise_max(
                     __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.x), __builtin_bit_cast(gm_u16x2, w.y)),
                     __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.z), __builtin_bit_cast(gm_u16x2, w.w)));
-                const bool any = uint32_t(mx.x > mx.y ? mx.x : mx.y) >= a.npts;
+                const bool any = row_ok && uint32_t(mx.x > mx.y ? mx.x : mx.y) >= a.npts;
                 if (__ballot(any)) {
-                    // rare: one copy of the slow path, stepping through the word
+                    // rare: escaped slots counted, malformed ones flagged
+                    if (any) {
 #pragma unroll 1
-                    for (uint32_t s = 0; s < 8; ++s) {
-                        const uint32_t h = s >> 1;
-                        const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
-                        const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
-                        if (id >= a.npts) gm_special<M>(a, b, row, 32u * c + 8u * q + s, id, row_ok, sp1, flags);
+                        for (uint32_t s = 0; s < 8; ++s) {
+                            const uint32_t h = s >> 1;
+                            const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
+                            const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
+                            if (id == 0xFFFFu) ++nesc;
+                            else if (id >= a.npts) flags |= E8Q_STATUS_BAD_INDEX;
+                        }
                     }
                 }
                 products();
@@ -841,11 +795,6 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc2[r] = acc2[r] + acc1[r];
                     acc1 = zero;
-#pragma unroll
-                    for (int v = 0; v < M; ++v) {
-                        sp2[v] = sp2[v] + sp1[v];
-                        sp1[v] = 0.0f;
-                    }
                 }
             }
         };
@@ -853,11 +802,12 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
 #pragma unroll
             for (int k = 0; k < kGmAhead; ++k) chunk(wq[k], c + uint32_t(k));
         }
-        // D (16 rows x 16 columns) and the four lane quarters' escaped-slot sums
+        // D (16 rows x 16 columns); the tile's escaped slots
 #pragma unroll
         for (int r = 0; r < 4; ++r) s_red[(4u * q + uint32_t(r)) * 16u + i16] = acc2[r];
 #pragma unroll
-        for (int v = 0; v < M; ++v) s_red[256u + (q * M + uint32_t(v)) * 16u + i16] = sp2[v];
+        for (int off = 32; off >= 1; off >>= 1) nesc += __shfl_xor(nesc, off, 64);
+        if (lane == 0u) a.tile_esc[uint64_t(b) * a.tiles_per_b + t] = nesc;
         gm_wave_sync();
         if (lane < kGmRows && r0 + lane < a.rows) {
             const uint32_t r = r0 + lane;
@@ -865,13 +815,10 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
             const bool bad = !(s > 0.0f) || __builtin_isinf(s);
             if (bad) flags |= E8Q_STATUS_BAD_SCALE;
             const float* d = s_red + lane * 16u;
-            const float* e = s_red + 256u + lane;
 #pragma unroll
             for (int v = 0; v < M; ++v) {
                 const float dv = (d[3 * v] + d[3 * v + 1]) + d[3 * v + 2];
-                const float ev =
-                    (e[(0 * M + v) * 16] + e[(1 * M + v) * 16]) + (e[(2 * M + v) * 16] + e[(3 * M + v) * 16]);
-                a.y[(uint64_t(b) * M + uint32_t(v)) * a.rows + r] = bad ? 0.0f : (0.5f * s) * (dv + ev);
+                a.y[(uint64_t(b) * M + uint32_t(v)) * a.rows + r] = bad ? 0.0f : (0.5f * s) * dv;
             }
         }
         gm_wave_sync();
@@ -879,14 +826,121 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
     flush_status(flags, a.status);
 }
 
+// The escaped slots of one batch item (one block each), after the sweep:
+// the item's records are esc[first, end) with first / end the clipped
+// running sums of the counts (as e8q_decode_core_escape's offsets).  The
+// thread holding a row's first record adds 2z . x~ of every record of that
+// row whose slot holds 0xFFFF and whose key differs from the previous
+// record's, in order, in blocks of 32 (each block summed from 0, the block
+// sums added in order), and adds (s / 2) times the sum to the row's y (not
+// for rows with a bad scale, whose y stays 0).  An item whose escaped slots
+// (counted by the sweep) outnumber those records lacks a record.
+template <int M>
+__global__ __launch_bounds__(1024) void gemv_escape_kernel(GemvMfmaArgs a) {
+    __shared__ uint64_t s_sum[32];
+    const uint32_t b = blockIdx.x, tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+    const uint32_t nw = blockDim.x >> 6;
+    // records before this item, and this item's escaped slots
+    uint64_t before = 0, slots = 0;
+    for (uint32_t i = tid; i < b; i += blockDim.x) before += a.esc_count[i] > 0 ? uint64_t(a.esc_count[i]) : 0ull;
+    for (uint32_t i = tid; i < a.tiles_per_b; i += blockDim.x) slots += a.tile_esc[uint64_t(b) * a.tiles_per_b + i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        before += __shfl_xor(before, off, 64);
+        slots += __shfl_xor(slots, off, 64);
+    }
+    if (lane == 0u) {
+        s_sum[wv] = before;
+        s_sum[16u + wv] = slots;
+    }
+    __syncthreads();
+    before = 0;
+    slots = 0;
+    for (uint32_t w = 0; w < nw; ++w) {
+        before += s_sum[w];
+        slots += s_sum[16u + w];
+    }
+    const uint64_t own = a.esc_count[b] > 0 ? uint64_t(a.esc_count[b]) : 0ull;
+    const uint64_t first = min(before, a.esc_capacity), end = min(before + own, a.esc_capacity);
+    const uint64_t gpb = uint64_t(a.rows) * a.gpr;
+    const uint16_t* slot_idx = a.core_idx + uint64_t(b) * gpb;
+    uint64_t matched = 0;
+    for (uint64_t i = first + tid; i < end; i += blockDim.x) {
+        const uint32_t key = a.esc[i * 5];
+        const uint32_t pk = i > first ? a.esc[(i - 1) * 5] : 0xFFFFFFFFu;
+        if (key >= gpb) continue;
+        const uint32_t row = key / a.gpr;
+        if (pk < gpb && pk / a.gpr == row) continue;   // not the row's first record
+        float total[M], blk[M];
+#pragma unroll
+        for (int v = 0; v < M; ++v) total[v] = blk[v] = 0.0f;
+        uint32_t in_blk = 0, prev = 0xFFFFFFFFu;
+        for (uint64_t j = i; j < end; ++j) {
+            const uint32_t kj = a.esc[j * 5];
+            if (kj >= gpb || kj / a.gpr != row) break;
+            if (kj != prev && slot_idx[kj] == 0xFFFFu) {
+                const uint32_t* rec = a.esc + j * 5 + 1;
+                float z[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t wd = rec[k];
+                    z[2 * k] = float(int32_t(int16_t(uint16_t(wd & 0xFFFFu))));
+                    z[2 * k + 1] = float(int32_t(int16_t(uint16_t(wd >> 16))));
+                }
+                const uint32_t g = kj - row * a.gpr;
+#pragma unroll
+                for (int v = 0; v < M; ++v) {
+                    const float* x = a.xt + ((uint64_t(b) * M + uint32_t(v)) * a.gpr + g) * 8u;
+                    float cs = z[0] * x[0];
+#pragma unroll
+                    for (int k = 1; k < 8; ++k) cs = fmaf(z[k], x[k], cs);
+                    blk[v] += cs;
+                }
+                ++matched;
+                if (++in_blk == 32u) {
+#pragma unroll
+                    for (int v = 0; v < M; ++v) {
+                        total[v] += blk[v];
+                        blk[v] = 0.0f;
+                    }
+                    in_blk = 0;
+                }
+            }
+            prev = kj;
+        }
+        const float s = a.scale[uint64_t(b) * a.rows + row];
+        if (s > 0.0f && !__builtin_isinf(s)) {
+#pragma unroll
+            for (int v = 0; v < M; ++v) {
+                float* yp = a.y + (uint64_t(b) * M + uint32_t(v)) * a.rows + row;
+                *yp = *yp + (0.5f * s) * (total[v] + blk[v]);
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) matched += __shfl_xor(matched, off, 64);
+    __syncthreads();
+    if (lane == 0u) s_sum[wv] = matched;
+    __syncthreads();
+    if (tid == 0u) {
+        uint64_t m = 0;
+        for (uint32_t w = 0; w < nw; ++w) m += s_sum[w];
+        if (m != slots) atomicOr(a.status, uint32_t(E8Q_STATUS_ESC_MISSING));
+    }
+}
+
 static size_t gemv_xt_bytes(int64_t batch, int64_t m, int64_t cols) {
     return (size_t(batch) * size_t(m) * size_t(cols) * 4 + 255) & ~size_t(255);
 }
 
-// offsets, x~ (float32), x~ parts (3 x 8 bf16 per group)
-static size_t gemv_ws_bytes(int64_t batch, int64_t m, int64_t cols) {
-    return decode_ws_bytes(batch) + gemv_xt_bytes(batch, m, cols) +
-           ((size_t(batch) * size_t(m) * size_t(cols / 8) * 48 + 255) & ~size_t(255));
+static size_t gemv_xb_bytes(int64_t batch, int64_t m, int64_t cols) {
+    return (size_t(batch) * size_t(m) * size_t(cols / 8) * 48 + 255) & ~size_t(255);
+}
+
+// offsets, x~ (float32), x~ parts (3 x 8 bf16 per group), escaped slots per 16-row tile
+static size_t gemv_ws_bytes(int64_t batch, int64_t m, int64_t rows, int64_t cols) {
+    return decode_ws_bytes(batch) + gemv_xt_bytes(batch, m, cols) + gemv_xb_bytes(batch, m, cols) +
+           ((size_t(batch) * size_t((rows + kGmRows - 1) / kGmRows) * 4 + 255) & ~size_t(255));
 }
 
 template <int M>
@@ -901,7 +955,7 @@ template <int M>
 static void launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t st) {
     const size_t tab = size_t(a.npts + 1) * 16;
     const size_t xs = size_t(M) * 3 * a.gpr * 16;
-    const size_t red16 = 16 * (256 + 64 * M) * 4, red8 = 8 * (256 + 64 * M) * 4;
+    const size_t red16 = 16 * 256 * 4, red8 = 8 * 256 * 4;
     const uint64_t tiles_per_b = a.tiles_per_b, batch = a.tiles / a.tiles_per_b;
     if (tab + xs + red16 <= 160 * 1024) {
         const uint64_t units = batch * ((tiles_per_b + 15) / 16);
@@ -917,9 +971,10 @@ static void launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t st) {
 
 }  // namespace e8q
 
-extern "C" size_t e8q_gemv_workspace_size(int64_t batch, int64_t m, int64_t cols) {
-    if (batch <= 0 || batch >= (int64_t(1) << 32) || m <= 0 || cols <= 0) return 0;
-    return e8q::gemv_ws_bytes(batch, m, cols);
+extern "C" size_t e8q_gemv_workspace_size(int64_t batch, int64_t m, int64_t rows, int64_t cols) {
+    if (batch <= 0 || batch >= (int64_t(1) << 32) || m <= 0 || rows <= 0 || rows >= (int64_t(1) << 32) || cols <= 0)
+        return 0;
+    return e8q::gemv_ws_bytes(batch, m, rows, cols);
 }
 
 extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q_escape_t* esc,
@@ -942,7 +997,7 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
         if (st != E8Q_OK) return st;
     }
     if (batch > 65535) return E8Q_ERR_UNSUPPORTED;   // one grid row per batch item
-    if (workspace_bytes < gemv_ws_bytes(batch, m, cols) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    if (workspace_bytes < gemv_ws_bytes(batch, m, rows, cols) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return E8Q_ERR_INVALID;
     const double groups = double(batch) * double(rows) * double(cols / 8);
     if (groups >= 4294967295.0 || double(batch) * double(m) * double(cols / 8) >= 4294967295.0 ||
@@ -960,12 +1015,20 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint64_t* offsets = static_cast<uint64_t*>(workspace);
     float* xt = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_ws_bytes(batch));
-    launch(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
-                       uint64_t(esc_capacity), offsets);
+    uint4* xb = reinterpret_cast<uint4*>(reinterpret_cast<char*>(xt) + gemv_xt_bytes(batch, m, cols));
+    uint32_t* tile_esc = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(xb) + gemv_xb_bytes(batch, m, cols));
+    const uint32_t gpr = uint32_t(cols / 8);
+    const uint64_t tiles = uint64_t(batch) * uint64_t((rows + kGmRows - 1) / kGmRows);
+    const bool mfma = gpr % 32 == 0 && (reinterpret_cast<uintptr_t>(core_idx) & 15u) == 0 && tiles < (uint64_t(1) << 32);
+    // the vector kernel finds escape records through the offsets
+    if (!mfma)
+        launch(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
+               uint64_t(esc_capacity), offsets);
 
     RotArgs ra;
     ra.x = x;
     ra.xt = xt;
+    ra.xb = mfma ? xb : nullptr;
     ra.signs = signs;
     ra.kappa = kappa_for(hb);
     ra.cols = uint32_t(cols);
@@ -978,19 +1041,16 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
     else
         launch_rotate<float>(hb, ra, rot_lds, s);
 
-    const uint32_t gpr = uint32_t(cols / 8);
-    const uint64_t tiles = uint64_t(batch) * uint64_t((rows + kGmRows - 1) / kGmRows);
-    if (gpr % 32 == 0 && (reinterpret_cast<uintptr_t>(core_idx) & 15u) == 0 && tiles < (uint64_t(1) << 32)) {
-        // the matrix-core path
-        uint4* xb = reinterpret_cast<uint4*>(reinterpret_cast<char*>(xt) + gemv_xt_bytes(batch, m, cols));
-        const uint32_t xg = uint32_t(uint64_t(batch) * uint64_t(m) * gpr);
-        launch(gemv_split_kernel, dim3(grid_for(xg, 256, 8)), dim3(256), 0, s, xt, xb, gpr, xg);
+    if (mfma) {
+        // the matrix-core path, then the escaped slots
         GemvMfmaArgs gm;
         gm.core_idx = core_idx;
         gm.esc = reinterpret_cast<const uint32_t*>(esc);
-        gm.offsets = offsets;
+        gm.esc_count = esc_count;
+        gm.esc_capacity = uint64_t(esc_capacity);
         gm.xt = xt;
         gm.xb = xb;
+        gm.tile_esc = tile_esc;
         gm.scale = row_scale;
         gm.tab = tab->dpts_bf16;
         gm.npts = uint32_t(tab->size);
@@ -1003,6 +1063,9 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
         if (m == 1) launch_gemv_mfma<1>(gm, s);
         else if (m == 2) launch_gemv_mfma<2>(gm, s);
         else launch_gemv_mfma<4>(gm, s);
+        if (m == 1) launch(gemv_escape_kernel<1>, dim3(unsigned(batch)), dim3(1024), 0, s, gm);
+        else if (m == 2) launch(gemv_escape_kernel<2>, dim3(unsigned(batch)), dim3(1024), 0, s, gm);
+        else launch(gemv_escape_kernel<4>, dim3(unsigned(batch)), dim3(1024), 0, s, gm);
         return launch_status();
     }
 

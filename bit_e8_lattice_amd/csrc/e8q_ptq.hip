@@ -562,6 +562,7 @@ extern "C" e8q_status_t e8q_ptq_init(const void* w, e8q_dtype_t w_dtype, int64_t
     RotArgs ra;
     ra.x = w;
     ra.xt = v;
+    ra.xb = nullptr;
     ra.signs = signs;
     ra.kappa = 1.0f;                      // the un-normalized transform
     ra.cols = uint32_t(cols);

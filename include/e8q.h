@@ -414,11 +414,13 @@ size_t e8q_decode_workspace_size(int64_t batch);
  *   had_block   as e8q_decode_core_escape (signs NULL: no rotation, W_hat = s z)
  *   x            [batch, m, cols] activations, x_dtype F32 or BF16; m in {1, 2, 4}
  *   y_out        [batch, m, rows] float32
- *   workspace    e8q_gemv_workspace_size(batch, m, cols) bytes, 256-byte aligned
- * Rows whose column count is a multiple of 64, with 16-byte aligned core_idx,
+ *   workspace    e8q_gemv_workspace_size(batch, m, rows, cols) bytes, 256-byte aligned
+ * Rows whose column count is a multiple of 256, with 16-byte aligned core_idx,
  * run on the matrix cores (x~ split into three bfloat16 parts, exact products,
- * float32 sums whose order inside one MFMA is the hardware's); other shapes
- * use float32 FMA chains.  Rounding, either way: |y - W_hat x| <=
+ * float32 sums whose order inside one MFMA is the hardware's); their escaped
+ * slots are added after the row sums, y += (s / 2) * sum of the row's records'
+ * 2z . x~ (float32, in record order, in blocks of 32).  Other shapes use
+ * float32 FMA chains with the escaped slots in place.  Rounding, either way: |y - W_hat x| <=
  * 2 (L + G + 66) 2^-24 S_r + 2^-120 s_r sum_g sum_i |z_gi| per output,
  * L = log2(b), G = ceil(cols / 512), S_r = s_r sum_g sum_i |z_gi| xbar_gi,
  * xbar = kappa_b times the block sums of |x| (|x| itself without rotation).
@@ -438,7 +440,7 @@ e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx,
                                   uint32_t* status_dev, void* stream);
 
 /* Workspace bytes e8q_gemv_core_escape needs (0 on bad sizes). */
-size_t e8q_gemv_workspace_size(int64_t batch, int64_t m, int64_t cols);
+size_t e8q_gemv_workspace_size(int64_t batch, int64_t m, int64_t rows, int64_t cols);
 
 /* ---------------------------------------------------------------------------
  * e8q_pack_escapes -- escape records to root-packed records (E8-QAT Table 3).

@@ -161,7 +161,7 @@ def run_gemv(core, esc, cnt, shape, bound, s, x, signs=None, hb=0, esc_records=N
     batch, rows, cols = shape
     m = x.shape[1]
     st = torch.zeros(1, dtype=torch.int32, device=d)
-    ws = torch.empty(e8q.e8q_gemv_workspace_size(batch, m, cols), dtype=torch.uint8, device=d)
+    ws = torch.empty(e8q.e8q_gemv_workspace_size(batch, m, rows, cols), dtype=torch.uint8, device=d)
     y = torch.empty((batch, m, rows), dtype=torch.float32, device=d)
     e8q.e8q_gemv_core_escape(core, esc, cnt, shape, bound, s, x, y, ws, st, signs=signs, had_block=hb,
                              esc_records=esc_records)

@@ -1,8 +1,9 @@
 """GPU GEMV from the exported form against the float64 product of the exact
 restored weights, within the documented bound (the evaluation order is the
 kernel's own, so the bar is a derived tolerance, not bit equality).  Rows of
-a multiple of 64 columns with 16-byte aligned indices take the matrix-core
-kernel; other shapes and alignments the vector kernel."""
+a multiple of 256 columns with 16-byte aligned indices take the product-table
+kernel (one activation vector, cores of at most 2557 points) or the
+matrix-core kernel; other shapes and alignments the vector kernel."""
 
 import numpy as np
 import pytest
@@ -207,3 +208,41 @@ def test_gemv_clustered_escapes(where):
     out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
     assert out["status"] == 0
     _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, 2048)
+
+
+@pytest.mark.parametrize("cols", [1024, 1000])
+def test_gemv_duplicate_and_unused_records(cols):
+    """A record repeated (same key and point) counts once, and a record whose
+    slot is a core index is ignored: y is the product of the original export
+    and no status bit is set (matrix-core and vector kernels)."""
+    d = device()
+    shape = (2, 40, cols)
+    w = workloads.normal(shape, 2100 + cols, d)
+    s = workloads.rms_scale(w, 1.5)
+    sg = workloads.signs(cols, 2101, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 8, 16)
+    rec, counts, gpb = enc["records"], enc["counts"].copy(), 40 * cols // 8
+    assert counts.min() >= 2
+    parts = []
+    off = 0
+    for b in range(2):
+        r = rec[off:off + counts[b]].copy()
+        off += counts[b]
+        # a duplicate of the second record, right after it
+        r = np.concatenate([r[:2], r[1:2], r[2:]])
+        # a record for a core slot of this item, at its sorted position
+        core_slots = np.nonzero(enc["core_idx"][b * gpb:(b + 1) * gpb] != oracle.ESCAPE_SLOT)[0]
+        extra = np.zeros(1, dtype=oracle.ESCAPE_RECORD_DTYPE)
+        extra["group"] = core_slots[len(core_slots) // 2]
+        extra["two_z"] = 2
+        pos = int(np.searchsorted(r["group"], extra["group"][0]))
+        r = np.concatenate([r[:pos], extra, r[pos:]])
+        parts.append(r)
+        counts[b] = len(r)
+    bad = {"core_idx": enc["core_idx"], "records": np.concatenate(parts), "counts": counts}
+    core, esc, cnt = upload_export(bad, d)
+    x = _x((2, 1, cols), 2102, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 8)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 8, cols)
