@@ -610,9 +610,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
 // 32c + 8q ... 32c + 8q + 7 (a whole 64-byte row segment per four lanes), and
 // step s of the chunk puts group 32c + 8q + s in K slice q (the order of the
 // groups along K is free).  Index words are loaded four chunks ahead, also
-// across the wave's tiles, into four fixed registers.  Every step's MFMA starts from 0; the
-// steps are added in float32 in order, 16 steps (512 columns) per partial
-// sum, the partials in order.  Escaped and malformed slots read the table's
+// across the wave's tiles, into four fixed registers.  Steps go in pairs: the
+// first MFMA starts from 0, the second accumulates onto it (64 products in an
+// order the hardware chooses); the pairs are added in float32 in order, 8
+// pairs (512 columns) per partial sum, the partials in order.  Escaped and malformed slots read the table's
 // zero entry; the sweep only counts the escaped ones (per tile, in the
 // workspace) and flags the malformed ones, and gemv_escape_kernel then adds
 // the escaped slots' records to the finished rows.
@@ -764,10 +765,13 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
                 // indices past the table (escapes, bad slots) read its zero entry
                 const auto products = [&]() {
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const uint4 pt = tab[min(idx[s], a.npts)];
+                    for (int s = 0; s < 8; s += 2) {
+                        const uint4 p0 = tab[min(idx[s], a.npts)];
+                        const uint4 p1 = tab[min(idx[s + 1], a.npts)];
+                        const gm_f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(gm_bf16x8, p0), __builtin_bit_cast(gm_bf16x8, xc[s]), zero, 0, 0, 0);
                         const gm_f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(gm_bf16x8, pt), __builtin_bit_cast(gm_bf16x8, xc[s]), zero, 0, 0, 0);
+                            __builtin_bit_cast(gm_bf16x8, p1), __builtin_bit_cast(gm_bf16x8, xc[s + 1]), d0, 0, 0, 0);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc1[r] = acc1[r] + d[r];
                     }

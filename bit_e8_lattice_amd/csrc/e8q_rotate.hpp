@@ -61,10 +61,12 @@ __global__ __launch_bounds__(kBlock) void rotate_act_kernel(RotArgs a) {
     const LaneFwht lf = lane_fwht<(HB > 128 ? 128 : HB)>(lane);
     const uint32_t lpos = wv * kWave + (lane & ~15u) + lf.logical;
     const uint32_t glast = a.groups - 1u;
-    for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
-#pragma unroll 1
-        for (int j = 0; j < kItems; ++j) {
-            const uint32_t g = tile * kTileGroups + uint32_t(j) * kBlock + lpos;
+    // one item (kBlock groups) of a tile per step, so that short inputs (an
+    // activation vector per batch item) still spread over many blocks
+    for (uint32_t ti = blockIdx.x; ti < a.num_tiles * uint32_t(kItems); ti += gridDim.x) {
+        {
+            const uint32_t tile = ti / uint32_t(kItems), j = ti - tile * uint32_t(kItems);
+            const uint32_t g = tile * kTileGroups + j * kBlock + lpos;
             const uint32_t gl = min(g, glast);
             const Raw raw = load_raw<WT>(a.x, gl);
             float v[8];
@@ -92,20 +94,25 @@ __global__ __launch_bounds__(kBlock) void rotate_act_kernel(RotArgs a) {
     }
 }
 
+template <typename K>
+inline void launch_tiles_items(K kernel, const RotArgs& a, uint64_t tiles, unsigned block, size_t lds, hipStream_t st) {
+    launch_tiles(kernel, a, tiles * uint64_t(kItems), block, lds, st);
+}
+
 template <typename WT>
 inline void launch_rotate(int hb, const RotArgs& a, size_t lds, hipStream_t st) {
     switch (hb) {
-        case 0: launch_tiles(rotate_act_kernel<WT, 0>, a, a.num_tiles, kBlock, lds, st); break;
-        case 8: launch_tiles(rotate_act_kernel<WT, 8>, a, a.num_tiles, kBlock, lds, st); break;
-        case 16: launch_tiles(rotate_act_kernel<WT, 16>, a, a.num_tiles, kBlock, lds, st); break;
-        case 32: launch_tiles(rotate_act_kernel<WT, 32>, a, a.num_tiles, kBlock, lds, st); break;
-        case 64: launch_tiles(rotate_act_kernel<WT, 64>, a, a.num_tiles, kBlock, lds, st); break;
-        case 128: launch_tiles(rotate_act_kernel<WT, 128>, a, a.num_tiles, kBlock, lds, st); break;
-        case 256: launch_tiles(rotate_act_kernel<WT, 256>, a, a.num_tiles, kBlock, lds, st); break;
-        case 512: launch_tiles(rotate_act_kernel<WT, 512>, a, a.num_tiles, kBlock, lds, st); break;
-        case 1024: launch_tiles(rotate_act_kernel<WT, 1024>, a, a.num_tiles, kBlock, lds, st); break;
-        case 2048: launch_tiles(rotate_act_kernel<WT, 2048>, a, a.num_tiles, kBlock, lds, st); break;
-        case 4096: launch_tiles(rotate_act_kernel<WT, 4096>, a, a.num_tiles, kBlock, lds, st); break;
+        case 0: launch_tiles_items(rotate_act_kernel<WT, 0>, a, a.num_tiles, kBlock, lds, st); break;
+        case 8: launch_tiles_items(rotate_act_kernel<WT, 8>, a, a.num_tiles, kBlock, lds, st); break;
+        case 16: launch_tiles_items(rotate_act_kernel<WT, 16>, a, a.num_tiles, kBlock, lds, st); break;
+        case 32: launch_tiles_items(rotate_act_kernel<WT, 32>, a, a.num_tiles, kBlock, lds, st); break;
+        case 64: launch_tiles_items(rotate_act_kernel<WT, 64>, a, a.num_tiles, kBlock, lds, st); break;
+        case 128: launch_tiles_items(rotate_act_kernel<WT, 128>, a, a.num_tiles, kBlock, lds, st); break;
+        case 256: launch_tiles_items(rotate_act_kernel<WT, 256>, a, a.num_tiles, kBlock, lds, st); break;
+        case 512: launch_tiles_items(rotate_act_kernel<WT, 512>, a, a.num_tiles, kBlock, lds, st); break;
+        case 1024: launch_tiles_items(rotate_act_kernel<WT, 1024>, a, a.num_tiles, kBlock, lds, st); break;
+        case 2048: launch_tiles_items(rotate_act_kernel<WT, 2048>, a, a.num_tiles, kBlock, lds, st); break;
+        case 4096: launch_tiles_items(rotate_act_kernel<WT, 4096>, a, a.num_tiles, kBlock, lds, st); break;
         default: break;
     }
 }
