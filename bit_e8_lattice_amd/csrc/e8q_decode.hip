@@ -658,7 +658,8 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
     constexpr uint32_t kWaves = X_LDS ? 16u : 8u;
     constexpr uint32_t kThreads = kWaves * kWave;
     extern __shared__ uint4 s_gm[];
-    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+    // the wave index in a scalar register: the index ring's bookkeeping is wave-uniform
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t tab_n = LDS_TAB ? a.npts + 1u : 0u;
     const uint32_t xs_n = X_LDS ? uint32_t(M) * 3u * a.gpr : 0u;
     uint4* s_x = s_gm + tab_n;
