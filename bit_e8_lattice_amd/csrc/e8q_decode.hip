@@ -749,7 +749,7 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
         // to a multiple of kGmAhead (padding chunks only refill), so no slot
         // rotates -- a rotation's register moves would wait for the newest load.
         const auto chunk = [&](uint4& slot, uint32_t c) {
-            const uint4 w = slot;
+            uint4 w = slot;
             slot = next_word();
             if (c < nc) {
                 // only the 3M lanes of real columns load (the D columns of the
@@ -759,16 +759,49 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
                     for (int s = 0; s < 8; ++s)
                         xc[s] = X_LDS ? xp[(32u * c + 4u * uint32_t(s)) * 3u * M] : xp[32u * c + uint32_t(s)];
                 }
+                // the largest of the eight 16-bit indices (packed 16-bit maxima)
+                const gm_u16x2 mx = __builtin_elementwise_max(
+                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.x), __builtin_bit_cast(gm_u16x2, w.y)),
+                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.z), __builtin_bit_cast(gm_u16x2, w.w)));
+                const bool big = uint32_t(mx.x > mx.y ? mx.x : mx.y) >= a.npts;
+                if (__ballot(big)) {
+                    // rare: escaped slots counted, malformed ones flagged, and
+                    // every index past the table set to its zero entry
+                    if (big) {
+                        if (row_ok) {
+#pragma unroll 1
+                            for (uint32_t s = 0; s < 8; ++s) {
+                                const uint32_t h = s >> 1;
+                                const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
+                                const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
+                                if (id == 0xFFFFu) ++nesc;
+                                else if (id >= a.npts) flags |= E8Q_STATUS_BAD_INDEX;
+                            }
+                        }
+                        const gm_u16x2 lim = {uint16_t(a.npts), uint16_t(a.npts)};
+                        w.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.x), lim));
+                        w.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.y), lim));
+                        w.z = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.z), lim));
+                        w.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.w), lim));
+                    }
+                }
                 const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-                uint32_t idx[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) idx[s] = (wd[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
-                // indices past the table (escapes, bad slots) read its zero entry
+                // table entries are 16 bytes; with the table in LDS (fewer than
+                // 4096 points, every index now <= npts) the high index's byte
+                // offset is word >> 12 (the low index is below 2^12)
+                const auto entry = [&](int s) {
+                    if constexpr (LDS_TAB) {
+                        const uint32_t off = (s & 1) ? (wd[s >> 1] >> 12) : ((wd[s >> 1] << 4) & 0xFFFF0u);
+                        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tab) + off);
+                    } else {
+                        return tab[(wd[s >> 1] >> (16 * (s & 1))) & 0xFFFFu];
+                    }
+                };
                 const auto products = [&]() {
 #pragma unroll
                     for (int s = 0; s < 8; s += 2) {
-                        const uint4 p0 = tab[min(idx[s], a.npts)];
-                        const uint4 p1 = tab[min(idx[s + 1], a.npts)];
+                        const uint4 p0 = entry(s);
+                        const uint4 p1 = entry(s + 1);
                         const gm_f32x4 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             __builtin_bit_cast(gm_bf16x8, p0), __builtin_bit_cast(gm_bf16x8, xc[s]), zero, 0, 0, 0);
                         const gm_f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -777,24 +810,6 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
                         for (int r = 0; r < 4; ++r) acc1[r] = acc1[r] + d[r];
                     }
                 };
-                // the largest of the eight 16-bit indices (packed 16-bit maxima)
-                const gm_u16x2 mx = __builtin_elementwise_max(
-                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.x), __builtin_bit_cast(gm_u16x2, w.y)),
-                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.z), __builtin_bit_cast(gm_u16x2, w.w)));
-                const bool any = row_ok && uint32_t(mx.x > mx.y ? mx.x : mx.y) >= a.npts;
-                if (__ballot(any)) {
-                    // rare: escaped slots counted, malformed ones flagged
-                    if (any) {
-#pragma unroll 1
-                        for (uint32_t s = 0; s < 8; ++s) {
-                            const uint32_t h = s >> 1;
-                            const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
-                            const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
-                            if (id == 0xFFFFu) ++nesc;
-                            else if (id >= a.npts) flags |= E8Q_STATUS_BAD_INDEX;
-                        }
-                    }
-                }
                 products();
                 if ((c & 1u) == 1u || c + 1u == nc) {
 #pragma unroll
@@ -962,12 +977,13 @@ static void launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t st) {
     const size_t xs = size_t(M) * 3 * a.gpr * 16;
     const size_t red16 = 16 * 256 * 4, red8 = 8 * 256 * 4;
     const uint64_t tiles_per_b = a.tiles_per_b, batch = a.tiles / a.tiles_per_b;
-    if (tab + xs + red16 <= 160 * 1024) {
+    // a table in LDS has fewer than 4096 entries (the sweep's byte offsets rely on it)
+    if (a.npts < 4096 && tab + xs + red16 <= 160 * 1024) {
         const uint64_t units = batch * ((tiles_per_b + 15) / 16);
         launch_tiles(gemv_mfma_kernel<M, true, true>, a, units, 1024, tab + xs + red16, st);
     } else {
         const uint64_t units = batch * ((tiles_per_b + 7) / 8);
-        if (tab <= 48 * 1024)
+        if (a.npts < 4096 && tab <= 48 * 1024)
             launch_tiles(gemv_mfma_kernel<M, true, false>, a, units, 512, tab + red8, st);
         else
             launch_tiles(gemv_mfma_kernel<M, false, false>, a, units, 512, red8, st);
