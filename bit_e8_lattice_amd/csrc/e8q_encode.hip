@@ -484,16 +484,29 @@ __global__ __launch_bounds__(256) void encode_place_kernel(EncodeArgs a) {
         const unsigned long long base = run + (incl - tot);
         run += __shfl(incl, 63, 64);
         if (t == first || tot == 0u || tot > kStagedRecs) continue;
-        const uint32_t* src = a.staged + t * kStagedRecs * 5u;
+        // the staging area and the record list never overlap: four records'
+        // loads are issued before their stores
+        const uint32_t* __restrict__ src = a.staged + t * kStagedRecs * 5u;
+        uint32_t* __restrict__ dst = reinterpret_cast<uint32_t*>(a.esc);
         uint32_t flags = 0;
-        for (uint32_t r = 0; r < tot; ++r) {
-            const unsigned long long pos = base + r;
-            if (pos < a.esc_cap) {
-                uint32_t* dst = reinterpret_cast<uint32_t*>(a.esc + pos);
+        for (uint32_t r0 = 0; r0 < tot; r0 += 4u) {
+            uint32_t v[4][5];
 #pragma unroll
-                for (int i = 0; i < 5; ++i) dst[i] = src[r * 5u + i];
-            } else {
-                flags |= E8Q_STATUS_ESC_OVERFLOW;
+            for (uint32_t k = 0; k < 4u; ++k)
+                if (r0 + k < tot) {
+#pragma unroll
+                    for (int i = 0; i < 5; ++i) v[k][i] = src[(r0 + k) * 5u + uint32_t(i)];
+                }
+#pragma unroll
+            for (uint32_t k = 0; k < 4u; ++k) {
+                if (r0 + k >= tot) break;
+                const unsigned long long pos = base + r0 + k;
+                if (pos < a.esc_cap) {
+#pragma unroll
+                    for (int i = 0; i < 5; ++i) dst[pos * 5u + uint64_t(i)] = v[k][i];
+                } else {
+                    flags |= E8Q_STATUS_ESC_OVERFLOW;
+                }
             }
         }
         if (flags) atomicOr(a.status, flags);
