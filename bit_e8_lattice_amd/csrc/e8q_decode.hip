@@ -628,6 +628,8 @@ struct GemvMfmaArgs {
     const uint32_t* esc;
     const int64_t* esc_count;
     uint64_t esc_capacity;
+    const uint64_t* offsets;   // record offsets per item (decode_offsets_kernel), or null:
+                               // each escape block then sums the counts before its item
     const float* xt;           // [batch, m, cols] x~ (float32), for the escaped slots
     const uint4* xb;           // [batch, m, 3, gpr] x~ parts hi, mid, lo (8 bf16 per group)
     uint32_t* tile_esc;        // [batch, tiles_per_b] escaped slots per 16-row tile
@@ -862,7 +864,8 @@ __global__ __launch_bounds__(1024) void gemv_escape_kernel(GemvMfmaArgs a) {
     const uint32_t nw = blockDim.x >> 6;
     // records before this item, and this item's escaped slots
     uint64_t before = 0, slots = 0;
-    for (uint32_t i = tid; i < b; i += blockDim.x) before += a.esc_count[i] > 0 ? uint64_t(a.esc_count[i]) : 0ull;
+    if (!a.offsets)
+        for (uint32_t i = tid; i < b; i += blockDim.x) before += a.esc_count[i] > 0 ? uint64_t(a.esc_count[i]) : 0ull;
     for (uint32_t i = tid; i < a.tiles_per_b; i += blockDim.x) slots += a.tile_esc[uint64_t(b) * a.tiles_per_b + i];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -881,7 +884,8 @@ __global__ __launch_bounds__(1024) void gemv_escape_kernel(GemvMfmaArgs a) {
         slots += s_sum[16u + w];
     }
     const uint64_t own = a.esc_count[b] > 0 ? uint64_t(a.esc_count[b]) : 0ull;
-    const uint64_t first = min(before, a.esc_capacity), end = min(before + own, a.esc_capacity);
+    const uint64_t first = a.offsets ? a.offsets[b] : min(before, a.esc_capacity);
+    const uint64_t end = a.offsets ? a.offsets[b + 1] : min(before + own, a.esc_capacity);
     const uint64_t gpb = uint64_t(a.rows) * a.gpr;
     const uint16_t* slot_idx = a.core_idx + uint64_t(b) * gpb;
     uint64_t matched = 0;
@@ -1041,8 +1045,11 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
     const uint32_t gpr = uint32_t(cols / 8);
     const uint64_t tiles = uint64_t(batch) * uint64_t((rows + kGmRows - 1) / kGmRows);
     const bool mfma = gpr % 32 == 0 && (reinterpret_cast<uintptr_t>(core_idx) & 15u) == 0 && tiles < (uint64_t(1) << 32);
-    // the vector kernel finds escape records through the offsets
-    if (!mfma)
+    // the vector kernel finds escape records through the offsets; so do the
+    // escape blocks of the matrix-core path when the batch is large (each
+    // would otherwise sum the counts of every item before its own)
+    const bool scan = !mfma || batch > 1024;
+    if (scan)
         launch(decode_offsets_kernel, dim3(1), dim3(1024), 0, s, esc_count, uint32_t(batch),
                uint64_t(esc_capacity), offsets);
 
@@ -1069,6 +1076,7 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
         gm.esc = reinterpret_cast<const uint32_t*>(esc);
         gm.esc_count = esc_count;
         gm.esc_capacity = uint64_t(esc_capacity);
+        gm.offsets = scan ? offsets : nullptr;
         gm.xt = xt;
         gm.xb = xb;
         gm.tile_esc = tile_esc;

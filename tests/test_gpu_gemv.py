@@ -265,3 +265,21 @@ def test_gemv_deterministic(m):
     b = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
     assert a["status"] == 0 and b["status"] == 0
     assert np.array_equal(a["y"].view(np.uint64), b["y"].view(np.uint64))
+
+
+def test_gemv_many_batch_items():
+    """More than 1024 batch items on the matrix-core path: the escape blocks
+    take their record ranges from the offsets scan."""
+    d = device()
+    shape = (1100, 16, 256)
+    w = workloads.normal(shape, 2300, d)
+    s = workloads.rms_scale(w, 1.5)
+    sg = workloads.signs(256, 2301, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, 16)
+    assert (enc["counts"] > 0).sum() > 1000
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((1100, 1, 256), 2302, d)
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
+    assert out["status"] == 0
+    _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, 256)
