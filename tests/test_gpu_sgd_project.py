@@ -146,8 +146,11 @@ def test_fused_restore_matches_unfused(hb, wh_dtype):
               {"q": o2["wh"], "tz": o2["tz"], "esc": o2["esc"], "st": o2["st"]})
 
 
-@pytest.mark.parametrize("hb,shape", [(128, (2, 24, 1024)), (16, (1, 12, 272)), (1024, (1, 16, 2048))])
-def test_fused_rotated_grad_matches_unfused(hb, shape):
+@pytest.mark.parametrize("hb,shape,q_dtype,tz", [(128, (2, 24, 1024), torch.bfloat16, True),
+                                               (16, (1, 12, 272), torch.bfloat16, True),
+                                               (1024, (1, 16, 2048), torch.bfloat16, True),
+                                               (8, (3, 5, 136), torch.float32, False)])
+def test_fused_rotated_grad_matches_unfused(hb, shape, q_dtype, tz):
     """The gradient taken back through the rotation: latents, q, escape counts
     and status bit for bit as e8q_ste_backward_hadamard +
     e8q_project_hadamard, also with non-finite gradient values."""
@@ -156,12 +159,12 @@ def test_fused_rotated_grad_matches_unfused(hb, shape):
     s = workloads.rms_scale(w, 1.5)
     sg = workloads.signs(shape[2], 751, d)
     w1, w2 = w.clone(), w.clone()
-    o1, o2 = _outputs(w, torch.bfloat16, True), _outputs(w, torch.bfloat16, True)
+    o1, o2 = _outputs(w, q_dtype, tz), _outputs(w, q_dtype, tz)
     for k in range(3):
         g = workloads.normal(shape, 760 + k, d, std=0.05)
         if k == 2:
             g[0, 1, 3] = float("nan")
-            g[0, 2, 5] = float("inf")
+            g[0, 2 % shape[1], 5] = float("inf")
         e8q.e8q_ste_backward_hadamard(g, sg, hb, w_latent=w1, lr=0.5)
         e8q.e8q_project_hadamard(w1, s, sg, hb, o1["st"], q_out=o1["q"], two_z_out=o1["tz"], core_bound=16,
                                  esc_count_out=o1["esc"])
