@@ -283,13 +283,13 @@ __device__ __forceinline__ bool fast_point(const float (&x)[8], uint32_t& t0, ui
     const uint32_t n1 = __builtin_amdgcn_perm(yb[5], yb[4], 0x0C0C0400u) | __builtin_amdgcn_perm(yb[7], yb[6], 0x04000C0Cu);
     const uint32_t m0 = __builtin_amdgcn_perm(db[1], db[0], 0x0C0C0B09u) | __builtin_amdgcn_perm(db[3], db[2], 0x0B090C0Cu);
     const uint32_t m1 = __builtin_amdgcn_perm(db[5], db[4], 0x0C0C0B09u) | __builtin_amdgcn_perm(db[7], db[6], 0x0B090C0Cu);
-    // parity of sum(n) and of sum(floor) = sum(n) - #(d < 0)
-    // byte sums with v_sad_u8 (sum of |byte - 0|): it pairs with other VALU
-    // instructions, v_dot4 does not
+    // parity of sum(n) and of sum(floor) = sum(n) - #(d < 0): byte sums with
+    // v_sad_u8 (sum of |byte - 0|; it pairs with other VALU instructions,
+    // v_dot4 does not), where a 0xFF byte of m adds 255, as odd as 1
     const uint32_t nsum = __builtin_amdgcn_sad_u8(n0, 0u, __builtin_amdgcn_sad_u8(n1, 0u, 0u));
-    const uint32_t negs8 = uint32_t(__builtin_popcount(m0)) + uint32_t(__builtin_popcount(m1));
+    const uint32_t fsum = __builtin_amdgcn_sad_u8(m0, 0u, __builtin_amdgcn_sad_u8(m1, 0u, nsum));
     const bool odd0 = (nsum & 1u) != 0u;
-    const bool odd1 = ((nsum + (negs8 >> 3)) & 1u) != 0u;
+    const bool odd1 = (fsum & 1u) != 0u;
     const float sa = ((fabsf(d[0]) + fabsf(d[1])) + (fabsf(d[2]) + fabsf(d[3]))) +
                      ((fabsf(d[4]) + fabsf(d[5])) + (fabsf(d[6]) + fabsf(d[7])));
     const float amax = fmaxf(fmaxf(fmaxf(fabsf(d[0]), fabsf(d[1])), fmaxf(fabsf(d[2]), fabsf(d[3]))),
@@ -304,34 +304,34 @@ __device__ __forceinline__ bool fast_point(const float (&x)[8], uint32_t& t0, ui
     const float tq1 = odd0 ? tq0 + fmaf(-2.0f, amax, 1.0f) : tq0;
     const float tq = odd1 ? fmaf(-2.0f, amin, tq1) : tq1;
     const bool fast = (xmax < kFastXMax) && (amin > 0.0f) && (fabsf(tq) > kFastDecision);
-    if (!fast) return false;
     d8 = tq < 0.0f;
-    // 2z + 64: D8 -> 2(n + 32); D8+1/2 -> 2(n + 32) + 1 - 2[d < 0]
-    const uint32_t hb = d8 ? 0u : 0x01010101u;
-    const uint32_t hn = d8 ? 0u : 0x02020202u;
-    t0 = ((n0 << 1) | hb) - (m0 & hn);
-    t1 = ((n1 << 1) | hb) - (m1 & hn);
-    // parity fix: first coordinate with |d| equal to the max (D8) or min (D8+1/2)
-    const float tgt = d8 ? amax : amin;
-    const bool fixon = (d8 && odd0) || (!d8 && odd1);
-    // the first match in each word (later matches are overwritten), and the
-    // second word's only when the first word has none
-    uint32_t sel0 = 0u, sel1 = 0u;
+    const bool fixon = (d8 && odd0) || (!d8 && odd1);   // lane masks: scalar logic
+    if (!fast) return false;
+    // e_i = w |d_i| + u is +0 exactly where |d_i| equals the target (the
+    // largest |d| for D8, the smallest for D8+1/2) and negative elsewhere (one
+    // rounding of an exact difference keeps its sign); -inf everywhere when
+    // the candidate's parity needs no fix
+    const float w = d8 ? 1.0f : -1.0f;
+    const float u = fixon ? (d8 ? -amax : amin) : -__builtin_inff();
+    uint32_t eb[8];
 #pragma unroll
-    for (int i = 3; i >= 0; --i) {
-        sel0 = fabsf(d[i]) == tgt ? (0xFFu << (8 * i)) : sel0;
-        sel1 = fabsf(d[4 + i]) == tgt ? (0xFFu << (8 * i)) : sel1;
-    }
-    sel1 = sel0 != 0u ? 0u : sel1;
-    sel0 = fixon ? sel0 : 0u;
-    sel1 = fixon ? sel1 : 0u;
-    // D8 moves the coordinate by +2 sgn(d), D8+1/2 by -2 sgn(d)
+    for (int i = 0; i < 8; ++i) eb[i] = __float_as_uint(fmaf(fabsf(d[i]), w, u));
+    // 0xFF bytes where e_i < 0, then 0x01 at the first (lowest-index) byte
+    // that is 0x00, if any: ~ne & (ne + 1) over the 64-bit pair
+    const uint32_t ne0 = __builtin_amdgcn_perm(eb[1], eb[0], 0x0C0C0B09u) | __builtin_amdgcn_perm(eb[3], eb[2], 0x0B090C0Cu);
+    const uint32_t ne1 = __builtin_amdgcn_perm(eb[5], eb[4], 0x0C0C0B09u) | __builtin_amdgcn_perm(eb[7], eb[6], 0x0B090C0Cu);
+    const uint64_t ne = (uint64_t(ne1) << 32) | ne0;
+    const uint64_t lb = ~ne & (ne + 1ull);
+    const uint32_t l0 = uint32_t(lb), l1 = uint32_t(lb >> 32);
+    // 2z + 64: D8 -> 2(n + 32); D8+1/2 -> 2(n + 32) + 1 - 2[d < 0].  The fix
+    // moves the coordinate by +2 sgn(d) (D8) or -2 sgn(d) (D8+1/2): by -2
+    // where X = m ^ (D8 ? 0 : ~0) has 0xFF, else by +2, i.e. + 2 l - 4 (l & X).
+    // Every byte stays in [2, 126] (|n| <= 30), so no carry or borrow crosses
+    // a byte.
     const uint32_t dm = d8 ? 0u : 0xFFFFFFFFu;
-    const uint32_t mx0 = m0 ^ dm, mx1 = m1 ^ dm;
-    t0 = t0 + __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x20) -
-         __builtin_amdgcn_bitop3_b32(sel0, mx0, 0x02020202u, 0x80);
-    t1 = t1 + __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x20) -
-         __builtin_amdgcn_bitop3_b32(sel1, mx1, 0x02020202u, 0x80);
+    const uint32_t hb = dm & 0x01010101u, hn = dm & 0x02020202u;
+    t0 = (((n0 << 1) | hb) + (l0 << 1)) - ((m0 & hn) + ((l0 & (m0 ^ dm)) << 2));
+    t1 = (((n1 << 1) | hb) + (l1 << 1)) - ((m1 & hn) + ((l1 & (m1 ^ dm)) << 2));
     return true;
 }
 

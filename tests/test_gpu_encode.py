@@ -218,3 +218,19 @@ def test_tile_escape_counts_around_the_staging_limit(cap):
                                     esc_capacity=(w.numel() // 8 if cap is None else cap))
     assert int(ref["counts"].sum()) == sum(per_tile)
     _compare(out, ref)
+
+
+@pytest.mark.parametrize("rows,cols", [(13, 4096), (5, 8192), (3, 12288)])
+@pytest.mark.parametrize("alpha", [1.0, 2.6])
+def test_row_items(rows, cols, alpha):
+    """Rows of 4096, 8192 and 12288 columns (one, two and three 512-group items
+    of a tile per row), a batch of 2 whose group count leaves the last tile
+    partly empty; 2.6 x RMS lists a few escapes per tile, 1 x RMS takes the
+    second pass."""
+    d = device()
+    w = workloads.normal((2, rows, cols), 7000 + rows, d)
+    s = workloads.rms_scale(w, alpha)
+    sg = workloads.signs(cols, 7100 + rows, d)
+    out = run_encode(w, s, 16, sg, 128)
+    ref = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sg.cpu().numpy(), 128, 16)
+    _compare(out, ref)
