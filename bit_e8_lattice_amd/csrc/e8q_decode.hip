@@ -635,6 +635,7 @@ struct GemvMfmaArgs {
     uint32_t* tile_esc;        // [batch, tiles_per_b] escaped slots per 16-row tile
     const float* scale;
     const uint4* tab;          // [npts + 1] points as 8 bf16 (entry npts: zero)
+    const uint32_t* pts8;      // [npts] points as 2z + 64 bytes, two words each (int8 kernel)
     uint32_t npts;
     uint32_t rows;
     uint32_t gpr;
@@ -653,24 +654,17 @@ __device__ __forceinline__ void gm_wave_sync() {
 
 // Work units: (batch item, kWaves consecutive tiles); each wave takes one
 // tile of a unit, a block a contiguous range of units (so its waves read
-// neighbouring rows and, with X_LDS, share one batch item's activation parts,
-// staged in LDS when the item changes).
-template <int M, bool LDS_TAB, bool X_LDS>
-__global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMfmaArgs a) {
-    constexpr uint32_t kWaves = X_LDS ? 16u : 8u;
-    constexpr uint32_t kThreads = kWaves * kWave;
+// neighbouring rows).  This kernel serves the cores of 4096 points or more
+// (B >= 24; smaller cores take gemv_i8_kernel): the point table and the
+// activation parts are read from global memory.
+template <int M>
+__global__ __launch_bounds__(512, 4) void gemv_mfma_kernel(GemvMfmaArgs a) {
+    constexpr uint32_t kWaves = 8u;
     extern __shared__ uint4 s_gm[];
     // the wave index in a scalar register: the index ring's bookkeeping is wave-uniform
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t tab_n = LDS_TAB ? a.npts + 1u : 0u;
-    const uint32_t xs_n = X_LDS ? uint32_t(M) * 3u * a.gpr : 0u;
-    uint4* s_x = s_gm + tab_n;
-    float* s_red = reinterpret_cast<float*>(s_gm + tab_n + xs_n) + wv * 256u;
-    if constexpr (LDS_TAB) {
-        for (uint32_t i = tid; i <= a.npts; i += kThreads) s_gm[i] = a.tab[i];
-        __syncthreads();
-    }
-    const uint4* tab = LDS_TAB ? s_gm : a.tab;
+    float* s_red = reinterpret_cast<float*>(s_gm) + wv * 256u;
+    const uint4* tab = a.tab;
     const uint32_t i16 = lane & 15u, q = lane >> 4;
     const uint32_t nc = a.gpr >> 5;                 // chunks of 32 groups per row
     const uint32_t ncp = (nc + uint32_t(kGmAhead) - 1u) / uint32_t(kGmAhead) * uint32_t(kGmAhead);
@@ -709,38 +703,18 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
     uint4 wq[kGmAhead];
 #pragma unroll
     for (int k = 0; k < kGmAhead; ++k) wq[k] = next_word();
-    uint32_t staged = 0xFFFFFFFFu;
     uint4 xc[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) xc[s] = make_uint4(0u, 0u, 0u, 0u);
     for (uint32_t u = u_begin; u < u_end; ++u) {
         const uint32_t b = u / units_per_b;
-        if constexpr (X_LDS) {
-            if (b != staged) {   // block-uniform
-                __syncthreads();
-                // staged in step order: entry ((8c + s) 4 + q) 3M + n holds column
-                // n's part for group 32c + 8q + s, so that the lanes of one
-                // step read consecutive entries (no bank conflicts)
-                const uint4* src = a.xb + uint64_t(b) * xs_n;
-                for (uint32_t i = tid; i < xs_n; i += kThreads) {
-                    const uint32_t n = i % (3u * M), rest = i / (3u * M);
-                    const uint32_t qq = rest & 3u, cs = rest >> 2;
-                    const uint32_t g = 32u * (cs >> 3) + 8u * qq + (cs & 7u);
-                    s_x[i] = src[n * a.gpr + g];
-                }
-                __syncthreads();
-                staged = b;
-            }
-        }
         const uint32_t t = wave_tile(u);
         if (t >= a.tiles_per_b) continue;
         const uint32_t r0 = t * kGmRows;
         const bool row_ok = r0 + i16 < a.rows;
         const uint32_t row = row_ok ? r0 + i16 : a.rows - 1u;   // rows past the end repeat the last
-        // this lane's activation part: step s of chunk c at xp[32c + s] (global,
-        // [batch, m, 3, gpr]) or at xp[(32c + 4s) 3M] (LDS, step order)
-        const uint4* xp = X_LDS ? s_x + (q * 3u * M + i16)
-                                : a.xb + uint64_t(b) * M * 3u * a.gpr + (bcol ? i16 : 0u) * a.gpr + 8u * q;
+        // this lane's activation part: step s of chunk c at xp[32c + s] ([batch, m, 3, gpr])
+        const uint4* xp = a.xb + uint64_t(b) * M * 3u * a.gpr + (bcol ? i16 : 0u) * a.gpr + 8u * q;
         // the row scale of lane (row) l < 16, loaded now and used at the end
         const float s_row = a.scale[uint64_t(b) * a.rows + min(r0 + (lane & 15u), a.rows - 1u)];
         gm_f32x4 acc1 = zero, acc2 = zero;
@@ -759,7 +733,7 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
                 if (bcol) {
 #pragma unroll
                     for (int s = 0; s < 8; ++s)
-                        xc[s] = X_LDS ? xp[(32u * c + 4u * uint32_t(s)) * 3u * M] : xp[32u * c + uint32_t(s)];
+                        xc[s] = xp[32u * c + uint32_t(s)];
                 }
                 // the largest of the eight 16-bit indices (packed 16-bit maxima)
                 const gm_u16x2 mx = __builtin_elementwise_max(
@@ -788,17 +762,8 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
                     }
                 }
                 const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-                // table entries are 16 bytes; with the table in LDS (fewer than
-                // 4096 points, every index now <= npts) the high index's byte
-                // offset is word >> 12 (the low index is below 2^12)
-                const auto entry = [&](int s) {
-                    if constexpr (LDS_TAB) {
-                        const uint32_t off = (s & 1) ? (wd[s >> 1] >> 12) : ((wd[s >> 1] << 4) & 0xFFFF0u);
-                        return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tab) + off);
-                    } else {
-                        return tab[(wd[s >> 1] >> (16 * (s & 1))) & 0xFFFFu];
-                    }
-                };
+                // every index is now <= npts (entry npts: zero)
+                const auto entry = [&](int s) { return tab[(wd[s >> 1] >> (16 * (s & 1))) & 0xFFFFu]; };
                 const auto products = [&]() {
 #pragma unroll
                     for (int s = 0; s < 8; s += 2) {
@@ -841,6 +806,252 @@ __global__ __launch_bounds__(X_LDS ? 1024 : 512, 4) void gemv_mfma_kernel(GemvMf
             for (int v = 0; v < M; ++v) {
                 const float dv = (d[3 * v] + d[3 * v + 1]) + d[3 * v + 2];
                 a.y[(uint64_t(b) * M + uint32_t(v)) * a.rows + r] = bad ? 0.0f : (0.5f * s) * dv;
+            }
+        }
+        gm_wave_sync();
+    }
+    flush_status(flags, a.status);
+}
+
+// ---------------------------------------------------------------------------
+// The GEMV on the int8 matrix cores (same shapes as gemv_mfma_kernel, table and
+// activations in LDS).  Each activation vector is held in fixed point: with e
+// the exponent of its largest |x~| (2^(e-1) <= max < 2^e), N_k = rint(x~_k
+// 2^(30-e)) (|N_k| <= 2^30) is written as four signed base-256 digits,
+// N = ((D0 256 + D1) 256 + D2) 256 + D3, D_i in [-128, 127].  One
+// v_mfma_i32_16x16x64_i8 takes 16 rows x 8 groups:
+//   A (16 x 64): the rows' points as signed bytes 2z (8 bytes per table entry,
+//     entry npts zero), two groups per lane;
+//   B (64 x 16): the same groups' digits, column 4v + d holding digit d of
+//     vector v (columns >= 4M unused);
+//   D (16 x 16) int32, accumulated over the whole row: every product and sum
+//     is exact (|2z_i| <= 6, |D| <= 128, cols < 2^19).
+// The row's y is then (s/2) 2^(e-30) ((I0 256 + I1) 256 + I2) 256 + I3 from the
+// four column sums (an exact int64, exact in float64 below 2^53), rounded once
+// to float32 after one float64 product: the only errors are the fixed-point
+// step (|x~ - N 2^(e-30)| <= 2^(e-31)) and those two roundings.  Lane l holds
+// row l % 16 of the tile in A; lane quarter q = l / 16 loads the index word of
+// groups 32c + 8q ... 32c + 8q + 7, and step s of the chunk puts groups
+// 32c + 8q + 2s, +1 in its K slice.  The same byte positions of A and B hold
+// the same group, so the K order the hardware uses does not matter.  Index
+// words run kI8Ahead chunks ahead, as in gemv_mfma_kernel; escaped and
+// malformed slots read the zero entry and are handled the same way.  A vector
+// with a non-finite x~ gives NaN rows and E8Q_STATUS_NONFINITE.
+typedef int gm_i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kI8Ahead = 4;   // index words (chunks) loaded ahead
+
+template <int M>
+__global__ __launch_bounds__(1024, 4) void gemv_i8_kernel(GemvMfmaArgs a) {
+    constexpr uint32_t kWaves = 16u;
+    constexpr uint32_t kThreads = kWaves * kWave;
+    constexpr uint32_t NCOL = 4u * uint32_t(M);
+    extern __shared__ uint4 s_gm[];   // table first (no static LDS: its offsets need no base)
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t cols = a.gpr * 8u;
+    const uint32_t tab_u4 = (a.npts + 2u) / 2u;      // 16-byte units holding npts + 1 entries of 8 bytes
+    const uint32_t xs_n = NCOL * (a.gpr / 2u);        // 16-byte digit entries: per pair of groups, per column
+    uint2* s_tab = reinterpret_cast<uint2*>(s_gm);
+    uint4* s_x = s_gm + tab_u4;
+    int* s_red = reinterpret_cast<int*>(s_gm + tab_u4 + xs_n) + wv * 256u;
+    // while a batch item's digits are staged the exchange area holds the
+    // per-wave maxima and the exponents
+    uint32_t (*s_mx)[M] = reinterpret_cast<uint32_t (*)[M]>(s_gm + tab_u4 + xs_n);
+    int* s_e = reinterpret_cast<int*>(s_gm + tab_u4 + xs_n) + kWaves * M;
+    // points as signed bytes: (b - 64) mod 256 per byte of b = 2z + 64, no borrow across bytes
+    for (uint32_t i = tid; i <= a.npts; i += kThreads) {
+        uint32_t p0 = 0x40404040u, p1 = 0x40404040u;
+        if (i < a.npts) {
+            p0 = a.pts8[2u * i];
+            p1 = a.pts8[2u * i + 1u];
+        }
+        s_tab[i] = make_uint2(((p0 | 0x80808080u) - 0x40404040u) ^ 0x80808080u,
+                              ((p1 | 0x80808080u) - 0x40404040u) ^ 0x80808080u);
+    }
+    __syncthreads();
+    const uint32_t i16 = lane & 15u, q = lane >> 4;
+    const uint32_t nc = a.gpr >> 5;
+    const uint32_t ncp = (nc + uint32_t(kI8Ahead) - 1u) / uint32_t(kI8Ahead) * uint32_t(kI8Ahead);
+    const bool bcol = i16 < NCOL;
+    uint32_t flags = 0;
+
+    const uint32_t units_per_b = (a.tiles_per_b + kWaves - 1u) / kWaves;
+    const uint32_t units = (a.tiles / a.tiles_per_b) * units_per_b;
+    const uint32_t per = (units + gridDim.x - 1u) / gridDim.x;
+    const uint32_t u_begin = min(blockIdx.x * per, units), u_end = min(u_begin + per, units);
+    const auto wave_tile = [&](uint32_t u) { return (u % units_per_b) * kWaves + wv; };
+    const auto row_words = [&](uint32_t u) {
+        const uint32_t bb = u / units_per_b;
+        const uint32_t rr = min(wave_tile(u) * kGmRows + i16, a.rows - 1u);
+        return reinterpret_cast<const uint4*>(a.core_idx + (uint64_t(bb) * a.rows + rr) * a.gpr) + q;
+    };
+    uint32_t pf_u = u_begin, pf_c = 0;
+    while (pf_u < u_end && wave_tile(pf_u) >= a.tiles_per_b) ++pf_u;
+    const uint4* pf_ip = pf_u < u_end ? row_words(pf_u) : reinterpret_cast<const uint4*>(a.core_idx) + q;
+    const auto next_word = [&]() {
+        const uint4 w = pf_ip[4u * min(pf_c, nc - 1u)];
+        if (++pf_c == ncp) {
+            pf_c = 0;
+            if (pf_u < u_end) {
+                do ++pf_u; while (pf_u < u_end && wave_tile(pf_u) >= a.tiles_per_b);
+                if (pf_u < u_end) pf_ip = row_words(pf_u);
+            }
+        }
+        return w;
+    };
+    uint4 wq[kI8Ahead];
+#pragma unroll
+    for (int k = 0; k < kI8Ahead; ++k) wq[k] = next_word();
+    uint32_t staged = 0xFFFFFFFFu;
+    int ev[M];
+#pragma unroll
+    for (int v = 0; v < M; ++v) ev[v] = 0;
+    for (uint32_t u = u_begin; u < u_end; ++u) {
+        const uint32_t b = u / units_per_b;
+        if (b != staged) {   // block-uniform
+            __syncthreads();
+            const float* xv = a.xt + uint64_t(b) * M * cols;
+            // largest |x~| bits per vector (NaN and infinity above every finite value)
+            uint32_t mx[M];
+#pragma unroll
+            for (int v = 0; v < M; ++v) {
+                mx[v] = 0u;
+                for (uint32_t i = tid; i < cols; i += kThreads)
+                    mx[v] = max(mx[v], __float_as_uint(xv[uint64_t(v) * cols + i]) & 0x7FFFFFFFu);
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) mx[v] = max(mx[v], uint32_t(__shfl_xor(mx[v], off, 64)));
+                if (lane == 0u) s_mx[wv][v] = mx[v];
+            }
+            __syncthreads();
+            if (tid < uint32_t(M)) {
+                uint32_t m = 0u;
+                for (uint32_t k = 0; k < kWaves; ++k) m = max(m, s_mx[k][tid]);
+                // e with 2^(e-1) <= max < 2^e; 0 for an all-zero vector; 255 marks a non-finite one
+                s_e[tid] = m >= 0x7F800000u ? 255 : (m == 0u ? 0 : __builtin_amdgcn_frexp_expf(__uint_as_float(m)));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int v = 0; v < M; ++v) ev[v] = s_e[v];
+            // digits in step order: entry ((4c + s) 4 + q) NCOL + n holds column n's
+            // digits for groups 32c + 8q + 2s, +1, so that the lanes of one step
+            // read consecutive entries
+            for (uint32_t i = tid; i < uint32_t(M) * (a.gpr / 2u); i += kThreads) {
+                const uint32_t v = i / (a.gpr / 2u), pr = i - v * (a.gpr / 2u);
+                const uint32_t c = pr >> 4, qq = (pr >> 2) & 3u, st = pr & 3u;
+                const float* src = xv + uint64_t(v) * cols + 16u * pr;
+                int evv = ev[0];
+#pragma unroll
+                for (int w2 = 1; w2 < M; ++w2)
+                    if (v == uint32_t(w2)) evv = ev[w2];
+                const bool fin = evv != 255;   // digits of a non-finite vector are never used
+                const int shv = fin ? 30 - evv : 0;
+                uint32_t dg[4][4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dg[d][k] = 0u;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const float xs = __builtin_ldexpf(src[k], shv);
+                    int n = fin ? int(__builtin_rintf(xs)) : 0;   // |xs| <= 2^30
+                    const int d3 = int(int8_t(uint8_t(n)));
+                    n = (n - d3) >> 8;
+                    const int d2 = int(int8_t(uint8_t(n)));
+                    n = (n - d2) >> 8;
+                    const int d1 = int(int8_t(uint8_t(n)));
+                    const int d0 = (n - d1) >> 8;
+                    const uint32_t sb = 8u * uint32_t(k & 3);
+                    dg[0][k >> 2] |= (uint32_t(d0) & 0xFFu) << sb;
+                    dg[1][k >> 2] |= (uint32_t(d1) & 0xFFu) << sb;
+                    dg[2][k >> 2] |= (uint32_t(d2) & 0xFFu) << sb;
+                    dg[3][k >> 2] |= (uint32_t(d3) & 0xFFu) << sb;
+                }
+                const uint32_t base = ((4u * c + st) * 4u + qq) * NCOL + 4u * v;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) s_x[base + uint32_t(d)] = make_uint4(dg[d][0], dg[d][1], dg[d][2], dg[d][3]);
+            }
+            __syncthreads();
+            staged = b;
+        }
+        const uint32_t t = wave_tile(u);
+        if (t >= a.tiles_per_b) continue;
+        const uint32_t r0 = t * kGmRows;
+        const bool row_ok = r0 + i16 < a.rows;
+        const uint4* xp = s_x + (q * NCOL + i16);
+        const float s_row = a.scale[uint64_t(b) * a.rows + min(r0 + (lane & 15u), a.rows - 1u)];
+        gm_i32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+        uint32_t nesc = 0;
+        const auto chunk = [&](uint4& slot, uint32_t c) {
+            uint4 w = slot;
+            slot = next_word();
+            if (c < nc) {
+                const gm_u16x2 mxi = __builtin_elementwise_max(
+                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.x), __builtin_bit_cast(gm_u16x2, w.y)),
+                    __builtin_elementwise_max(__builtin_bit_cast(gm_u16x2, w.z), __builtin_bit_cast(gm_u16x2, w.w)));
+                const bool big = uint32_t(mxi.x > mxi.y ? mxi.x : mxi.y) >= a.npts;
+                if (__ballot(big)) {
+                    if (big) {
+                        if (row_ok) {
+#pragma unroll 1
+                            for (uint32_t s = 0; s < 8; ++s) {
+                                const uint32_t h = s >> 1;
+                                const uint32_t word = h == 0 ? w.x : h == 1 ? w.y : h == 2 ? w.z : w.w;
+                                const uint32_t id = (word >> (16u * (s & 1u))) & 0xFFFFu;
+                                if (id == 0xFFFFu) ++nesc;
+                                else if (id >= a.npts) flags |= E8Q_STATUS_BAD_INDEX;
+                            }
+                        }
+                        const gm_u16x2 lim = {uint16_t(a.npts), uint16_t(a.npts)};
+                        w.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.x), lim));
+                        w.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.y), lim));
+                        w.z = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.z), lim));
+                        w.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(gm_u16x2, w.w), lim));
+                    }
+                }
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    // entries are 8 bytes and every index is now <= npts < 4096
+                    const uint2 p0 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) +
+                                                                     ((wd[s] << 3) & 0x7FFF8u));
+                    const uint2 p1 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) +
+                                                                     (wd[s] >> 13));
+                    // only the lanes of real columns read their digits (the D columns of
+                    // the others are never read)
+                    const uint4 xc = bcol ? xp[(4u * c + uint32_t(s)) * 4u * NCOL] : make_uint4(0u, 0u, 0u, 0u);
+                    const gm_i32x4 av = {int(p0.x), int(p0.y), int(p1.x), int(p1.y)};
+                    const gm_i32x4 bv = {int(xc.x), int(xc.y), int(xc.z), int(xc.w)};
+                    if (s & 1) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc1, 0, 0, 0);
+                    else acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc0, 0, 0, 0);
+                }
+            }
+        };
+        for (uint32_t c = 0; c < ncp; c += uint32_t(kI8Ahead)) {
+#pragma unroll
+            for (int k = 0; k < kI8Ahead; ++k) chunk(wq[k], c + uint32_t(k));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_red[(4u * q + uint32_t(r)) * 16u + i16] = acc0[r] + acc1[r];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) nesc += __shfl_xor(nesc, off, 64);
+        if (lane == 0u) a.tile_esc[uint64_t(b) * a.tiles_per_b + t] = nesc;
+        gm_wave_sync();
+        if (lane < kGmRows && r0 + lane < a.rows) {
+            const uint32_t r = r0 + lane;
+            const float s = s_row;
+            const bool bad = !(s > 0.0f) || __builtin_isinf(s);
+            if (bad) flags |= E8Q_STATUS_BAD_SCALE;
+            const int* d = s_red + lane * 16u;
+#pragma unroll
+            for (int v = 0; v < M; ++v) {
+                const int64_t yi = ((int64_t(d[4 * v]) * 256 + d[4 * v + 1]) * 256 + d[4 * v + 2]) * 256 + d[4 * v + 3];
+                float yv;
+                if (ev[v] == 255) {
+                    yv = __uint_as_float(0x7FC00000u);
+                    flags |= E8Q_STATUS_NONFINITE;
+                } else {
+                    yv = float((0.5 * double(s)) * __builtin_ldexp(double(yi), ev[v] - 30));
+                }
+                a.y[(uint64_t(b) * M + uint32_t(v)) * a.rows + r] = bad ? 0.0f : yv;
             }
         }
         gm_wave_sync();
@@ -975,23 +1186,27 @@ static void launch_gemv(bool lds_pts, const GemvArgs& a, dim3 grid, size_t lds, 
         launch((gemv_kernel<M, false>), grid, dim3(kGemvThreads), lds, st, a);
 }
 
+// LDS bytes of gemv_i8_kernel: the int8 table, the activation digits (4 bytes
+// per element and vector) and the row exchange of 16 waves.
+static size_t gemv_i8_lds(uint32_t npts, int64_t m, int64_t cols) {
+    return size_t((npts + 2) / 2) * 16 + size_t(m) * 4 * size_t(cols) + 16 * 256 * 4;
+}
+
 template <int M>
 static void launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t st) {
-    const size_t tab = size_t(a.npts + 1) * 16;
-    const size_t xs = size_t(M) * 3 * a.gpr * 16;
-    const size_t red16 = 16 * 256 * 4, red8 = 8 * 256 * 4;
-    const uint64_t tiles_per_b = a.tiles_per_b, batch = a.tiles / a.tiles_per_b;
-    // a table in LDS has fewer than 4096 entries (the sweep's byte offsets rely on it)
-    if (a.npts < 4096 && tab + xs + red16 <= 160 * 1024) {
-        const uint64_t units = batch * ((tiles_per_b + 15) / 16);
-        launch_tiles(gemv_mfma_kernel<M, true, true>, a, units, 1024, tab + xs + red16, st);
-    } else {
-        const uint64_t units = batch * ((tiles_per_b + 7) / 8);
-        if (a.npts < 4096 && tab <= 48 * 1024)
-            launch_tiles(gemv_mfma_kernel<M, true, false>, a, units, 512, tab + red8, st);
-        else
-            launch_tiles(gemv_mfma_kernel<M, false, false>, a, units, 512, red8, st);
+    // the int8 kernel: table in LDS (fewer than 4096 points: byte offsets from
+    // two shifts), digits in LDS, exact int32 row sums (cols < 2^19)
+    const size_t i8_lds = gemv_i8_lds(a.npts, M, int64_t(a.gpr) * 8);
+    const uint64_t batch = a.tiles / a.tiles_per_b;
+    if (a.npts < 4096 && a.gpr < (1u << 16) && i8_lds <= 160 * 1024) {
+        const uint64_t units = batch * ((a.tiles_per_b + 15) / 16);
+        launch_tiles(gemv_i8_kernel<M>, a, units, 1024, i8_lds, st);
+        return;
     }
+    // the bfloat16 kernel (cores of 4096 points or more): table and activation
+    // parts from global memory
+    const uint64_t units = batch * ((a.tiles_per_b + 7) / 8);
+    launch_tiles(gemv_mfma_kernel<M>, a, units, 512, size_t(8 * 256 * 4), st);
 }
 
 }  // namespace e8q
@@ -1082,6 +1297,7 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
         gm.tile_esc = tile_esc;
         gm.scale = row_scale;
         gm.tab = tab->dpts_bf16;
+        gm.pts8 = tab->dpoints;
         gm.npts = uint32_t(tab->size);
         gm.rows = uint32_t(rows);
         gm.gpr = gpr;

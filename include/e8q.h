@@ -409,21 +409,28 @@ size_t e8q_decode_workspace_size(int64_t batch);
  * restored weight matrix of each batch item (as e8q_decode_core_escape's
  * w_hat, before any rounding); it is never formed: with x~ = kappa_b H_b
  * (sigma * x) computed once per activation vector in float32,
- * y_r = (s_r / 2) * sum_g 2z_g . x~_g, float32 accumulation.
+ * y_r = (s_r / 2) * sum_g 2z_g . x~_g.
  *   core_idx, esc, esc_capacity, esc_count, core_bound, row_scale, signs,
  *   had_block   as e8q_decode_core_escape (signs NULL: no rotation, W_hat = s z)
  *   x            [batch, m, cols] activations, x_dtype F32 or BF16; m in {1, 2, 4}
  *   y_out        [batch, m, rows] float32
  *   workspace    e8q_gemv_workspace_size(batch, m, rows, cols) bytes, 256-byte aligned
  * Rows whose column count is a multiple of 256, with 16-byte aligned core_idx,
- * run on the matrix cores (x~ split into three bfloat16 parts, exact products,
- * float32 sums whose order inside one MFMA is the hardware's); their escaped
- * slots are added after the row sums, y += (s / 2) * sum of the row's records'
- * 2z . x~ (float32, in record order, in blocks of 32).  Other shapes use
- * float32 FMA chains with the escaped slots in place.  Rounding, either way: |y - W_hat x| <=
- * 2 (L + G + 66) 2^-24 S_r + 2^-120 s_r sum_g sum_i |z_gi| per output,
- * L = log2(b), G = ceil(cols / 512), S_r = s_r sum_g sum_i |z_gi| xbar_gi,
- * xbar = kappa_b times the block sums of |x| (|x| itself without rotation).
+ * run on the matrix cores.  With cores below 4096 points (B < 24) every
+ * activation vector is put in fixed point, x~_k ~ N_k 2^(e-30) with
+ * N_k = rint(x~_k 2^(30-e)) and 2^(e-1) <= max_k |x~_k| < 2^e, and the row
+ * sums sum_g 2z_g . N_g are exact int32 sums on the int8 matrix cores
+ * (N as four signed base-256 digits), y = fl32(fl64((s/2) 2^(e-30) sum));
+ * a vector holding a NaN or infinity gives NaN rows (E8Q_STATUS_NONFINITE).
+ * With larger cores x~ is split into three bfloat16 parts (exact products,
+ * float32 sums whose order inside one MFMA is the hardware's).  Either way the
+ * escaped slots are added after the row sums, y += (s / 2) * sum of the row's
+ * records' 2z . x~ (float32, in record order, in blocks of 32).  Other shapes
+ * use float32 FMA chains with the escaped slots in place.  Rounding, on every
+ * path: |y - W_hat x| <= 2 (L + G + 66) 2^-24 S_r + s_r sum_g sum_i |z_gi|
+ * (2^(e-31) + 2^-120) per output, L = log2(b), G = ceil(cols / 512),
+ * S_r = s_r sum_g sum_i |z_gi| xbar_gi, xbar = kappa_b times the block sums
+ * of |x| (|x| itself without rotation).
  * Limits: m * cols * 4 <= 96 KiB, batch <= 65535.  Malformed exports and bad
  * scales are flagged as in e8q_decode_core_escape (a bad row gives y = 0).
  * ------------------------------------------------------------------------- */

@@ -70,7 +70,7 @@ from .restore import (  # noqa: F401
     ste_backward_hadamard,
 )
 from .decode import decode_outputs  # noqa: F401
-from .gemv import exact_restored, gemv_reference, rotated_magnitude  # noqa: F401
+from .gemv import exact_restored, gemv_reference, rotated_bound, rotated_magnitude  # noqa: F401
 from .roots import (  # noqa: F401
     e8_roots,
     pack_escapes,

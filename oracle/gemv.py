@@ -45,6 +45,20 @@ def gemv_reference(two_z, s, x, signs=None, had_block=0):
     return y, mag
 
 
+def rotated_bound(x, signs=None, had_block=0):
+    """``xbar``: the block sums of ``|x|`` scaled by 1/sqrt(b) (``|x|`` with no
+    rotation), a bound on every ``|x_tilde_i|`` of the rotated activation
+    ``x_tilde = H_b (sigma * x) / sqrt(b)`` (each entry is a signed sum over
+    the block)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    if signs is None or had_block == 0:
+        return x
+    b = int(had_block)
+    lead = x.shape[:-1]
+    cols = x.shape[-1]
+    return np.repeat(x.reshape(lead + (cols // b, b)).sum(-1), b, axis=-1) / np.sqrt(float(b))
+
+
 def rotated_magnitude(two_z, s, x, signs=None, had_block=0):
     """``s_r * sum_g sum_i |z_gi| * xbar_gi`` with ``xbar`` the block sums of
     ``|x|`` scaled by 1/sqrt(b): a bound on the terms of the rotated-basis

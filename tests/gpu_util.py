@@ -170,14 +170,21 @@ def run_gemv(core, esc, cnt, shape, bound, s, x, signs=None, hb=0, esc_records=N
 
 
 def gemv_tolerance(two_z, s, x_vals, signs, hb, cols):
-    """The documented bound 2 (L + G + 66) 2^-24 S_r + 2^-120 s_r sum|z| of
-    the GEMV (both of its evaluation orders)."""
+    """The documented bound 2 (L + G + 66) 2^-24 S_r + s_r sum|z| (2^(e-30) +
+    2^-120) of the GEMV (every evaluation order), e = 1 + the binary exponent
+    of the largest xbar of the activation vector (xbar_i >= |x~_i|, so 2^e is
+    at least twice the vector's largest |x~|: the int8 kernel's fixed-point
+    step is at most 2^(e-31))."""
     L = int(np.log2(hb)) if hb else 0
     G = -(-cols // 512)
     S = oracle.rotated_magnitude(two_z, s, x_vals, signs, hb)
     tz = np.asarray(two_z, dtype=np.float64)
     z1 = np.abs(tz).sum(-1) * 0.5 * np.asarray(s, dtype=np.float64).reshape(tz.shape[0], tz.shape[1])
-    return 2.0 * (L + G + 66) * 2.0 ** -24 * S + 2.0 ** -120 * z1[:, None, :]
+    xbar = oracle.rotated_bound(x_vals, signs, hb)
+    mx = xbar.max(axis=-1)                                   # [batch, m]
+    e = np.frexp(np.where(mx > 0, mx, 1.0))[1] + 1
+    step = np.where(mx > 0, np.ldexp(1.0, e - 30), 0.0)
+    return 2.0 * (L + G + 66) * 2.0 ** -24 * S + (step[:, :, None] + 2.0 ** -120) * z1[:, None, :]
 
 
 def run_ptq(w, s0, alphas, bound, signs=None, hb=0):

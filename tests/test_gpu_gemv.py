@@ -1,9 +1,10 @@
 """GPU GEMV from the exported form against the float64 product of the exact
 restored weights, within the documented bound (the evaluation order is the
 kernel's own, so the bar is a derived tolerance, not bit equality).  Rows of
-a multiple of 256 columns with 16-byte aligned indices take the product-table
-kernel (one activation vector, cores of at most 2557 points) or the
-matrix-core kernel; other shapes and alignments the vector kernel."""
+a multiple of 256 columns with 16-byte aligned indices take the int8
+matrix-core kernel (cores below 4096 points whose table and activation
+digits fit in LDS) or the bfloat16 matrix-core kernel; other shapes and
+alignments the vector kernel."""
 
 import numpy as np
 import pytest
@@ -54,7 +55,9 @@ def test_gemv_oracle_export(m, hb, alpha):
 
 @pytest.mark.parametrize("bound", [0, 24, 40])
 def test_gemv_bounds_and_f32_activations(bound):
-    """Point table in LDS and in global memory; float32 activations."""
+    """Cores below 4096 points (the int8 kernel, table in LDS) and of 9121 and
+    56881 points (the bfloat16 kernel, table in global memory); float32
+    activations."""
     d = device()
     shape = (2, 33, 4096)
     w = workloads.normal(shape, 1700 + bound, d)
@@ -153,10 +156,10 @@ def test_gemv_vector_path_shapes(m):
 
 
 @pytest.mark.parametrize("m,cols", [(4, 4096), (2, 11008)])
-def test_gemv_activation_parts_from_global(m, cols):
-    """Shapes whose activation parts do not fit in LDS next to the point table
-    (four vectors of 4096 columns, two of 11008): the matrix-core kernel reads
-    them from global memory."""
+def test_gemv_wide_activations(m, cols):
+    """The widest activation shapes the call takes (four vectors of 4096
+    columns, two of 11008): the int8 kernel keeps their digits in LDS beside
+    the point table."""
     d = device()
     shape = (2, 45, cols)
     w = workloads.normal(shape, 1770 + m, d)
@@ -283,3 +286,35 @@ def test_gemv_many_batch_items():
     out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
     assert out["status"] == 0
     _check(out, enc["two_z"].reshape(shape), s.cpu().numpy(), x, sn, 128, 256)
+
+
+def test_gemv_int8_zero_nonfinite_and_wide_range_vectors():
+    """The int8 kernel's fixed point per activation vector: an all-zero vector
+    gives y = 0 exactly; a vector holding a NaN gives NaN rows and the
+    NONFINITE bit while the other vectors stay within the bound; a vector with
+    one entry 10^6 times the rest stays within the bound, whose fixed-point
+    term grows with the vector's largest entry."""
+    d = device()
+    shape = (3, 40, 2048)
+    w = workloads.normal(shape, 1900, d)
+    s = workloads.rms_scale(w, 2.0)
+    sg = workloads.signs(2048, 1901, d)
+    sn = sg.cpu().numpy()
+    enc = oracle.encode_core_escape(wbits(w), s.cpu().numpy(), sn, 128, 16)
+    core, esc, cnt = upload_export(enc, d)
+    x = _x((3, 2, 2048), 1902, d, torch.float32)
+    x[0, 1] = 0.0
+    x[1, 0, 77] = float("nan")
+    x[2, 1, 1500] = 1.0e6
+    out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
+    assert out["status"] == 1   # NONFINITE
+    assert np.all(out["y"][0, 1] == 0.0)
+    assert np.all(np.isnan(out["y"][1, 0]))
+    xv = _xvals(x)
+    tz = enc["two_z"].reshape(shape)
+    y, _ = oracle.gemv_reference(tz, s.cpu().numpy(), np.nan_to_num(xv), sn, 128)
+    tol = gemv_tolerance(tz, s.cpu().numpy(), np.nan_to_num(xv), sn, 128, 2048)
+    keep = np.ones((3, 2), dtype=bool)
+    keep[1, 0] = False
+    err = np.abs(out["y"] - y)[keep]
+    assert (err <= tol[keep]).all(), f"max err/tol {np.max(err / np.maximum(tol[keep], 1e-300)):.3g}"
