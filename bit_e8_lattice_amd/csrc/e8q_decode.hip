@@ -839,24 +839,26 @@ __global__ __launch_bounds__(512, 4) void gemv_mfma_kernel(GemvMfmaArgs a) {
 // with a non-finite x~ gives NaN rows and E8Q_STATUS_NONFINITE.
 typedef int gm_i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kI8Ahead = 4;   // index words (chunks) loaded ahead
+constexpr uint32_t kI8TabEntries = 4096;   // table entries in LDS (cores below 4096 points + the zero entry)
 
 template <int M>
 __global__ __launch_bounds__(1024, 4) void gemv_i8_kernel(GemvMfmaArgs a) {
     constexpr uint32_t kWaves = 16u;
     constexpr uint32_t kThreads = kWaves * kWave;
     constexpr uint32_t NCOL = 4u * uint32_t(M);
-    extern __shared__ uint4 s_gm[];   // table first (no static LDS: its offsets need no base)
+    // the table at a fixed LDS address (its offsets fold into the reads), then
+    // the dynamic LDS: digits and the row exchange
+    __shared__ uint2 s_tab[kI8TabEntries];
+    extern __shared__ uint4 s_gm[];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t cols = a.gpr * 8u;
-    const uint32_t tab_u4 = (a.npts + 2u) / 2u;      // 16-byte units holding npts + 1 entries of 8 bytes
     const uint32_t xs_n = NCOL * (a.gpr / 2u);        // 16-byte digit entries: per pair of groups, per column
-    uint2* s_tab = reinterpret_cast<uint2*>(s_gm);
-    uint4* s_x = s_gm + tab_u4;
-    int* s_red = reinterpret_cast<int*>(s_gm + tab_u4 + xs_n) + wv * 256u;
+    uint4* s_x = s_gm;
+    int* s_red = reinterpret_cast<int*>(s_gm + xs_n) + wv * 256u;
     // while a batch item's digits are staged the exchange area holds the
     // per-wave maxima and the exponents
-    uint32_t (*s_mx)[M] = reinterpret_cast<uint32_t (*)[M]>(s_gm + tab_u4 + xs_n);
-    int* s_e = reinterpret_cast<int*>(s_gm + tab_u4 + xs_n) + kWaves * M;
+    uint32_t (*s_mx)[M] = reinterpret_cast<uint32_t (*)[M]>(s_gm + xs_n);
+    int* s_e = reinterpret_cast<int*>(s_gm + xs_n) + kWaves * M;
     // points as signed bytes: (b - 64) mod 256 per byte of b = 2z + 64, no borrow across bytes
     for (uint32_t i = tid; i <= a.npts; i += kThreads) {
         uint32_t p0 = 0x40404040u, p1 = 0x40404040u;
@@ -976,7 +978,9 @@ __global__ __launch_bounds__(1024, 4) void gemv_i8_kernel(GemvMfmaArgs a) {
         if (t >= a.tiles_per_b) continue;
         const uint32_t r0 = t * kGmRows;
         const bool row_ok = r0 + i16 < a.rows;
-        const uint4* xp = s_x + (q * NCOL + i16);
+        // lanes of unused columns read column 0's entry (an LDS broadcast; their D
+        // columns are never read)
+        const uint4* xp = s_x + (q * NCOL + (bcol ? i16 : 0u));
         const float s_row = a.scale[uint64_t(b) * a.rows + min(r0 + (lane & 15u), a.rows - 1u)];
         gm_i32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
         uint32_t nesc = 0;
@@ -1008,18 +1012,21 @@ __global__ __launch_bounds__(1024, 4) void gemv_i8_kernel(GemvMfmaArgs a) {
                     }
                 }
                 const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+                // the chunk's eight table reads and four digit reads first, then its
+                // four MFMAs (entries are 8 bytes and every index is now <= npts < 4096)
+                uint2 p0[4], p1[4];
+                uint4 xc[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    // entries are 8 bytes and every index is now <= npts < 4096
-                    const uint2 p0 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) +
-                                                                     ((wd[s] << 3) & 0x7FFF8u));
-                    const uint2 p1 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) +
-                                                                     (wd[s] >> 13));
-                    // only the lanes of real columns read their digits (the D columns of
-                    // the others are never read)
-                    const uint4 xc = bcol ? xp[(4u * c + uint32_t(s)) * 4u * NCOL] : make_uint4(0u, 0u, 0u, 0u);
-                    const gm_i32x4 av = {int(p0.x), int(p0.y), int(p1.x), int(p1.y)};
-                    const gm_i32x4 bv = {int(xc.x), int(xc.y), int(xc.z), int(xc.w)};
+                    p0[s] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) +
+                                                            ((wd[s] << 3) & 0x7FFF8u));
+                    p1[s] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(s_tab) + (wd[s] >> 13));
+                    xc[s] = xp[(4u * c + uint32_t(s)) * 4u * NCOL];
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const gm_i32x4 av = {int(p0[s].x), int(p0[s].y), int(p1[s].x), int(p1[s].y)};
+                    const gm_i32x4 bv = {int(xc[s].x), int(xc[s].y), int(xc[s].z), int(xc[s].w)};
                     if (s & 1) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc1, 0, 0, 0);
                     else acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc0, 0, 0, 0);
                 }
@@ -1186,19 +1193,20 @@ static void launch_gemv(bool lds_pts, const GemvArgs& a, dim3 grid, size_t lds, 
         launch((gemv_kernel<M, false>), grid, dim3(kGemvThreads), lds, st, a);
 }
 
-// LDS bytes of gemv_i8_kernel: the int8 table, the activation digits (4 bytes
-// per element and vector) and the row exchange of 16 waves.
-static size_t gemv_i8_lds(uint32_t npts, int64_t m, int64_t cols) {
-    return size_t((npts + 2) / 2) * 16 + size_t(m) * 4 * size_t(cols) + 16 * 256 * 4;
+// Dynamic LDS bytes of gemv_i8_kernel: the activation digits (4 bytes per
+// element and vector) and the row exchange of 16 waves (the table's 32 KiB
+// are static).
+static size_t gemv_i8_lds(int64_t m, int64_t cols) {
+    return size_t(m) * 4 * size_t(cols) + 16 * 256 * 4;
 }
 
 template <int M>
 static void launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t st) {
     // the int8 kernel: table in LDS (fewer than 4096 points: byte offsets from
     // two shifts), digits in LDS, exact int32 row sums (cols < 2^19)
-    const size_t i8_lds = gemv_i8_lds(a.npts, M, int64_t(a.gpr) * 8);
+    const size_t i8_lds = gemv_i8_lds(M, int64_t(a.gpr) * 8);
     const uint64_t batch = a.tiles / a.tiles_per_b;
-    if (a.npts < 4096 && a.gpr < (1u << 16) && i8_lds <= 160 * 1024) {
+    if (a.npts < kI8TabEntries && a.gpr < (1u << 16) && kI8TabEntries * 8 + i8_lds <= 160 * 1024) {
         const uint64_t units = batch * ((a.tiles_per_b + 15) / 16);
         launch_tiles(gemv_i8_kernel<M>, a, units, 1024, i8_lds, st);
         return;
