@@ -1200,15 +1200,20 @@ static size_t gemv_i8_lds(int64_t m, int64_t cols) {
     return size_t(m) * 4 * size_t(cols) + 16 * 256 * 4;
 }
 
+// Whether the matrix-core GEMV of these shapes runs on the int8 kernel: table
+// in LDS (fewer than 4096 points: byte offsets from two shifts), digits in
+// LDS, exact int32 row sums (cols < 2^19).
+static bool gemv_use_i8(uint32_t npts, int64_t m, uint32_t gpr) {
+    return npts < kI8TabEntries && gpr < (1u << 16) &&
+           kI8TabEntries * 8 + gemv_i8_lds(m, int64_t(gpr) * 8) <= 160 * 1024;
+}
+
 template <int M>
 static void launch_gemv_mfma(const GemvMfmaArgs& a, hipStream_t st) {
-    // the int8 kernel: table in LDS (fewer than 4096 points: byte offsets from
-    // two shifts), digits in LDS, exact int32 row sums (cols < 2^19)
-    const size_t i8_lds = gemv_i8_lds(M, int64_t(a.gpr) * 8);
     const uint64_t batch = a.tiles / a.tiles_per_b;
-    if (a.npts < kI8TabEntries && a.gpr < (1u << 16) && kI8TabEntries * 8 + i8_lds <= 160 * 1024) {
+    if (gemv_use_i8(a.npts, M, a.gpr)) {
         const uint64_t units = batch * ((a.tiles_per_b + 15) / 16);
-        launch_tiles(gemv_i8_kernel<M>, a, units, 1024, i8_lds, st);
+        launch_tiles(gemv_i8_kernel<M>, a, units, 1024, gemv_i8_lds(M, int64_t(a.gpr) * 8), st);
         return;
     }
     // the bfloat16 kernel (cores of 4096 points or more): table and activation
@@ -1279,7 +1284,9 @@ extern "C" e8q_status_t e8q_gemv_core_escape(const uint16_t* core_idx, const e8q
     RotArgs ra;
     ra.x = x;
     ra.xt = xt;
-    ra.xb = mfma ? xb : nullptr;
+    // the bfloat16 parts only for the bfloat16 matrix-core kernel (the int8
+    // kernel makes its digits from x~ itself)
+    ra.xb = mfma && !gemv_use_i8(uint32_t(tab->size), m, uint32_t(cols / 8)) ? xb : nullptr;
     ra.signs = signs;
     ra.kappa = kappa_for(hb);
     ra.cols = uint32_t(cols);
