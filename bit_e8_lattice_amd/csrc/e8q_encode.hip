@@ -207,6 +207,7 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
         for (int j = 0; j < kItems; ++j) {
             const uint32_t g = g1;
             const bool live = g < a.groups;
+            const uint64_t live_mask = __ballot(live);   // scalar: taken before the decoder's branches
             const uint32_t gl = min(g, glast);
             const uint32_t row = r1;
             const Raw raw = w1;
@@ -279,8 +280,10 @@ __global__ __launch_bounds__(kBlock, 6) void encode_kernel(EncodeArgs a) {
                     flags |= f8;
                 }
             }
-            if (live) a.core_idx[g] = uint16_t(escaped ? 0xFFFFu : cidx);
-            const uint64_t mask = __ballot(escaped);
+            // cidx is 0xFFFF exactly for the points outside the core (a rank is
+            // below 65535), so it is also the escape flag
+            if (live) a.core_idx[g] = uint16_t(cidx);
+            const uint64_t mask = __ballot(cidx == 0xFFFFu) & live_mask;
             if (lane == 0) {
                 s_cnt[j * kWaves + wv] = uint32_t(__popcll(mask));
                 s_ball[j][wv] = mask;
