@@ -293,7 +293,8 @@ def test_gemv_int8_zero_nonfinite_and_wide_range_vectors():
     gives y = 0 exactly; a vector holding a NaN gives NaN rows and the
     NONFINITE bit while the other vectors stay within the bound; a vector with
     one entry 10^6 times the rest stays within the bound, whose fixed-point
-    term grows with the vector's largest entry."""
+    term grows with the vector's largest entry; a vector of float32
+    subnormals (scale exponent about -130) stays within it too."""
     d = device()
     shape = (3, 40, 2048)
     w = workloads.normal(shape, 1900, d)
@@ -306,6 +307,7 @@ def test_gemv_int8_zero_nonfinite_and_wide_range_vectors():
     x[0, 1] = 0.0
     x[1, 0, 77] = float("nan")
     x[2, 1, 1500] = 1.0e6
+    x[2, 0] *= 1.0e-39
     out = run_gemv(core, esc, cnt, shape, 16, s, x, sg, 128)
     assert out["status"] == 1   # NONFINITE
     assert np.all(out["y"][0, 1] == 0.0)
