@@ -105,3 +105,29 @@ def test_gemv_reference_is_the_restored_product(hb):
         assert np.allclose(y2, y, rtol=0, atol=1e-12 * mag.max())
         rmag = oracle.rotated_magnitude(two_z, s, x, sig, hb)
         assert (rmag >= np.abs(y2) - 1e-12).all()
+
+
+@pytest.mark.parametrize("hb", [0, 8, 128])
+def test_rotated_bound_covers_the_rotated_activations(hb):
+    """rotated_bound (the GEMV tolerance's xbar) bounds every |x_tilde_i| of the
+    rotated activation H_b (sigma x) / sqrt(b) computed densely in float64, and
+    is attained at position 0 of a block whose signed entries are all
+    non-negative (that row of H_b is all ones)."""
+    rng = np.random.default_rng(70 + hb)
+    batch, m, cols = 2, 3, 512
+    x = rng.normal(size=(batch, m, cols))
+    sig = np.where(rng.integers(0, 2, cols) == 1, 1, -1).astype(np.int8) if hb else None
+    xbar = oracle.rotated_bound(x, sig, hb)
+    if hb:
+        H = oracle.sylvester_matrix(hb)
+        xt = ((x * sig).reshape(batch, m, cols // hb, hb) @ H.T).reshape(batch, m, cols) / np.sqrt(hb)
+    else:
+        xt = x
+    assert (xbar >= np.abs(xt) * (1 - 1e-12)).all()
+    if hb:
+        y = np.abs(x) * sig                     # sigma * y >= 0 everywhere
+        xb = oracle.rotated_bound(y, sig, hb)
+        first = ((y * sig).reshape(batch, m, cols // hb, hb) @ oracle.sylvester_matrix(hb).T)[..., 0] / np.sqrt(hb)
+        assert np.allclose(xb.reshape(batch, m, cols // hb, hb)[..., 0], first, rtol=1e-12, atol=0)
+    else:
+        assert np.array_equal(xbar, np.abs(x))
