@@ -153,8 +153,25 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
     // escape counts per batch item, held back per wave while its items stay in
     // one batch item (wave-uniform, so scalar registers)
     uint32_t pend_b = 0u, pend_n = 0u;
+    // Rows of at least 64 groups: a tile touches at most 65 rows, whose
+    // coefficients fl32(kappa * fl32(1/s)) the block computes once per tile
+    // into LDS (NaN marks a bad scale), instead of a division per group.
+    __shared__ float s_coef[kTileGroups / 64u + 2u];
+    const bool row_tab = a.gpr >= 64u;   // kernel-uniform
     for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
         const uint32_t tbase = tile * kTileGroups + lpos;
+        uint32_t row0 = 0;
+        if (row_tab) {
+            row0 = fdiv(tile * kTileGroups, a.gpr_div);
+            const uint32_t nrows = fdiv(min(tile * kTileGroups + (kTileGroups - 1u), glast), a.gpr_div) - row0 + 1u;
+            __syncthreads();   // the previous tile's reads are done
+            if (tid < nrows) {
+                bool bad_r;
+                const float c = row_coef(a.scale[row0 + tid], a.kappa, bad_r);
+                s_coef[tid] = bad_r ? __uint_as_float(0x7FC00000u) : c;
+            }
+            __syncthreads();
+        }
         uint32_t g1 = tbase, g2 = tbase + kBlock;
         uint32_t r1 = fdiv(min(g1, glast), a.gpr_div), r2 = fdiv(min(g2, glast), a.gpr_div);
         Raw w1 = load_raw<WT>(a.w, min(g1, glast)), w2 = load_raw<WT>(a.w, min(g2, glast));
@@ -212,7 +229,13 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
                                      fmaf(v[7], kap, 0.0f));
             }
             bool bad;
-            const float c0 = row_coef(s, a.kappa, bad);
+            float c0;
+            if (row_tab) {
+                c0 = s_coef[row - row0];
+                bad = __builtin_isnan(c0);
+            } else {
+                c0 = row_coef(s, a.kappa, bad);
+            }
             const float c = __uint_as_float(__float_as_uint(c0) ^ vsign);
             float x[8];
 #pragma unroll

@@ -117,6 +117,23 @@ def test_invalid_data_status_bits():
         assert out["status"] & oracle.STATUS_BAD_SCALE
 
 
+def test_bad_scales_wide_rows():
+    """Rows of 128 groups (row coefficients computed once per tile and row),
+    40 rows over two tiles, bf16 with a 128-wide rotation: every kind of bad
+    scale on rows of both tiles; each bad row projects to 0 with BAD_SCALE."""
+    d = device()
+    w = workloads.normal((40, 1024), 120, d)
+    s = workloads.rms_scale(w, 1.0)
+    sc = s.cpu()
+    for r, bad in zip((1, 8, 31, 32, 39), (0.0, -2.0, float("nan"), float("inf"), 1e-45)):
+        sc[r] = bad
+    sg = workloads.signs(1024, 121, d)
+    out = run_project(w, sc.to(d), sg, 128)
+    ref = oracle.project(wbits(w), sc.numpy(), sg.cpu().numpy(), 128)
+    _compare(out, ref)
+    assert out["status"] == oracle.STATUS_BAD_SCALE
+
+
 def test_exact_ties_and_lattice_points():
     """Quarter/half grids and exact lattice points: tie rules must match."""
     d = device()
