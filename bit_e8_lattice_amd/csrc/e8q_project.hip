@@ -155,9 +155,12 @@ __global__ __launch_bounds__(kBlock, 6) void project_kernel(ProjectArgs a) {
     uint32_t pend_b = 0u, pend_n = 0u;
     // Rows of at least 64 groups: a tile touches at most 65 rows, whose
     // coefficients fl32(kappa * fl32(1/s)) the block computes once per tile
-    // into LDS (NaN marks a bad scale), instead of a division per group.
-    __shared__ float s_coef[kTileGroups / 64u + 2u];
-    const bool row_tab = a.gpr >= 64u;   // kernel-uniform
+    // into LDS (NaN marks a bad scale), instead of a division per group.  Not
+    // in the restore and rotated-gradient forms: their register pressure made
+    // them slower with it (scalar and vector spills).
+    constexpr bool kRowTab = !RESTORE && SGD != 2;
+    __shared__ float s_coef[kRowTab ? kTileGroups / 64u + 2u : 1u];
+    const bool row_tab = kRowTab && a.gpr >= 64u;   // kernel-uniform
     for (uint32_t tile = blockIdx.x; tile < a.num_tiles; tile += gridDim.x) {
         const uint32_t tbase = tile * kTileGroups + lpos;
         uint32_t row0 = 0;
